@@ -1,0 +1,186 @@
+// C ABI entry points: argument checks on the host, then one kernel launch on
+// the caller's stream.  Nothing is allocated and no state is kept between
+// calls except the calling thread's last error message.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/mhc.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+mhc_status fail(mhc_status s, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+mhc_status ok()
+{
+    g_last_error[0] = '\0';
+    return MHC_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// [a, a+na) and [b, b+nb) share at least one byte
+bool overlap(const void* a, size_t na, const void* b, size_t nb)
+{
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+// Largest batch / token count accepted (2^36 matrices = 4 TiB of fp32); keeps
+// every grid far below the 2^31 - 1 workgroup limit.
+constexpr int64_t kMaxBatch = (int64_t)1 << 36;
+constexpr int64_t kMaxTokens = (int64_t)1 << 34;
+
+mhc_status check_opts(const mhc_proj_opts* in, mhc::SolverOpts* out)
+{
+    mhc_proj_opts o;
+    mhc_proj_opts_default(&o);
+    if (in != nullptr) o = *in;
+    if (o.solver != MHC_SOLVER_NEWTON && o.solver != MHC_SOLVER_SINKHORN)
+        return fail(MHC_ERR_INVALID_ARGUMENT, "opts.solver must be 0 (Newton) or 1 (Sinkhorn)");
+    if (o.max_iters < 1 || o.max_iters > 10000)
+        return fail(MHC_ERR_INVALID_ARGUMENT, "opts.max_iters must be in 1..10000");
+    if (!(o.tol >= 0.f) || o.tol > 1.f)
+        return fail(MHC_ERR_INVALID_ARGUMENT, "opts.tol must be in [0, 1]");
+    if (o.warm_sweeps < 0 || o.warm_sweeps > 64)
+        return fail(MHC_ERR_INVALID_ARGUMENT, "opts.warm_sweeps must be in 0..64");
+    *out = mhc::SolverOpts{o.solver, o.max_iters, o.tol, o.warm_sweeps};
+    return MHC_OK;
+}
+
+mhc_status launched(hipError_t e, const char* what)
+{
+    if (e != hipSuccess) return fail(MHC_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+mhc_status mhc_proj_opts_default(mhc_proj_opts* opts)
+{
+    if (opts == nullptr) return fail(MHC_ERR_INVALID_ARGUMENT, "opts is NULL");
+    opts->solver = MHC_SOLVER_NEWTON;
+    opts->max_iters = 30;
+    opts->tol = 1e-6f;
+    opts->warm_sweeps = 1;
+    return MHC_OK;
+}
+
+mhc_status mhc_birkhoff_fwd(const float* logits, float* P, int64_t B, const mhc_proj_opts* opts,
+                            uint8_t* iters, void* stream)
+{
+    if (B < 0 || B > kMaxBatch) return fail(MHC_ERR_INVALID_ARGUMENT, "B=%lld out of range", (long long)B);
+    mhc::SolverOpts o;
+    const mhc_status s = check_opts(opts, &o);
+    if (s != MHC_OK) return s;
+    if (B == 0) return ok();
+    if (logits == nullptr || P == nullptr) return fail(MHC_ERR_INVALID_ARGUMENT, "logits and P must not be NULL");
+    if (!aligned16(logits) || !aligned16(P)) return fail(MHC_ERR_INVALID_ARGUMENT, "logits and P must be 16-byte aligned");
+    const size_t bytes = (size_t)B * 64;
+    if (logits != P && overlap(logits, bytes, P, bytes))
+        return fail(MHC_ERR_INVALID_ARGUMENT, "P partially overlaps logits");
+    if (iters != nullptr && (overlap(iters, (size_t)B, logits, bytes) || overlap(iters, (size_t)B, P, bytes)))
+        return fail(MHC_ERR_INVALID_ARGUMENT, "iters overlaps logits or P");
+    return launched(mhc::launch_birkhoff_fwd(logits, P, iters, B, o, (hipStream_t)stream),
+                    "birkhoff_fwd launch");
+}
+
+mhc_status mhc_birkhoff_bwd(const float* P, const float* grad_P, float* grad_logits, int64_t B,
+                            void* stream)
+{
+    if (B < 0 || B > kMaxBatch) return fail(MHC_ERR_INVALID_ARGUMENT, "B=%lld out of range", (long long)B);
+    if (B == 0) return ok();
+    if (P == nullptr || grad_P == nullptr || grad_logits == nullptr)
+        return fail(MHC_ERR_INVALID_ARGUMENT, "P, grad_P and grad_logits must not be NULL");
+    if (!aligned16(P) || !aligned16(grad_P) || !aligned16(grad_logits))
+        return fail(MHC_ERR_INVALID_ARGUMENT, "P, grad_P and grad_logits must be 16-byte aligned");
+    const size_t bytes = (size_t)B * 64;
+    if (overlap(P, bytes, grad_logits, bytes))
+        return fail(MHC_ERR_INVALID_ARGUMENT, "grad_logits overlaps P");
+    if (grad_P != grad_logits && overlap(grad_P, bytes, grad_logits, bytes))
+        return fail(MHC_ERR_INVALID_ARGUMENT, "grad_logits partially overlaps grad_P");
+    return launched(mhc::launch_birkhoff_bwd(P, grad_P, grad_logits, B, (hipStream_t)stream),
+                    "birkhoff_bwd launch");
+}
+
+mhc_status mhc_stream_mix(const void* x, const float* H_or_logits, float* H_out, void* out,
+                          int64_t T, int32_t n, int64_t C, const mhc_proj_opts* proj,
+                          void* stream)
+{
+    if (n != 4) return fail(MHC_ERR_UNSUPPORTED, "only n = 4 streams are supported (got %d)", n);
+    if (T < 0 || T > kMaxTokens) return fail(MHC_ERR_INVALID_ARGUMENT, "T=%lld out of range", (long long)T);
+    if (C < 8 || C % 8 != 0 || C > ((int64_t)1 << 30))
+        return fail(MHC_ERR_INVALID_ARGUMENT, "C must be a positive multiple of 8 (got %lld)", (long long)C);
+    mhc::SolverOpts o{};
+    if (proj != nullptr) {
+        const mhc_status s = check_opts(proj, &o);
+        if (s != MHC_OK) return s;
+    }
+    if (T == 0) return ok();
+    if (x == nullptr || H_or_logits == nullptr || out == nullptr)
+        return fail(MHC_ERR_INVALID_ARGUMENT, "x, H_or_logits and out must not be NULL");
+    if (!aligned16(x) || !aligned16(H_or_logits) || !aligned16(out) || (H_out && !aligned16(H_out)))
+        return fail(MHC_ERR_INVALID_ARGUMENT, "tensors must be 16-byte aligned");
+    const size_t xbytes = (size_t)T * 4 * (size_t)C * 2, hbytes = (size_t)T * 64;
+    if (overlap(x, xbytes, out, xbytes) || overlap(H_or_logits, hbytes, out, xbytes))
+        return fail(MHC_ERR_INVALID_ARGUMENT, "out overlaps an input");
+    if (proj != nullptr && H_out != nullptr &&
+        (overlap(H_out, hbytes, x, xbytes) || overlap(H_out, hbytes, out, xbytes) ||
+         (H_out != H_or_logits && overlap(H_out, hbytes, H_or_logits, hbytes))))
+        return fail(MHC_ERR_INVALID_ARGUMENT, "H_out overlaps another tensor");
+    return launched(mhc::launch_stream_mix_fwd(x, H_or_logits, proj ? H_out : nullptr, out, T, C,
+                                               proj ? &o : nullptr, (hipStream_t)stream),
+                    "stream_mix launch");
+}
+
+mhc_status mhc_stream_mix_bwd(const void* x, const float* H, const void* grad_out, void* grad_x,
+                              float* grad_H, int64_t T, int32_t n, int64_t C, void* stream)
+{
+    if (n != 4) return fail(MHC_ERR_UNSUPPORTED, "only n = 4 streams are supported (got %d)", n);
+    if (T < 0 || T > kMaxTokens) return fail(MHC_ERR_INVALID_ARGUMENT, "T=%lld out of range", (long long)T);
+    if (C < 8 || C % 8 != 0 || C > ((int64_t)1 << 30))
+        return fail(MHC_ERR_INVALID_ARGUMENT, "C must be a positive multiple of 8 (got %lld)", (long long)C);
+    if (T == 0) return ok();
+    if (!x || !H || !grad_out || !grad_x || !grad_H)
+        return fail(MHC_ERR_INVALID_ARGUMENT, "x, H, grad_out, grad_x and grad_H must not be NULL");
+    if (!aligned16(x) || !aligned16(H) || !aligned16(grad_out) || !aligned16(grad_x) || !aligned16(grad_H))
+        return fail(MHC_ERR_INVALID_ARGUMENT, "tensors must be 16-byte aligned");
+    const size_t xbytes = (size_t)T * 4 * (size_t)C * 2, hbytes = (size_t)T * 64;
+    if (overlap(grad_x, xbytes, x, xbytes) || overlap(grad_x, xbytes, grad_out, xbytes) ||
+        overlap(grad_x, xbytes, H, hbytes) || overlap(grad_x, xbytes, grad_H, hbytes) ||
+        overlap(grad_H, hbytes, x, xbytes) || overlap(grad_H, hbytes, grad_out, xbytes) ||
+        overlap(grad_H, hbytes, H, hbytes))
+        return fail(MHC_ERR_INVALID_ARGUMENT, "an output overlaps another tensor");
+    return launched(mhc::launch_stream_mix_bwd(x, H, grad_out, grad_x, grad_H, T, C,
+                                               (hipStream_t)stream),
+                    "stream_mix_bwd launch");
+}
+
+const char* mhc_status_string(mhc_status s)
+{
+    switch (s) {
+    case MHC_OK: return "ok";
+    case MHC_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MHC_ERR_UNSUPPORTED: return "unsupported";
+    case MHC_ERR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+const char* mhc_last_error(void) { return g_last_error; }
+
+int32_t mhc_abi_version(void) { return MHC_ABI_VERSION; }
+
+}  // extern "C"

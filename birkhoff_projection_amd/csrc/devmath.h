@@ -1,0 +1,28 @@
+// Device math used by the gfx950 kernels: the hardware transcendental
+// instructions, called through clang's amdgcn builtins.
+//
+//   mhc_exp2(x)  v_exp_f32   2^x      (about 1 ulp)
+//   mhc_log2(x)  v_log_f32   log2(x)  (about 1 ulp)
+//   mhc_rcp(x)   v_rcp_f32   1/x      (about 1 ulp)
+//
+// The solver works in base 2: logits are multiplied by log2(e) once at load,
+// so exp(a) = 2^(a log2 e) and a log-sum-exp becomes a log2-sum-exp2.  The
+// caller always shifts the argument of mhc_exp2 to be <= 0 (a row max-shift),
+// so there is no overflow and the result lies in (0, 1].
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define MHC_DEV __device__ __forceinline__
+
+MHC_DEV float mhc_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+MHC_DEV float mhc_log2(float x) { return __builtin_amdgcn_logf(x); }
+MHC_DEV float mhc_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+MHC_DEV float mhc_max(float a, float b) { return __builtin_fmaxf(a, b); }
+MHC_DEV float mhc_min(float a, float b) { return __builtin_fminf(a, b); }
+MHC_DEV float mhc_abs(float a) { return __builtin_fabsf(a); }
+
+// bf16 <-> fp32.  A bf16 is the top half of an fp32, so widening is a shift.
+MHC_DEV float mhc_bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+MHC_DEV float mhc_bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }

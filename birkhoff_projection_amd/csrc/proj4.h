@@ -1,0 +1,384 @@
+// Per-lane 4x4 Birkhoff projection: forward (Newton on the column potentials,
+// or Sinkhorn-Knopp) and backward (implicit differentiation).
+//
+// One lane owns one matrix.  All 16 entries, the potentials and the solver
+// state stay in VGPRs; no cross-lane traffic, no LDS.  Every loop below is
+// fully unrolled so that array indices are compile-time constants.
+//
+// Method ("Accelerating Birkhoff projection for mHC", gist.science summary):
+//  * section 2 -- the projection of A is the entropy-regularised transport
+//    plan P = diag(u) exp(A) diag(v), the unique doubly stochastic scaling;
+//  * section 2.1 -- the dual has one redundant direction (a common shift), so
+//    for 4x4 it is a three-variable unconstrained convex problem solved by
+//    Newton's method with closed-form gradient and Hessian; rows are shifted
+//    by their maximum before the softmax;
+//  * section 2.2 -- the gradient comes from the implicit function theorem,
+//    with no forward state kept, and the last Newton Hessian is the matrix
+//    the backward needs.
+//
+// Reading taken here: the row potentials are eliminated in closed form by a
+// row softmax, leaving column potentials g = (g0, g1, g2, 0):
+//     P(g)_ij = exp(A_ij + g_j) / sum_k exp(A_ik + g_k)
+//     psi(g)  = sum_i logsumexp_j(A_ij + g_j) - sum_j g_j        (convex)
+//     grad    = c - 1,   c_j = sum_i P_ij (column sums)
+//     Hessian = diag(c) - P^T P  =  graph Laplacian with edge weights
+//               W_jk = sum_i P_ij P_ik  (because rows of P sum to 1)
+// Rows of P(g) are stochastic by construction; g solves the problem when the
+// columns are too.  At the solution the Hessian is I - P^T P, the matrix of
+// the implicit-differentiation system -- the "Hessian reuse" of section 2.2.
+//
+// Everything is computed in base 2 (a = A log2 e, g in log2 units):
+// 2^(a + g) = e^(A + g ln 2).  The Newton direction of the base-2 objective is
+// the natural-units direction times log2 e; the gradient is still c - 1.
+#pragma once
+
+#include "devmath.h"
+
+namespace mhc {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kFltEps = 1.1920928955078125e-07f;
+// Longest first trial step of a Newton iteration, in base-2 potential units
+// (a factor 2^8 in a column's scaling).  Far from the solution the Newton
+// model of the exponential objective can propose steps of thousands of
+// units; starting the backtracking at this length instead saves the many
+// halvings that would otherwise be spent getting back down.
+constexpr float kMaxStep = 8.f;
+
+// Solver selection and limits (mirrors mhc_proj_opts of the public header).
+struct SolverOpts {
+    int solver;       // 0 = Newton, 1 = Sinkhorn
+    int max_iters;    // Newton iterations / Sinkhorn sweeps
+    float tol;        // stop when max_j |c_j - 1| <= tol
+    int warm_sweeps;  // log-domain Sinkhorn sweeps before Newton
+};
+
+// Value, column sums and row-softmax matrix of the semi-dual at g.
+struct Eval {
+    float P[16];
+    float c[4];
+    float psi;    // base-2 objective
+    float scale;  // sum of the magnitudes of the terms psi is summed from
+    float res;    // max_j |c_j - 1|
+};
+
+// Row softmax of a + 1 g^T (g3 = 0) with the row max-shift before exp2.
+MHC_DEV void evaluate(const float* a, float g0, float g1, float g2, Eval& E)
+{
+    float lse = 0.f, lse_abs = 0.f;
+    E.c[0] = E.c[1] = E.c[2] = E.c[3] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float z0 = a[4 * i + 0] + g0;
+        const float z1 = a[4 * i + 1] + g1;
+        const float z2 = a[4 * i + 2] + g2;
+        const float z3 = a[4 * i + 3];
+        const float m = mhc_max(mhc_max(z0, z1), mhc_max(z2, z3));
+        const float e0 = mhc_exp2(z0 - m);
+        const float e1 = mhc_exp2(z1 - m);
+        const float e2 = mhc_exp2(z2 - m);
+        const float e3 = mhc_exp2(z3 - m);
+        const float s = (e0 + e1) + (e2 + e3);
+        const float r = mhc_rcp(s);
+        E.P[4 * i + 0] = e0 * r;
+        E.P[4 * i + 1] = e1 * r;
+        E.P[4 * i + 2] = e2 * r;
+        E.P[4 * i + 3] = e3 * r;
+        const float l = m + mhc_log2(s);
+        lse += l;
+        lse_abs += mhc_abs(l);
+        E.c[0] += E.P[4 * i + 0];
+        E.c[1] += E.P[4 * i + 1];
+        E.c[2] += E.P[4 * i + 2];
+        E.c[3] += E.P[4 * i + 3];
+    }
+    E.psi = lse - ((g0 + g1) + g2);
+    E.scale = lse_abs + (mhc_abs(g0) + mhc_abs(g1)) + mhc_abs(g2);
+    E.res = mhc_max(mhc_max(mhc_abs(E.c[0] - 1.f), mhc_abs(E.c[1] - 1.f)),
+                    mhc_max(mhc_abs(E.c[2] - 1.f), mhc_abs(E.c[3] - 1.f)));
+}
+
+// Solve L d = b for the Laplacian L of the complete graph on {0,1,2,3} with
+// edge weights w01..w23, vertex 3 grounded (d3 = 0), plus a ridge lam on the
+// three free vertices (an extra edge of weight lam from each to vertex 3).
+//
+// Gaussian elimination of a Laplacian vertex is Kron reduction: removing
+// vertex k leaves a Laplacian whose weights are w_ij + w_ik w_jk / deg(k).
+// Every quantity below is a sum of non-negative terms, so there is no
+// cancellation however small some weights are; the pivots are the vertex
+// degrees, which the ridge keeps positive.
+MHC_DEV void laplacian_solve(float w01, float w02, float w03, float w12, float w13,
+                             float w23, float lam, float b0, float b1, float b2,
+                             float& d0, float& d1, float& d2)
+{
+    w03 += lam;
+    w13 += lam;
+    w23 += lam;
+    // eliminate vertex 0
+    const float inv0 = mhc_rcp((w01 + w02) + w03);
+    const float k1 = w01 * inv0;
+    const float k2 = w02 * inv0;
+    const float w12r = w12 + w01 * k2;
+    const float w13r = w13 + w03 * k1;
+    const float w23r = w23 + w03 * k2;
+    const float b1r = b1 + k1 * b0;
+    const float b2r = b2 + k2 * b0;
+    // eliminate vertex 1
+    const float inv1 = mhc_rcp(w12r + w13r);
+    const float m2 = w12r * inv1;
+    const float w23rr = w23r + w13r * m2;
+    const float b2rr = b2r + m2 * b1r;
+    // vertex 2 is tied only to the grounded vertex now
+    d2 = b2rr * mhc_rcp(w23rr);
+    d1 = (b1r + w12r * d2) * inv1;
+    d0 = ((b0 + w01 * d1) + w02 * d2) * inv0;
+}
+
+// Edge weights W_jk = sum_i P_ij P_ik of the Hessian's Laplacian.
+struct Weights {
+    float w01, w02, w03, w12, w13, w23;
+};
+
+MHC_DEV Weights laplacian_weights(const float* P)
+{
+    Weights w;
+    w.w01 = P[0] * P[1];
+    w.w02 = P[0] * P[2];
+    w.w03 = P[0] * P[3];
+    w.w12 = P[1] * P[2];
+    w.w13 = P[1] * P[3];
+    w.w23 = P[2] * P[3];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) {
+        const float* p = P + 4 * i;
+        w.w01 = __builtin_fmaf(p[0], p[1], w.w01);
+        w.w02 = __builtin_fmaf(p[0], p[2], w.w02);
+        w.w03 = __builtin_fmaf(p[0], p[3], w.w03);
+        w.w12 = __builtin_fmaf(p[1], p[2], w.w12);
+        w.w13 = __builtin_fmaf(p[1], p[3], w.w13);
+        w.w23 = __builtin_fmaf(p[2], p[3], w.w23);
+    }
+    return w;
+}
+
+// Relative ridge: 8 eps times the trace of the reduced Hessian, plus a floor
+// that only matters when every off-diagonal weight underflowed.
+MHC_DEV float ridge(const Weights& w)
+{
+    const float tr = 2.f * (w.w01 + w.w02 + w.w12) + (w.w03 + w.w13 + w.w23);
+    return __builtin_fmaf(8.f * kFltEps, tr, 1e-30f);
+}
+
+// Iteration counter encoding for the optional per-matrix output.
+constexpr uint32_t kNotConverged = 255u;
+MHC_DEV uint32_t iters_code(int n) { return n > 254 ? 254u : (uint32_t)n; }
+
+// Forward projection of one matrix by Newton's method on the semi-dual.
+//   a_nat : the 16 logits (natural units), row-major
+//   P_out : the projected matrix
+//   returns the Newton iteration count (warm sweeps not counted), or
+//   kNotConverged when max_iters or the line search ran out first.
+MHC_DEV uint32_t project_newton(const float* a_nat, float* P_out, const SolverOpts& o)
+{
+    // base-2 logits, each row shifted so that its maximum is 0
+    float a[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float m = mhc_max(mhc_max(a_nat[4 * i], a_nat[4 * i + 1]),
+                                mhc_max(a_nat[4 * i + 2], a_nat[4 * i + 3]));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a[4 * i + j] = (a_nat[4 * i + j] - m) * kLog2e;
+    }
+
+    float g0 = 0.f, g1 = 0.f, g2 = 0.f;     // accepted potentials
+    float d0 = 0.f, d1 = 0.f, d2 = 0.f;     // current direction (base 2)
+    float t = 0.f;                          // current step length
+    float psi = 0.f, res = 0.f, slope = 0.f;
+    int warm = o.warm_sweeps;
+    int newton = 0;                         // Newton directions taken
+    int trials = 0;                         // backtracking halvings this step
+    bool first = true;
+    bool in_warm = false;
+    Eval E;
+
+    for (;;) {
+        const float t0 = g0 + t * d0, t1 = g1 + t * d1, t2 = g2 + t * d2;
+        evaluate(a, t0, t1, t2, E);
+
+        bool accept;
+        if (first || in_warm) {
+            accept = true;
+        } else {
+            // Armijo on the convex objective.  When the change of the
+            // objective is below its fp32 rounding noise (set by the size of
+            // the terms it is summed from, not by its own size) it cannot
+            // judge the step; then a step that halves the column-sum
+            // residual is taken, and one that does not means the iteration
+            // has reached the fp32 noise floor: keep the better point, stop.
+            const float armijo = psi + 1e-4f * t * slope;
+            const bool flat = mhc_abs(E.psi - psi) <= 64.f * kFltEps * E.scale;
+            accept = (E.psi <= armijo) || (flat && E.res <= 0.5f * res);
+            if (!accept && flat) {
+                if (E.res < res) {
+                    g0 = t0;
+                    g1 = t1;
+                    g2 = t2;
+                    res = E.res;
+                }
+                break;
+            }
+        }
+
+        if (accept) {
+            first = false;
+            g0 = t0;
+            g1 = t1;
+            g2 = t2;
+            psi = E.psi;
+            res = E.res;
+            trials = 0;
+            if (res <= o.tol) {
+#pragma unroll
+                for (int k = 0; k < 16; ++k) P_out[k] = E.P[k];
+                return iters_code(newton);
+            }
+            if (warm > 0) {
+                // log-domain Sinkhorn sweep: scale every column to unit sum
+                // (g_j -= log c_j), re-gauged so that g3 stays 0
+                const float l3 = mhc_log2(E.c[3]);
+                d0 = l3 - mhc_log2(E.c[0]);
+                d1 = l3 - mhc_log2(E.c[1]);
+                d2 = l3 - mhc_log2(E.c[2]);
+                t = 1.f;
+                --warm;
+                in_warm = true;
+                continue;
+            }
+            in_warm = false;
+            if (newton >= o.max_iters) break;
+            ++newton;
+            const Weights w = laplacian_weights(E.P);
+            const float lam = ridge(w);
+            float n0, n1, n2;
+            laplacian_solve(w.w01, w.w02, w.w03, w.w12, w.w13, w.w23, lam,
+                            1.f - E.c[0], 1.f - E.c[1], 1.f - E.c[2], n0, n1, n2);
+            d0 = n0 * kLog2e;
+            d1 = n1 * kLog2e;
+            d2 = n2 * kLog2e;
+            slope = (E.c[0] - 1.f) * d0 + (E.c[1] - 1.f) * d1 + (E.c[2] - 1.f) * d2;
+            const float dmax = mhc_max(mhc_max(mhc_abs(d0), mhc_abs(d1)), mhc_abs(d2));
+            t = mhc_min(1.f, kMaxStep * mhc_rcp(dmax));
+        } else {
+            if (++trials > 30) break;
+            t *= 0.5f;
+        }
+    }
+    // Stopped at the noise floor, by max_iters or by the line search:
+    // hand back the row-stochastic P of the best accepted point.
+    evaluate(a, g0, g1, g2, E);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) P_out[k] = E.P[k];
+    return E.res <= o.tol ? iters_code(newton) : kNotConverged;
+}
+
+// Forward projection of one matrix by Sinkhorn-Knopp sweeps (each sweep:
+// divide rows by their sums, then columns by theirs; Deep Signal mHC article,
+// section on Sinkhorn-Knopp).  With tol > 0 it stops once the row sums after
+// a sweep are within tol of 1 (column sums are 1 to rounding right after the
+// column step); with tol == 0 it runs exactly max_iters sweeps, the
+// fixed-count practice the summary's section 1 describes.
+MHC_DEV uint32_t project_sinkhorn(const float* a_nat, float* K, const SolverOpts& o)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float m = mhc_max(mhc_max(a_nat[4 * i], a_nat[4 * i + 1]),
+                                mhc_max(a_nat[4 * i + 2], a_nat[4 * i + 3]));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) K[4 * i + j] = mhc_exp2((a_nat[4 * i + j] - m) * kLog2e);
+    }
+    float r[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = (K[4 * i] + K[4 * i + 1]) + (K[4 * i + 2] + K[4 * i + 3]);
+    int s = 0;
+    bool done = false;
+    while (s < o.max_iters) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float inv = mhc_rcp(r[i]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) K[4 * i + j] *= inv;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float inv = mhc_rcp((K[j] + K[4 + j]) + (K[8 + j] + K[12 + j]));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) K[4 * i + j] *= inv;
+        }
+        ++s;
+        float rr = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            r[i] = (K[4 * i] + K[4 * i + 1]) + (K[4 * i + 2] + K[4 * i + 3]);
+            rr = mhc_max(rr, mhc_abs(r[i] - 1.f));
+        }
+        if (o.tol > 0.f && rr <= o.tol) {
+            done = true;
+            break;
+        }
+    }
+    if (o.tol > 0.f && !done) return kNotConverged;
+    return iters_code(s);
+}
+
+// Row-centred differences: out_j = sum_k p_k (x_j - x_k) for one row p of P
+// (sum_k p_k = 1), i.e. x_j minus the p-weighted mean of the row, written as
+// a weighted sum of differences so that no large terms cancel.
+MHC_DEV void centred_row(const float* p, const float* x, float* out)
+{
+    const float x01 = x[0] - x[1], x02 = x[0] - x[2], x03 = x[0] - x[3];
+    const float x12 = x[1] - x[2], x13 = x[1] - x[3], x23 = x[2] - x[3];
+    out[0] = __builtin_fmaf(p[3], x03, __builtin_fmaf(p[2], x02, p[1] * x01));
+    out[1] = __builtin_fmaf(p[3], x13, __builtin_fmaf(p[2], x12, -(p[0] * x01)));
+    out[2] = __builtin_fmaf(p[3], x23, __builtin_fmaf(-p[1], x12, -(p[0] * x02)));
+    out[3] = __builtin_fmaf(-p[2], x23, __builtin_fmaf(-p[1], x13, -(p[0] * x03)));
+}
+
+// Backward of the projection for one matrix (summary, section 2.2).
+// Implicit differentiation of the scaling conditions gives
+//   dA = P o (G - alpha 1^T - 1 beta^T),   (I - P^T P) beta = b - P^T a,
+//   alpha = a - P beta,   a = (P o G) 1,   b = (P o G)^T 1,   beta3 = 0,
+// and I - P^T P is the Newton Hessian at the solution (its Laplacian form,
+// rebuilt from P).  With unit row sums the same quantities are
+//   (b - P^T a)_j          = sum_i P_ij sum_k P_ik (G_ij - G_ik)
+//   G_ij - alpha_i - beta_j = sum_k P_ik (H_ij - H_ik),   H = G - 1 beta^T,
+// which are what is evaluated here: in fp32 the first forms cancel
+// catastrophically when P is close to a permutation (b and P^T a agree to
+// about the size of the true gradient), the second forms do not.
+MHC_DEV void project_bwd(const float* P, const float* G, float* dA)
+{
+    float rhs0 = 0.f, rhs1 = 0.f, rhs2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float gc[4];
+        centred_row(P + 4 * i, G + 4 * i, gc);
+        rhs0 = __builtin_fmaf(P[4 * i + 0], gc[0], rhs0);
+        rhs1 = __builtin_fmaf(P[4 * i + 1], gc[1], rhs1);
+        rhs2 = __builtin_fmaf(P[4 * i + 2], gc[2], rhs2);
+    }
+    const Weights w = laplacian_weights(P);
+    const float lam = ridge(w);
+    float be0, be1, be2;
+    laplacian_solve(w.w01, w.w02, w.w03, w.w12, w.w13, w.w23, lam, rhs0, rhs1, rhs2,
+                    be0, be1, be2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float h[4] = {G[4 * i + 0] - be0, G[4 * i + 1] - be1, G[4 * i + 2] - be2,
+                            G[4 * i + 3]};
+        float hc[4];
+        centred_row(P + 4 * i, h, hc);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dA[4 * i + j] = P[4 * i + j] * hc[j];
+    }
+}
+
+}  // namespace mhc

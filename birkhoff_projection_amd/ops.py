@@ -1,0 +1,151 @@
+"""Python entry points over the C ABI (argument marshalling only).
+
+Every function takes CUDA (HIP) tensors, checks dtype/shape/contiguity,
+passes raw device pointers and torch's current stream to ``libmhc.so`` and
+returns the output tensors.  All arithmetic runs in the gfx950 kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from ._lib import ProjOpts, check, lib
+
+SOLVERS = {"newton": 0, "sinkhorn": 1}
+
+
+def make_opts(solver="newton", max_iters=None, tol=None, warm_sweeps=None) -> ProjOpts:
+    o = ProjOpts()
+    check(lib().mhc_proj_opts_default(ctypes.byref(o)))
+    if solver not in SOLVERS:
+        raise ValueError(f"solver must be one of {sorted(SOLVERS)}")
+    o.solver = SOLVERS[solver]
+    if solver == "sinkhorn":
+        o.max_iters = 1000
+    if max_iters is not None:
+        o.max_iters = int(max_iters)
+    if tol is not None:
+        o.tol = float(tol)
+    if warm_sweeps is not None:
+        o.warm_sweeps = int(warm_sweeps)
+    return o
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtype, last_dims=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if last_dims is not None and tuple(t.shape[-len(last_dims):]) != tuple(last_dims):
+        raise ValueError(f"{name} must have trailing shape {last_dims}, got {tuple(t.shape)}")
+
+
+def birkhoff_fwd(logits: torch.Tensor, *, solver="newton", max_iters=None, tol=None,
+                 warm_sweeps=None, out=None, return_iters=False):
+    """Project [..., 4, 4] fp32 logits onto the doubly stochastic matrices.
+    Returns P (and the uint8 iteration codes if ``return_iters``)."""
+    _need(logits, "logits", torch.float32, (4, 4))
+    B = logits.numel() // 16
+    P = torch.empty_like(logits) if out is None else out
+    if out is not None:
+        _need(out, "out", torch.float32, (4, 4))
+        if out.shape != logits.shape or out.device != logits.device:
+            raise ValueError("out must match logits in shape and device")
+    iters = torch.empty(logits.shape[:-2], dtype=torch.uint8, device=logits.device) if return_iters else None
+    o = make_opts(solver, max_iters, tol, warm_sweeps)
+    with torch.cuda.device(logits.device):
+        check(lib().mhc_birkhoff_fwd(_ptr(logits), _ptr(P), B, ctypes.byref(o), _ptr(iters),
+                                     _stream(logits.device)))
+    return (P, iters) if return_iters else P
+
+
+def birkhoff_bwd(P: torch.Tensor, grad_P: torch.Tensor, out=None):
+    """dL/dlogits from P = projection(logits) and dL/dP (fp32 [..., 4, 4])."""
+    _need(P, "P", torch.float32, (4, 4))
+    _need(grad_P, "grad_P", torch.float32, (4, 4))
+    if P.shape != grad_P.shape or P.device != grad_P.device:
+        raise ValueError("P and grad_P must match in shape and device")
+    dA = torch.empty_like(P) if out is None else out
+    if out is not None:
+        _need(out, "out", torch.float32, (4, 4))
+    with torch.cuda.device(P.device):
+        check(lib().mhc_birkhoff_bwd(_ptr(P), _ptr(grad_P), _ptr(dA), P.numel() // 16,
+                                     _stream(P.device)))
+    return dA
+
+
+class BirkhoffProjection(torch.autograd.Function):
+    """Autograd wrapper: saves only P for the backward (nothing else from the
+    forward solve is needed)."""
+
+    @staticmethod
+    def forward(ctx, logits, solver="newton", max_iters=None, tol=None, warm_sweeps=None):
+        P = birkhoff_fwd(logits.contiguous(), solver=solver, max_iters=max_iters, tol=tol,
+                         warm_sweeps=warm_sweeps)
+        ctx.save_for_backward(P)
+        return P
+
+    @staticmethod
+    def backward(ctx, grad_P):
+        (P,) = ctx.saved_tensors
+        return birkhoff_bwd(P, grad_P.contiguous()), None, None, None, None
+
+
+def birkhoff_project(logits, **kw):
+    """Differentiable projection (see BirkhoffProjection)."""
+    return BirkhoffProjection.apply(logits, kw.get("solver", "newton"), kw.get("max_iters"),
+                                    kw.get("tol"), kw.get("warm_sweeps"))
+
+
+def stream_mix(x: torch.Tensor, H: torch.Tensor = None, *, logits: torch.Tensor = None,
+               out=None, return_H=False, solver="newton", max_iters=None, tol=None,
+               warm_sweeps=None):
+    """out[t,i,:] = sum_j H[t,i,j] x[t,j,:] for x [T,4,C] bf16.
+
+    Pass either ``H`` [T,4,4] fp32, or ``logits`` [T,4,4] fp32 to project in
+    the same kernel (then ``return_H`` also returns the projected H)."""
+    _need(x, "x", torch.bfloat16)
+    if x.dim() != 3:
+        raise ValueError("x must be [T, n, C]")
+    T, n, C = x.shape
+    if (H is None) == (logits is None):
+        raise ValueError("pass exactly one of H or logits")
+    src = H if H is not None else logits
+    _need(src, "H" if H is not None else "logits", torch.float32, (n, n))
+    if src.shape[0] != T:
+        raise ValueError("H/logits must have T rows")
+    y = torch.empty_like(x) if out is None else out
+    H_out = None
+    if logits is not None and return_H:
+        H_out = torch.empty_like(logits)
+    o = make_opts(solver, max_iters, tol, warm_sweeps) if logits is not None else None
+    with torch.cuda.device(x.device):
+        check(lib().mhc_stream_mix(_ptr(x), _ptr(src), _ptr(H_out), _ptr(y), T, n, C,
+                                   ctypes.byref(o) if o is not None else None,
+                                   _stream(x.device)))
+    return (y, H_out) if return_H else y
+
+
+def stream_mix_bwd(x: torch.Tensor, H: torch.Tensor, grad_out: torch.Tensor):
+    """(grad_x bf16 [T,4,C], grad_H fp32 [T,4,4]) of the stream mix."""
+    _need(x, "x", torch.bfloat16)
+    _need(grad_out, "grad_out", torch.bfloat16)
+    T, n, C = x.shape
+    _need(H, "H", torch.float32, (n, n))
+    gx = torch.empty_like(x)
+    gH = torch.empty_like(H)
+    with torch.cuda.device(x.device):
+        check(lib().mhc_stream_mix_bwd(_ptr(x), _ptr(H), _ptr(grad_out), _ptr(gx), _ptr(gH), T,
+                                       n, C, _stream(x.device)))
+    return gx, gH

@@ -1,0 +1,176 @@
+/* mhc.h -- C ABI of the MI355X (gfx950) mHC hot path.
+ *
+ * Manifold-Constrained Hyper-Connections widen the residual into n = 4
+ * parallel streams mixed by a per-token n x n matrix that is projected onto
+ * the Birkhoff polytope of doubly stochastic matrices (entries >= 0, every row
+ * and column summing to 1).  This library provides, for n = 4:
+ *
+ *   mhc_birkhoff_fwd    the projection of a batch of logit matrices
+ *   mhc_birkhoff_bwd    its gradient by implicit differentiation
+ *   mhc_stream_mix      out[t,i,:] = sum_j H[t,i,j] x[t,j,:], optionally with
+ *                       the projection of H's logits fused in
+ *   mhc_stream_mix_bwd  gradients of the stream mix
+ *   mhc_layer_fwd/bwd   one full mHC residual-layer step (RMSNorm, dynamic
+ *                       map, sigmoid read/write maps, projected residual map,
+ *                       read-mix and write-back)
+ *
+ * Sources (cited by page title and section):
+ *  - Deep Signal, "DeepSeek mHC: Manifold-Constrained Hyper-Connections"
+ *    article, sections on the Birkhoff polytope constraint and on the
+ *    Sinkhorn-Knopp projection;
+ *  - forpes.ru mHC explainer, sections "Hyper-Connections" and "mHC: bring
+ *    back the guarantee" (stream widening, read/write maps, sigmoid on the
+ *    pre/post maps);
+ *  - neo-ai mHC paper summary, section on memory-bandwidth optimisation
+ *    (fused RMSNorm + matmul + activation, mixed precision);
+ *  - gist.science summary of "Accelerating Birkhoff projection for mHC",
+ *    sections 2 (entropic-OT equivalence), 2.1 (Newton on the reduced dual,
+ *    max-shift), 2.2 (implicit differentiation, Hessian reuse).
+ *
+ * Conventions for every call
+ *  - All tensor pointers are DEVICE pointers (HBM) owned by the caller.  The
+ *    library allocates nothing and keeps no state between calls; it is safe
+ *    to call from several host threads.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Every call only enqueues work and returns; results are ready when the
+ *    stream reaches that point.
+ *  - Layouts are dense row-major (C order), no strides.  fp32 tensors must be
+ *    16-byte aligned; bf16 tensors 16-byte aligned with C a multiple of 8.
+ *  - Argument errors are detected on the host before anything is enqueued and
+ *    return MHC_ERR_INVALID_ARGUMENT (or MHC_ERR_UNSUPPORTED for n != 4); a
+ *    failed launch returns MHC_ERR_LAUNCH.  mhc_last_error() gives a message
+ *    for the calling thread's last failure.
+ *  - A batch size of 0 returns MHC_OK without enqueueing anything.
+ *  - Outputs may alias inputs only where a call says so, and then exactly
+ *    (same pointer); partial overlap is undefined and not detected.
+ *  - Inputs must be finite.  Non-convergence of the forward solver is
+ *    reported per matrix through the optional `iters` array, never as a
+ *    status code.
+ */
+#ifndef MHC_H
+#define MHC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MHC_ABI_VERSION 1
+
+typedef enum {
+    MHC_OK = 0,
+    MHC_ERR_INVALID_ARGUMENT = 1,
+    MHC_ERR_UNSUPPORTED = 2,
+    MHC_ERR_LAUNCH = 3
+} mhc_status;
+
+typedef enum {
+    MHC_SOLVER_NEWTON = 0,   /* Newton on the three column potentials */
+    MHC_SOLVER_SINKHORN = 1  /* alternating row / column normalisation */
+} mhc_solver;
+
+/* Forward-solver options.  mhc_proj_opts_default() fills the defaults. */
+typedef struct {
+    int32_t solver;      /* mhc_solver; default MHC_SOLVER_NEWTON */
+    int32_t max_iters;   /* Newton iterations (default 30) or Sinkhorn sweeps
+                            (default 1000); 1 .. 10000 */
+    float tol;           /* stop once max_j |column sum_j - 1| <= tol (rows are
+                            normalised last, so they sum to 1 up to rounding);
+                            default 1e-6.  Sinkhorn with tol == 0 runs exactly
+                            max_iters sweeps (fixed-count mode). */
+    int32_t warm_sweeps; /* log-domain Sinkhorn sweeps before the first Newton
+                            step; default 1; 0 .. 64 */
+} mhc_proj_opts;
+
+/* Iteration codes written to the optional `iters` output. */
+#define MHC_ITERS_SATURATED 254u   /* 254 or more iterations */
+#define MHC_ITERS_NOT_CONVERGED 255u
+
+/* Fill *opts with the defaults (never fails for a non-NULL pointer). */
+mhc_status mhc_proj_opts_default(mhc_proj_opts* opts);
+
+/* mhc_birkhoff_fwd -- project B logit matrices onto the doubly stochastic
+ * matrices.
+ *
+ * For each b, P[b] is the unique doubly stochastic matrix of the form
+ * diag(u) exp(logits[b]) diag(v): the limit of Sinkhorn-Knopp normalisation
+ * (Deep Signal article, Sinkhorn-Knopp section) and the entropic optimal
+ * transport plan (gist.science summary, section 2).  The Newton solver works
+ * on the three column potentials left after the row potentials are
+ * eliminated by a row softmax and one potential is fixed (summary, section
+ * 2.1), with each row max-shifted before the exponential.
+ *
+ *   logits  [B,4,4] fp32, device, 16-byte aligned (64 bytes per matrix)
+ *   P       [B,4,4] fp32, device, 16-byte aligned; may alias logits exactly
+ *   B       number of matrices, >= 0
+ *   opts    solver options, NULL = defaults; host pointer, read during the call
+ *   iters   NULL or device [B] uint8: Newton iterations (or Sinkhorn sweeps)
+ *           used, 254 = 254 or more, 255 = stopped with the column residual
+ *           above tol (fp32 noise floor, max_iters, or line-search failure);
+ *           P is then the best row-stochastic iterate reached
+ *   stream  hipStream_t
+ */
+mhc_status mhc_birkhoff_fwd(const float* logits, float* P, int64_t B,
+                            const mhc_proj_opts* opts, uint8_t* iters, void* stream);
+
+/* mhc_birkhoff_bwd -- gradient of a loss L through the projection.
+ *
+ * Given P = projection(A) and G = dL/dP, returns dL/dA by implicit
+ * differentiation of the scaling conditions (gist.science summary, section
+ * 2.2): dA = P o (G - alpha 1^T - 1 beta^T) with (I - P^T P) beta = b - P^T a,
+ * beta_3 = 0, alpha = a - P beta, a = (P o G) 1, b = (P o G)^T 1.  The system
+ * matrix is the last Newton Hessian, rebuilt from P; nothing else from the
+ * forward pass is needed.
+ *
+ *   P            [B,4,4] fp32, device, as returned by mhc_birkhoff_fwd
+ *   grad_P       [B,4,4] fp32, device
+ *   grad_logits  [B,4,4] fp32, device; may alias grad_P exactly
+ *   B >= 0, stream as above.
+ */
+mhc_status mhc_birkhoff_bwd(const float* P, const float* grad_P, float* grad_logits,
+                            int64_t B, void* stream);
+
+/* mhc_stream_mix -- apply per-token mixing matrices to the n residual streams:
+ *   out[t,i,c] = sum_j H[t,i,j] x[t,j,c]
+ * (forpes.ru explainer, "Hyper-Connections": the streams are mixed by an
+ * n x n matrix at every layer).  bf16 in and out, fp32 accumulation, the
+ * result rounded to nearest-even.
+ *
+ *   x            [T,n,C] bf16, device
+ *   H_or_logits  [T,n,n] fp32, device: the mixing matrices H when proj is
+ *                NULL, otherwise logits that are projected in the same kernel
+ *                (as mhc_birkhoff_fwd with *proj) before the mix
+ *   H_out        NULL or [T,n,n] fp32, device: receives the projected H (only
+ *                used when proj != NULL)
+ *   out          [T,n,C] bf16, device; must not overlap x
+ *   T >= 0 tokens, n == 4 (else MHC_ERR_UNSUPPORTED), C >= 8, C % 8 == 0
+ *   proj         NULL or host pointer to solver options (see above)
+ */
+mhc_status mhc_stream_mix(const void* x, const float* H_or_logits, float* H_out, void* out,
+                          int64_t T, int32_t n, int64_t C, const mhc_proj_opts* proj,
+                          void* stream);
+
+/* mhc_stream_mix_bwd -- gradients of the stream mix for upstream grad_out:
+ *   grad_x[t,j,c] = sum_i H[t,i,j] grad_out[t,i,c]     (bf16, fp32 accumulation)
+ *   grad_H[t,i,j] = sum_c grad_out[t,i,c] x[t,j,c]     (fp32)
+ *
+ *   x, grad_out  [T,n,C] bf16, device;  H [T,n,n] fp32, device
+ *   grad_x       [T,n,C] bf16, device, must not overlap the inputs
+ *   grad_H       [T,n,n] fp32, device
+ *   n == 4, C % 8 == 0 as above.
+ */
+mhc_status mhc_stream_mix_bwd(const void* x, const float* H, const void* grad_out,
+                              void* grad_x, float* grad_H, int64_t T, int32_t n, int64_t C,
+                              void* stream);
+
+const char* mhc_status_string(mhc_status s);
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char* mhc_last_error(void);
+int32_t mhc_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MHC_H */

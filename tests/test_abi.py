@@ -1,0 +1,117 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+include/mhc.h declares, and rejects bad arguments before touching the GPU.
+No GPU needed (only error paths and empty batches are called)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from birkhoff_projection_amd import _lib
+from birkhoff_projection_amd._lib import ProjOpts
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mhc.h")
+
+INVALID, UNSUPPORTED = 1, 2
+FAKE = 0x10000  # aligned address that is never dereferenced: every call below fails validation
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mhc_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert "mhc_birkhoff_fwd" in names and "mhc_stream_mix" in names
+    for name in names:
+        assert hasattr(L, name), name
+    assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
+
+
+def test_abi_version_and_strings(L):
+    assert L.mhc_abi_version() == 1
+    assert L.mhc_status_string(0) == b"ok"
+    assert L.mhc_status_string(1) == b"invalid argument"
+    assert L.mhc_status_string(2) == b"unsupported"
+    assert L.mhc_status_string(3) == b"kernel launch failed"
+
+
+def test_default_opts(L):
+    o = ProjOpts()
+    assert L.mhc_proj_opts_default(ctypes.byref(o)) == 0
+    assert (o.solver, o.max_iters, o.warm_sweeps) == (0, 30, 1)
+    assert abs(o.tol - 1e-6) < 1e-12
+    assert L.mhc_proj_opts_default(None) == INVALID
+
+
+def test_empty_batch_is_noop(L):
+    assert L.mhc_birkhoff_fwd(None, None, 0, None, None, None) == 0
+    assert L.mhc_birkhoff_bwd(None, None, None, 0, None) == 0
+    assert L.mhc_stream_mix(None, None, None, None, 0, 4, 8, None, None) == 0
+    assert L.mhc_stream_mix_bwd(None, None, None, None, None, 0, 4, 8, None) == 0
+
+
+def _err(L):
+    return L.mhc_last_error().decode()
+
+
+def test_fwd_argument_errors(L):
+    assert L.mhc_birkhoff_fwd(FAKE, FAKE, -1, None, None, None) == INVALID
+    assert "out of range" in _err(L)
+    assert L.mhc_birkhoff_fwd(None, FAKE, 5, None, None, None) == INVALID
+    assert L.mhc_birkhoff_fwd(FAKE + 4, FAKE + 4096, 5, None, None, None) == INVALID
+    assert "aligned" in _err(L)
+    # partial overlap of P and logits
+    assert L.mhc_birkhoff_fwd(FAKE, FAKE + 64, 5, None, None, None) == INVALID
+    assert "overlap" in _err(L)
+    for field, value in (("solver", 3), ("max_iters", 0), ("max_iters", 10001),
+                         ("tol", -1.0), ("tol", float("nan")), ("warm_sweeps", 65)):
+        o = ProjOpts()
+        L.mhc_proj_opts_default(ctypes.byref(o))
+        setattr(o, field, value)
+        assert L.mhc_birkhoff_fwd(FAKE, FAKE, 5, ctypes.byref(o), None, None) == INVALID, field
+        assert field in _err(L)
+
+
+def test_bwd_argument_errors(L):
+    assert L.mhc_birkhoff_bwd(FAKE, FAKE, FAKE, -3, None) == INVALID
+    assert L.mhc_birkhoff_bwd(FAKE, None, FAKE, 3, None) == INVALID
+    assert L.mhc_birkhoff_bwd(FAKE, FAKE + 8192, FAKE + 8, 3, None) == INVALID
+    # grad_logits may not overlap P at all
+    assert L.mhc_birkhoff_bwd(FAKE, FAKE + 8192, FAKE, 3, None) == INVALID
+    assert "overlaps P" in _err(L)
+
+
+def test_mix_argument_errors(L):
+    x, h, o = FAKE, FAKE + (1 << 24), FAKE + (1 << 25)
+    assert L.mhc_stream_mix(x, h, None, o, 4, 3, 64, None, None) == UNSUPPORTED
+    assert L.mhc_stream_mix(x, h, None, o, 4, 4, 12, None, None) == INVALID
+    assert L.mhc_stream_mix(x, h, None, o, 4, 4, 0, None, None) == INVALID
+    assert L.mhc_stream_mix(x, h, None, o, -1, 4, 64, None, None) == INVALID
+    assert L.mhc_stream_mix(x, None, None, o, 4, 4, 64, None, None) == INVALID
+    assert L.mhc_stream_mix(x + 2, h, None, o, 4, 4, 64, None, None) == INVALID
+    # out overlapping x
+    assert L.mhc_stream_mix(x, h, None, x + 256, 4, 4, 64, None, None) == INVALID
+    bad = ProjOpts()
+    L.mhc_proj_opts_default(ctypes.byref(bad))
+    bad.solver = 7
+    assert L.mhc_stream_mix(x, h, None, o, 4, 4, 64, ctypes.byref(bad), None) == INVALID
+    assert L.mhc_stream_mix_bwd(x, h, o, FAKE + (1 << 26), FAKE + (1 << 27), 4, 5, 64, None) == UNSUPPORTED
+    assert L.mhc_stream_mix_bwd(x, h, o, x, FAKE + (1 << 27), 4, 4, 64, None) == INVALID
+
+
+def test_python_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    import birkhoff_projection_amd as bp
+    with pytest.raises(TypeError):
+        bp.birkhoff_fwd(torch.zeros(3, 4, 4))
+    with pytest.raises(TypeError):
+        bp.stream_mix(torch.zeros(3, 4, 8, dtype=torch.bfloat16), torch.zeros(3, 4, 4))

@@ -1,0 +1,227 @@
+"""GPU parity of the Birkhoff projection kernels against the float64 oracle.
+
+Bars (per matrix):
+  forward  -- max |P_gpu - P_ref| <= 1e-5, every row and column sum of P_gpu
+              (evaluated in float64) within 1e-5 of 1, entries >= 0;
+  backward -- max |dA_gpu - dA_ref| <= 1e-4 max|dA_ref| + 1e-5 max|G|.  The
+              absolute floor is needed because near-permutation P have true
+              gradients of 1e-8 and less, far below fp32 resolution of the
+              O(1) intermediate quantities.
+The GPU backward is fed the GPU forward's P; the oracle's backward its own P.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import birkhoff_project, birkhoff_project_bwd, sinkhorn_fixed
+
+pytestmark = pytest.mark.gpu
+
+P_TOL = 1e-5
+SUM_TOL = 1e-5
+
+
+def _fwd(bp, A, **kw):
+    At = torch.from_numpy(np.ascontiguousarray(A, dtype=np.float32)).cuda()
+    P, it = bp.birkhoff_fwd(At, return_iters=True, **kw)
+    torch.cuda.synchronize()
+    return P.cpu().numpy(), it.cpu().numpy()
+
+
+def _bwd(bp, P, G):
+    dA = bp.birkhoff_bwd(torch.from_numpy(P).cuda(), torch.from_numpy(np.ascontiguousarray(G, dtype=np.float32)).cuda())
+    torch.cuda.synchronize()
+    return dA.cpu().numpy()
+
+
+def assert_fwd(P, ref, tol=P_TOL, label=""):
+    P64 = P.astype(np.float64)
+    err = np.abs(P64 - ref).max(axis=(-2, -1))
+    worst = int(np.argmax(err))
+    assert err.max() <= tol, f"{label}: P error {err.max():.3e} at {worst}"
+    assert (P >= 0).all(), label
+    rs = np.abs(P64.sum(-1) - 1).max()
+    cs = np.abs(P64.sum(-2) - 1).max()
+    assert rs <= SUM_TOL and cs <= SUM_TOL, f"{label}: sums {rs:.2e} {cs:.2e}"
+    return err
+
+
+def assert_bwd(dA, ref, G, label=""):
+    tol = 1e-4 * np.abs(ref).max(axis=(-2, -1)) + 1e-5 * np.abs(G).max(axis=(-2, -1))
+    ratio = np.abs(dA.astype(np.float64) - ref).max(axis=(-2, -1)) / tol
+    worst = int(np.argmax(ratio))
+    assert ratio.max() <= 1.0, f"{label}: gradient error {ratio.max():.3f} x tolerance at {worst}"
+    return ratio
+
+
+@pytest.mark.parametrize("kind", ["normal1", "normal10", "diag20", "normal2"])
+@pytest.mark.parametrize("B", [1, 63, 64, 65, 257, 4099])
+def test_fwd_bwd_ragged(gpu_lib, kind, B):
+    print(f"fwd/bwd parity kind={kind} B={B}", flush=True)
+    A = W.logits_batch(kind, B, 100 + B)
+    G = W.grad_batch(B, 200 + B)
+    P, it = _fwd(gpu_lib, A)
+    ref = birkhoff_project(A.astype(np.float64))
+    assert_fwd(P, ref, label=f"{kind} B={B}")
+    assert it.shape == (B,)
+    dA = _bwd(gpu_lib, P, G)
+    assert_bwd(dA, birkhoff_project_bwd(ref, G.astype(np.float64)), G, label=f"{kind} B={B}")
+
+
+def test_config1_forward(gpu_lib):
+    """4096 N(0,1) matrices, seed 0: every matrix converged (column residual
+    <= 1e-6 by the kernel's own fp32 test) and matches the oracle."""
+    A = W.config1()
+    P, it = _fwd(gpu_lib, A)
+    assert (it != 255).all()
+    ref = birkhoff_project(A.astype(np.float64))
+    assert_fwd(P, ref, label="config1")
+    # sums evaluated in float64 of the fp32 output: within the fp32 rounding of P
+    P64 = P.astype(np.float64)
+    assert np.abs(P64.sum(-2) - 1).max() <= 1.5e-6
+    assert np.abs(P64.sum(-1) - 1).max() <= 1.5e-6
+
+
+def _sample(n_total, n_pick, seed, must=()):
+    g = np.random.Generator(np.random.PCG64(seed))
+    idx = g.choice(n_total, size=min(n_pick, n_total), replace=False)
+    return np.unique(np.concatenate([idx, np.asarray(must, dtype=np.int64)]))
+
+
+def test_config2_full(gpu_lib):
+    """131072 N(0,10^2) matrices (seed 2) in one launch each for fwd and bwd,
+    as bench.py times them.  All outputs: non-negativity, sums, flags.
+    Oracle parity on 12288 sampled matrices plus every flagged one."""
+    A, G = W.config2()
+    P, it = _fwd(gpu_lib, A)
+    dA = _bwd(gpu_lib, P, G)
+    P64 = P.astype(np.float64)
+    assert (P >= 0).all()
+    assert np.abs(P64.sum(-1) - 1).max() <= SUM_TOL
+    assert np.abs(P64.sum(-2) - 1).max() <= SUM_TOL
+    flagged = np.nonzero(it == 255)[0]
+    assert flagged.size <= 0.001 * A.shape[0], f"{flagged.size} unconverged"
+    # gradients of a projection have zero row and column sums
+    assert np.abs(dA.astype(np.float64).sum(-1)).max() <= 1e-4
+    idx = _sample(A.shape[0], 12288, 7, must=flagged)
+    ref = birkhoff_project(A[idx].astype(np.float64))
+    assert_fwd(P[idx], ref, label="config2")
+    assert_bwd(dA[idx], birkhoff_project_bwd(ref, G[idx].astype(np.float64)), G[idx], label="config2")
+
+
+def test_config3_full(gpu_lib):
+    """1,048,576 mixed-difficulty matrices (seed 3).  All outputs checked for
+    the doubly stochastic properties; 16384 sampled per distribution against
+    the oracle, plus every flagged matrix."""
+    A, G, kind = W.config3()
+    P, it = _fwd(gpu_lib, A)
+    dA = _bwd(gpu_lib, P, G)
+    P64 = P.astype(np.float64)
+    assert (P >= 0).all()
+    assert np.abs(P64.sum(-1) - 1).max() <= SUM_TOL
+    assert np.abs(P64.sum(-2) - 1).max() <= SUM_TOL
+    flagged = np.nonzero(it == 255)[0]
+    assert flagged.size <= 0.001 * A.shape[0]
+    g = np.random.Generator(np.random.PCG64(9))
+    picks = [g.choice(np.nonzero(kind == k)[0], 4096, replace=False) for k in range(3)]
+    idx = np.unique(np.concatenate(picks + [flagged]))
+    ref = birkhoff_project(A[idx].astype(np.float64))
+    assert_fwd(P[idx], ref, label="config3")
+    assert_bwd(dA[idx], birkhoff_project_bwd(ref, G[idx].astype(np.float64)), G[idx], label="config3")
+    # near-identity inputs converge without a Newton step
+    assert (it[kind == 2] == 0).mean() > 0.99
+
+
+def test_equivariance_on_gpu(gpu_lib):
+    A = np.concatenate([W.logits_batch("normal1", 500, 31), W.logits_batch("normal10", 500, 32)])
+    P, _ = _fwd(gpu_lib, A)
+    p1, p2 = [2, 0, 3, 1], [1, 3, 0, 2]
+    Pp, _ = _fwd(gpu_lib, A[:, p1][:, :, p2])
+    assert np.abs(Pp - P[:, p1][:, :, p2]).max() <= 2 * P_TOL
+    Pt, _ = _fwd(gpu_lib, np.swapaxes(A, 1, 2))
+    assert np.abs(Pt - np.swapaxes(P, 1, 2)).max() <= 2 * P_TOL
+
+
+def test_closed_forms_on_gpu(gpu_lib):
+    """Rank-one logits give J/4; t*I gives e^t/(e^t+3) on the diagonal."""
+    g = np.random.Generator(np.random.PCG64(33))
+    u = g.standard_normal((256, 4, 1)) * 5
+    v = g.standard_normal((256, 1, 4)) * 5
+    P, it = _fwd(gpu_lib, (u + v).astype(np.float32))
+    assert np.abs(P - 0.25).max() <= P_TOL
+    t = np.linspace(-5, 12, 64)
+    A = (t[:, None, None] * np.eye(4)[None]).astype(np.float32)
+    P, _ = _fwd(gpu_lib, A)
+    a = np.exp(t) / (np.exp(t) + 3)
+    b = 1 / (np.exp(t) + 3)
+    want = b[:, None, None] + (a - b)[:, None, None] * np.eye(4)
+    assert np.abs(P - want).max() <= P_TOL
+
+
+def test_extreme_logits(gpu_lib):
+    """Very large magnitudes (N(0,40^2)) still give finite doubly stochastic P."""
+    A = (40.0 * np.random.Generator(np.random.PCG64(34)).standard_normal((2048, 4, 4))).astype(np.float32)
+    P, it = _fwd(gpu_lib, A)
+    assert np.isfinite(P).all()
+    ref = birkhoff_project(A.astype(np.float64))
+    ok = it != 255
+    assert ok.mean() > 0.99
+    assert_fwd(P[ok], ref[ok], tol=2e-5, label="N(0,40^2)")
+
+
+def test_inplace_alias(gpu_lib):
+    A = W.logits_batch("normal10", 1000, 35)
+    At = torch.from_numpy(A).cuda()
+    P_sep = gpu_lib.birkhoff_fwd(At.clone())
+    gpu_lib.birkhoff_fwd(At, out=At)
+    torch.cuda.synchronize()
+    assert torch.equal(P_sep, At)
+    G = torch.from_numpy(W.grad_batch(1000, 36)).cuda()
+    d_sep = gpu_lib.birkhoff_bwd(P_sep, G.clone())
+    gpu_lib.birkhoff_bwd(P_sep, G, out=G)
+    torch.cuda.synchronize()
+    assert torch.equal(d_sep, G)
+
+
+def test_max_iters_flags_and_nan(gpu_lib):
+    """Capping Newton at one iteration flags most large-magnitude matrices as
+    not converged (255) while P stays row-stochastic; a NaN matrix is flagged
+    and does not disturb its neighbours; the call returns (bounded loop)."""
+    A = W.logits_batch("normal10", 512, 37)
+    P, it = _fwd(gpu_lib, A, max_iters=1)
+    assert (it == 255).mean() > 0.5
+    assert np.abs(P.astype(np.float64).sum(-1) - 1).max() <= 1e-5
+    A2 = W.logits_batch("normal1", 130, 38)
+    A2[64, 1, 2] = np.nan
+    P2, it2 = _fwd(gpu_lib, A2)
+    assert it2[64] == 255
+    assert np.isnan(P2[64]).any()
+    good = np.arange(130) != 64
+    assert_fwd(P2[good], birkhoff_project(A2[good].astype(np.float64)), label="nan neighbours")
+
+
+def test_sinkhorn_mode(gpu_lib):
+    """Sinkhorn solver: to tolerance on N(0,1), and the fixed 20-sweep mode
+    against the oracle's own fixed-count Sinkhorn (float64)."""
+    A = W.logits_batch("normal1", 2000, 39)
+    P, it = _fwd(gpu_lib, A, solver="sinkhorn", tol=1e-6, max_iters=1000)
+    assert (it != 255).all()
+    assert_fwd(P, birkhoff_project(A.astype(np.float64)), label="sinkhorn tol")
+    for kind in ("normal1", "normal2"):
+        A = W.logits_batch(kind, 2000, 40)
+        P, it = _fwd(gpu_lib, A, solver="sinkhorn", tol=0.0, max_iters=20)
+        assert (it == 20).all()
+        ref = sinkhorn_fixed(A.astype(np.float64), 20)
+        assert np.abs(P.astype(np.float64) - ref).max() <= 1e-5, kind
+
+
+def test_autograd_function(gpu_lib):
+    A = torch.from_numpy(W.logits_batch("normal1", 300, 41)).cuda().requires_grad_(True)
+    G = torch.from_numpy(W.grad_batch(300, 42)).cuda()
+    P = gpu_lib.birkhoff_project(A)
+    (P * G).sum().backward()
+    torch.cuda.synchronize()
+    ref = birkhoff_project(A.detach().cpu().numpy().astype(np.float64))
+    dref = birkhoff_project_bwd(ref, G.cpu().numpy().astype(np.float64))
+    assert_bwd(A.grad.cpu().numpy(), dref, G.cpu().numpy(), label="autograd")
