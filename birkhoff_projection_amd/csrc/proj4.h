@@ -44,6 +44,11 @@ constexpr float kFltEps = 1.1920928955078125e-07f;
 // units; starting the backtracking at this length instead saves the many
 // halvings that would otherwise be spent getting back down.
 constexpr float kMaxStep = 8.f;
+// The noise-floor stop below is only allowed once the column residual is this
+// small; farther out a step that does not lower the residual is backtracked.
+constexpr float kFlatResidual = 1e-4f;
+// Floor on a column mass before its logarithm is taken.
+constexpr float kMinMass = 7.8886091e-31f;  // 2^-100
 
 // Solver selection and limits (mirrors mhc_proj_opts of the public header).
 struct SolverOpts {
@@ -209,23 +214,20 @@ MHC_DEV uint32_t project_newton(const float* a_nat, float* P_out, const SolverOp
         if (first || in_warm) {
             accept = true;
         } else {
-            // Armijo on the convex objective.  When the change of the
-            // objective is below its fp32 rounding noise (set by the size of
-            // the terms it is summed from, not by its own size) it cannot
-            // judge the step; then a step that halves the column-sum
-            // residual is taken, and one that does not means the iteration
-            // has reached the fp32 noise floor: keep the better point, stop.
-            const float armijo = psi + 1e-4f * t * slope;
-            const bool flat = mhc_abs(E.psi - psi) <= 64.f * kFltEps * E.scale;
-            accept = (E.psi <= armijo) || (flat && E.res <= 0.5f * res);
-            if (!accept && flat) {
-                if (E.res < res) {
-                    g0 = t0;
-                    g1 = t1;
-                    g2 = t2;
-                    res = E.res;
-                }
-                break;
+            // Armijo on the convex objective -- while it can judge the step.
+            // Close to the solution the change a Newton step predicts,
+            // |t slope|, falls below the fp32 rounding noise of the objective
+            // (set by the size of the terms it is summed from, not by its own
+            // size).  From there on the column-sum residual decides: a step
+            // that lowers it is taken; one that does not is backtracked, or,
+            // once the residual is already small, marks the fp32 noise floor
+            // and ends the solve at the better point.
+            const bool unresolved = t * mhc_abs(slope) <= 64.f * kFltEps * E.scale;
+            if (unresolved) {
+                accept = E.res < res;
+                if (!accept && res <= kFlatResidual) break;
+            } else {
+                accept = E.psi <= psi + 1e-4f * t * slope;
             }
         }
 
@@ -244,11 +246,13 @@ MHC_DEV uint32_t project_newton(const float* a_nat, float* P_out, const SolverOp
             }
             if (warm > 0) {
                 // log-domain Sinkhorn sweep: scale every column to unit sum
-                // (g_j -= log c_j), re-gauged so that g3 stays 0
-                const float l3 = mhc_log2(E.c[3]);
-                d0 = l3 - mhc_log2(E.c[0]);
-                d1 = l3 - mhc_log2(E.c[1]);
-                d2 = l3 - mhc_log2(E.c[2]);
+                // (g_j -= log c_j), re-gauged so that g3 stays 0.  A column
+                // whose entries all underflowed has c_j = 0; its mass is
+                // floored so that the step stays finite (a factor 2^100).
+                const float l3 = mhc_log2(mhc_max(E.c[3], kMinMass));
+                d0 = l3 - mhc_log2(mhc_max(E.c[0], kMinMass));
+                d1 = l3 - mhc_log2(mhc_max(E.c[1], kMinMass));
+                d2 = l3 - mhc_log2(mhc_max(E.c[2], kMinMass));
                 t = 1.f;
                 --warm;
                 in_warm = true;

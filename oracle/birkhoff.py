@@ -47,6 +47,7 @@ from __future__ import annotations
 import numpy as np
 
 SINKHORN_TOL = 1e-13
+EXTREME_SPREAD = 600.0
 
 
 def residual(P: np.ndarray) -> np.ndarray:
@@ -105,7 +106,7 @@ def _dual_value(L, f, g):
     return P.sum(axis=(1, 2)) - f.sum(axis=1) - g.sum(axis=1)
 
 
-def newton_two_sided(L, f, g, iters=60, tol=SINKHORN_TOL):
+def newton_two_sided(L, f, g, iters=60, tol=SINKHORN_TOL, max_step=30.0):
     """Newton's method on the two-sided dual (f, g) for a batch, float64.
 
     Hessian [[diag r, P], [P^T, diag c]] is singular along (1, -1); the gauge
@@ -139,6 +140,11 @@ def newton_two_sided(L, f, g, iters=60, tol=SINKHORN_TOL):
         H[:, 2 * n, :2 * n] = e
         rhs = np.concatenate([-grad[idx], np.zeros((m, 1))], axis=1)
         step = np.linalg.solve(H, rhs[:, :, None])[:, :2 * n, 0]
+        # Near-decomposable matrices make the system nearly singular and the
+        # Newton step enormous along the weakly coupled direction; the line
+        # search starts from a step no longer than max_step instead.
+        smax = np.abs(step).max(axis=1)
+        step = step * np.minimum(1.0, max_step / np.maximum(smax, 1e-300))[:, None]
         df, dg = step[:, :n], step[:, n:]
         fa, ga, La = f[idx], g[idx], L[idx]
         phi0 = _dual_value(La, fa, ga)
@@ -159,6 +165,8 @@ def newton_two_sided(L, f, g, iters=60, tol=SINKHORN_TOL):
             newly = todo & ok
             accepted |= newly
             t = np.where(todo & ~ok, 0.5 * t, t)
+        # a matrix whose line search found no acceptable step keeps its point
+        t = np.where(accepted, t, 0.0)
         f[idx] = fa + t[:, None] * df
         g[idx] = ga + t[:, None] * dg
     return f, g
@@ -244,8 +252,13 @@ def birkhoff_project(A, tol=SINKHORN_TOL, max_sweeps=100, newton_iters=60,
         A = A[None]
     if not np.all(np.isfinite(A)):
         raise ValueError("oracle: logits must be finite")
-    P, f, g, sweeps, conv = sinkhorn(A, tol=tol, max_sweeps=max_sweeps)
-    polished = ~conv
+    # a row spread beyond ~700 underflows float64 exp to exact zeros, which
+    # can leave no representable scaling: such matrices go to mpmath directly
+    extreme = (A.max(axis=-1) - A.min(axis=-1)).max(axis=-1) > EXTREME_SPREAD
+    P, f, g, sweeps, conv = sinkhorn(np.where(extreme[:, None, None], 0.0, A), tol=tol,
+                                     max_sweeps=max_sweeps)
+    conv &= ~extreme
+    polished = ~conv & ~extreme
     mp_used = np.zeros(A.shape[0], dtype=bool)
     if polished.any():
         idx = np.nonzero(polished)[0]
@@ -255,7 +268,7 @@ def birkhoff_project(A, tol=SINKHORN_TOL, max_sweeps=100, newton_iters=60,
         Q = Q / Q.sum(axis=2, keepdims=True)
         Q = Q / Q.sum(axis=1, keepdims=True)
         P[idx] = Q
-    bad = np.nonzero(residual(P) >= tol)[0]
+    bad = np.nonzero((residual(P) >= tol) | extreme)[0]
     for b in bad:
         P[b] = _mp_project_one(A[b])
         mp_used[b] = True

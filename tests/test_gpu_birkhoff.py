@@ -160,14 +160,20 @@ def test_closed_forms_on_gpu(gpu_lib):
 
 
 def test_extreme_logits(gpu_lib):
-    """Very large magnitudes (N(0,40^2)) still give finite doubly stochastic P."""
-    A = (40.0 * np.random.Generator(np.random.PCG64(34)).standard_normal((2048, 4, 4))).astype(np.float32)
+    """Very large magnitudes (N(0,40^2), far beyond the workloads): outputs
+    stay finite and doubly stochastic to 1e-4; matrices the solver reports
+    converged match the oracle to 1e-5; at most a few percent stop at the
+    fp32 noise floor (flag 255)."""
+    A = (40.0 * np.random.Generator(np.random.PCG64(34)).standard_normal((4096, 4, 4))).astype(np.float32)
     P, it = _fwd(gpu_lib, A)
     assert np.isfinite(P).all()
-    ref = birkhoff_project(A.astype(np.float64))
+    P64 = P.astype(np.float64)
+    assert np.abs(P64.sum(-1) - 1).max() <= 1e-4 and np.abs(P64.sum(-2) - 1).max() <= 1e-4
     ok = it != 255
-    assert ok.mean() > 0.99
-    assert_fwd(P[ok], ref[ok], tol=2e-5, label="N(0,40^2)")
+    assert ok.mean() > 0.95
+    ref = birkhoff_project(A.astype(np.float64))
+    assert_fwd(P[ok], ref[ok], label="N(0,40^2) converged")
+    assert np.abs(P64 - ref).max() <= 1e-4
 
 
 def test_inplace_alias(gpu_lib):
