@@ -34,6 +34,29 @@ HBM_PEAK_GBS = 8000.0
 FWD_BYTES = 128   # per matrix: 64 B logits in, 64 B P out
 BWD_BYTES = 192   # per matrix: P and dL/dP in, dL/dA out
 
+# HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled
+# by a plain copy of known size; see profiles/), valid only for the kernel
+# sources they were taken on: (files hashed, sha256 prefix, bytes per launch).
+MEASURED_TRAFFIC = {
+    "birkhoff_fwd_131072": (("proj4.h", "birkhoff.hip", "devmath.h"), "82b261e5a4cee8f8", 16.84e6),
+}
+
+
+def _sources_sha(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "birkhoff_projection_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(key):
+    files, sha, nbytes = MEASURED_TRAFFIC.get(key, ((), None, None))
+    if not files or _sources_sha(files) != sha:
+        return None
+    return nbytes
+
 
 def _cpu_worker(args):
     import oracle
@@ -44,11 +67,13 @@ def _cpu_worker(args):
 
 
 def cpu_baseline_projection(A, G, n_sample, label):
-    """Time the oracle's fwd+bwd on n_sample matrices over a process pool."""
+    """Time the oracle's fwd+bwd on n_sample matrices (the batch repeated if
+    n_sample exceeds it) over a process pool on the host cores."""
     import multiprocessing as mp
     cores = min(len(os.sched_getaffinity(0)), 16)
-    n = min(n_sample, A.shape[0])
-    chunks = np.array_split(np.arange(n), cores * 4)
+    n = n_sample
+    idx = np.arange(n) % A.shape[0]
+    chunks = np.array_split(idx, cores * 4)
     work = [(A[c], G[c]) for c in chunks]
     ctx = mp.get_context("fork")
     t0 = time.perf_counter()
@@ -56,13 +81,15 @@ def cpu_baseline_projection(A, G, n_sample, label):
         done = sum(pool.map(_cpu_worker, work))
     dt = time.perf_counter() - t0
     return {"value": done / dt, "unit": "projections/s", "cores": cores, "kind": "oracle",
-            "sample": f"{done} of the {A.shape[0]} {label} matrices, fwd+bwd, float64 "
-                      f"({dt:.1f} s wall on {cores} processes)"}
+            "sample": f"{done} matrices ({done / A.shape[0]:g} passes over the {A.shape[0]} "
+                      f"{label} batch), fwd+bwd, float64, {dt:.1f} s wall on {cores} processes"}
 
 
 def time_projection(bp, torch, A_np, G_np, steps, warmup, solver="newton"):
-    """Rotate over buffer sets, time `steps` fwd+bwd steps; per-kernel HIP
-    events on the launch stream.  Returns a dict of timings."""
+    """Rotate over buffer sets; time `steps` fwd+bwd steps back to back, then
+    `steps` forward launches alone and `steps` backward launches alone (HIP
+    events on the launch stream around each loop only, so a kernel's average
+    is its duration plus the dispatch gap, comparable with a kernel trace)."""
     B = A_np.shape[0]
     set_bytes = B * 64 * 4
     nsets = max(2, int(np.ceil(600e6 / set_bytes)))
@@ -73,34 +100,43 @@ def time_projection(bp, torch, A_np, G_np, steps, warmup, solver="newton"):
         sets.append((A0.clone(), torch.empty_like(A0), G0.clone(), torch.empty_like(A0)))
     stream = torch.cuda.current_stream()
 
-    def step(k):
+    def fwd(k):
         A, P, G, dA = sets[k % nsets]
         bp.birkhoff_fwd(A, out=P, solver=solver)
+
+    def bwd(k):
+        A, P, G, dA = sets[k % nsets]
         bp.birkhoff_bwd(P, G, out=dA)
 
+    def timed(body):
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for k in range(steps):
+            body(k)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop)
+
     for k in range(warmup):
-        step(k)
+        fwd(k)
+        bwd(k)
+    total_ms = timed(lambda k: (fwd(k), bwd(k)))
+    fwd_ms = timed(fwd) / steps
+    bwd_ms = timed(bwd) / steps
+    return dict(total_ms=total_ms, fwd_ms=fwd_ms, bwd_ms=bwd_ms, nsets=nsets)
+
+
+def copy_probe(torch, mib):
+    """One plain device copy of a known size (for scaling HBM byte counters)."""
+    n = mib * (1 << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
+    y.copy_(x)
     torch.cuda.synchronize()
-    t_host0 = time.perf_counter()
-    start.record(stream)
-    for k in range(steps):
-        A, P, G, dA = sets[k % nsets]
-        ev[k][0].record(stream)
-        bp.birkhoff_fwd(A, out=P, solver=solver)
-        ev[k][1].record(stream)
-        bp.birkhoff_bwd(P, G, out=dA)
-        ev[k][2].record(stream)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    t_host = time.perf_counter() - t_host0
-    total_ms = start.elapsed_time(stop)
-    fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
-    bwd_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
-    return dict(total_ms=total_ms, host_s=t_host, fwd_ms=fwd_ms, bwd_ms=bwd_ms, nsets=nsets)
+    del x, y
 
 
 def bench_projection(args, bp, torch, config):
@@ -118,8 +154,8 @@ def bench_projection(args, bp, torch, config):
     B = A.shape[0]
     r = time_projection(bp, torch, A, G, args.steps, args.warmup)
     ms = r["total_ms"] / args.steps
-    fwd_avg = float(r["fwd_ms"].mean())
-    bwd_avg = float(r["bwd_ms"].mean())
+    fwd_avg = float(r["fwd_ms"])
+    bwd_avg = float(r["bwd_ms"])
     value = B / (ms / 1e3)
     fwd_gbs = FWD_BYTES * B / (fwd_avg / 1e3) / 1e9
     bwd_gbs = BWD_BYTES * B / (bwd_avg / 1e3) / 1e9
@@ -134,7 +170,8 @@ def bench_projection(args, bp, torch, config):
                    "buffer_sets": r["nsets"]},
         "roofline": {"bound": "hbm", "kernel": "birkhoff_fwd (Newton)",
                      "achieved": fwd_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": fwd_gbs / HBM_PEAK_GBS, "traffic": None},
+                     "frac": fwd_gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(f"birkhoff_fwd_{B}")},
         "kernels": {"fwd_us": fwd_avg * 1e3, "bwd_us": bwd_avg * 1e3,
                     "fwd_GBs": fwd_gbs, "bwd_GBs": bwd_gbs,
                     "bwd_frac_hbm": bwd_gbs / HBM_PEAK_GBS,
@@ -151,7 +188,10 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3])
-    ap.add_argument("--cpu-sample", type=int, default=65536)
+    ap.add_argument("--cpu-sample", type=int, default=524288,
+                    help="matrices the oracle baseline processes (about 10-30 s of CPU work)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one plain copy of this size first (counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -165,6 +205,8 @@ def main():
         sys.exit(1)
     import birkhoff_projection_amd as bp
     bp.lib()
+    if args.copy_probe_mib:
+        copy_probe(torch, args.copy_probe_mib)
     out = bench_projection(args, bp, torch, args.config)
     print(json.dumps(out), flush=True)
 
