@@ -8,7 +8,9 @@ for device memory and streams.
 """
 from ._lib import LIB_PATH, MHCError, lib
 from .ops import (BirkhoffProjection, birkhoff_bwd, birkhoff_fwd, birkhoff_project,
-                  make_opts, stream_mix, stream_mix_bwd)
+                  layer_bwd, layer_fwd, layer_workspace, make_opts, stream_mix,
+                  stream_mix_bwd)
 
 __all__ = ["LIB_PATH", "MHCError", "lib", "BirkhoffProjection", "birkhoff_bwd",
-           "birkhoff_fwd", "birkhoff_project", "make_opts", "stream_mix", "stream_mix_bwd"]
+           "birkhoff_fwd", "birkhoff_project", "layer_bwd", "layer_fwd", "layer_workspace",
+           "make_opts", "stream_mix", "stream_mix_bwd"]

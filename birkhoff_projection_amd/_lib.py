@@ -22,6 +22,19 @@ class ProjOpts(ctypes.Structure):
                 ("tol", ctypes.c_float), ("warm_sweeps", ctypes.c_int32)]
 
 
+class LayerArgs(ctypes.Structure):
+    """Mirror of ``mhc_layer_args``."""
+    _fields_ = [("T", ctypes.c_int64), ("n", ctypes.c_int32), ("C", ctypes.c_int64),
+                ("eps", ctypes.c_float), ("proj", ctypes.POINTER(ProjOpts)),
+                ("x", c_void_p), ("W", c_void_p), ("f", c_void_p),
+                ("u", c_void_p), ("x_out", c_void_p), ("rms", c_void_p), ("logits", c_void_p),
+                ("H_pre", c_void_p), ("H_post", c_void_p), ("H_res", c_void_p),
+                ("grad_x_out", c_void_p), ("grad_u", c_void_p),
+                ("grad_x", c_void_p), ("grad_f", c_void_p), ("grad_W", c_void_p),
+                ("grad_logits", c_void_p), ("workspace", c_void_p),
+                ("workspace_bytes", ctypes.c_int64)]
+
+
 # name -> (restype, argtypes), exactly as declared in include/mhc.h
 SIGNATURES = {
     "mhc_proj_opts_default": (c_int32, [ctypes.POINTER(ProjOpts)]),
@@ -32,6 +45,9 @@ SIGNATURES = {
                                  c_int64, ctypes.POINTER(ProjOpts), c_void_p]),
     "mhc_stream_mix_bwd": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int64,
                                      c_int32, c_int64, c_void_p]),
+    "mhc_layer_workspace_bytes": (c_int64, [c_int64, c_int32, c_int64]),
+    "mhc_layer_fwd": (c_int32, [ctypes.POINTER(LayerArgs), c_void_p]),
+    "mhc_layer_bwd": (c_int32, [ctypes.POINTER(LayerArgs), c_void_p]),
     "mhc_status_string": (ctypes.c_char_p, [c_int32]),
     "mhc_last_error": (ctypes.c_char_p, []),
     "mhc_abi_version": (c_int32, []),

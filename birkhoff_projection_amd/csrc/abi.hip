@@ -168,6 +168,107 @@ mhc_status mhc_stream_mix_bwd(const void* x, const float* H, const void* grad_ou
                     "stream_mix_bwd launch");
 }
 
+static mhc_status check_layer_shape(int64_t T, int32_t n, int64_t C)
+{
+    if (n != 4) return fail(MHC_ERR_UNSUPPORTED, "only n = 4 streams are supported (got %d)", n);
+    if (T < 0 || T > kMaxTokens) return fail(MHC_ERR_INVALID_ARGUMENT, "T=%lld out of range", (long long)T);
+    if (C < 64 || C % 64 != 0 || C > ((int64_t)1 << 24))
+        return fail(MHC_ERR_INVALID_ARGUMENT, "C must be a positive multiple of 64 (got %lld)", (long long)C);
+    return MHC_OK;
+}
+
+int64_t mhc_layer_workspace_bytes(int64_t T, int32_t n, int64_t C)
+{
+    if (check_layer_shape(T, n, C) != MHC_OK) return -1;
+    return mhc::layer_plan(T, C).bytes;
+}
+
+namespace {
+
+struct Buf {
+    const void* p;
+    size_t bytes;
+    const char* name;
+};
+
+// every pointer non-NULL and 16-byte aligned; no two buffers overlap
+static mhc_status check_buffers(const Buf* b, int nb)
+{
+    for (int i = 0; i < nb; ++i) {
+        if (b[i].p == nullptr) return fail(MHC_ERR_INVALID_ARGUMENT, "%s must not be NULL", b[i].name);
+        if (!aligned16(b[i].p)) return fail(MHC_ERR_INVALID_ARGUMENT, "%s must be 16-byte aligned", b[i].name);
+    }
+    for (int i = 0; i < nb; ++i)
+        for (int j = i + 1; j < nb; ++j)
+            if (overlap(b[i].p, b[i].bytes, b[j].p, b[j].bytes))
+                return fail(MHC_ERR_INVALID_ARGUMENT, "%s overlaps %s", b[i].name, b[j].name);
+    return MHC_OK;
+}
+
+}  // namespace
+
+mhc_status mhc_layer_fwd(const mhc_layer_args* a, void* stream)
+{
+    if (a == nullptr) return fail(MHC_ERR_INVALID_ARGUMENT, "args is NULL");
+    mhc_status s = check_layer_shape(a->T, a->n, a->C);
+    if (s != MHC_OK) return s;
+    if (!(a->eps > 0.f) || !(a->eps < 1.f)) return fail(MHC_ERR_INVALID_ARGUMENT, "eps must be in (0, 1)");
+    mhc::SolverOpts o;
+    s = check_opts(a->proj, &o);
+    if (s != MHC_OK) return s;
+    if (a->T == 0) return ok();
+    const size_t T = (size_t)a->T, C = (size_t)a->C;
+    const Buf b[] = {{a->x, T * 4 * C * 2, "x"},          {a->W, 24 * 4 * C * 2, "W"},
+                     {a->f, T * C * 2, "f"},              {a->u, T * C * 2, "u"},
+                     {a->x_out, T * 4 * C * 2, "x_out"},  {a->rms, T * 4, "rms"},
+                     {a->logits, T * 96, "logits"},       {a->H_pre, T * 16, "H_pre"},
+                     {a->H_post, T * 16, "H_post"},       {a->H_res, T * 64, "H_res"}};
+    s = check_buffers(b, sizeof(b) / sizeof(b[0]));
+    if (s != MHC_OK) return s;
+    const mhc::LayerPtrs p{a->x,   a->W,      a->f,     a->u,     a->x_out, a->rms,
+                           a->logits, a->H_pre, a->H_post, a->H_res, nullptr, nullptr,
+                           nullptr, nullptr,  nullptr,  nullptr,  nullptr};
+    return launched(mhc::launch_layer_fwd(p, a->T, a->C, a->eps, o, (hipStream_t)stream),
+                    "layer_fwd launch");
+}
+
+mhc_status mhc_layer_bwd(const mhc_layer_args* a, void* stream)
+{
+    if (a == nullptr) return fail(MHC_ERR_INVALID_ARGUMENT, "args is NULL");
+    mhc_status s = check_layer_shape(a->T, a->n, a->C);
+    if (s != MHC_OK) return s;
+    if (a->T == 0) return ok();
+    const size_t T = (size_t)a->T, C = (size_t)a->C;
+    const int64_t need = mhc::layer_plan(a->T, a->C).bytes;
+    if (a->workspace_bytes < need)
+        return fail(MHC_ERR_INVALID_ARGUMENT, "workspace_bytes=%lld < %lld required",
+                    (long long)a->workspace_bytes, (long long)need);
+    if (((uintptr_t)a->workspace & 255u) != 0)
+        return fail(MHC_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    const Buf b[] = {{a->x, T * 4 * C * 2, "x"},
+                     {a->W, 24 * 4 * C * 2, "W"},
+                     {a->f, T * C * 2, "f"},
+                     {a->rms, T * 4, "rms"},
+                     {a->logits, T * 96, "logits"},
+                     {a->H_pre, T * 16, "H_pre"},
+                     {a->H_post, T * 16, "H_post"},
+                     {a->H_res, T * 64, "H_res"},
+                     {a->grad_x_out, T * 4 * C * 2, "grad_x_out"},
+                     {a->grad_u, T * C * 2, "grad_u"},
+                     {a->grad_x, T * 4 * C * 2, "grad_x"},
+                     {a->grad_f, T * C * 2, "grad_f"},
+                     {a->grad_W, 24 * 4 * C * 4, "grad_W"},
+                     {a->grad_logits, T * 96, "grad_logits"},
+                     {a->workspace, (size_t)need, "workspace"}};
+    s = check_buffers(b, sizeof(b) / sizeof(b[0]));
+    if (s != MHC_OK) return s;
+    const mhc::LayerPtrs p{a->x,         a->W,      a->f,      nullptr,       nullptr,
+                           a->rms,       a->logits, a->H_pre,  a->H_post,     a->H_res,
+                           a->grad_x_out, a->grad_u, a->grad_x, a->grad_f,    a->grad_W,
+                           a->grad_logits, a->workspace};
+    return launched(mhc::launch_layer_bwd(p, a->T, a->C, (hipStream_t)stream), "layer_bwd launch");
+}
+
 const char* mhc_status_string(mhc_status s)
 {
     switch (s) {

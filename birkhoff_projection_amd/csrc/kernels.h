@@ -19,4 +19,40 @@ hipError_t launch_stream_mix_fwd(const void* x, const float* Hl, float* H_out, v
 hipError_t launch_stream_mix_bwd(const void* x, const float* H, const void* gout, void* gx,
                                  float* gH, int64_t T, int64_t C, hipStream_t stream);
 
+// Device pointers of one layer step (see mhc_layer_args in include/mhc.h).
+struct LayerPtrs {
+    const void* x;
+    const void* W;
+    const void* f;
+    void* u;
+    void* x_out;
+    float* rms;
+    float* logits;
+    float* H_pre;
+    float* H_post;
+    float* H_res;
+    const void* grad_x_out;
+    const void* grad_u;
+    void* grad_x;
+    void* grad_f;
+    float* grad_W;
+    float* grad_logits;
+    void* workspace;
+};
+
+// Backward workspace layout: s[Tp] fp32 | dl^T hi [24][Tp] bf16 | dl^T lo
+// [24][Tp] bf16 | grad_W partials [groups][24][4C] fp32 (each 256-byte aligned).
+struct LayerPlan {
+    int64_t Tp;            // T rounded up to 64
+    int64_t group_tokens;  // tokens per grad_W partial
+    int64_t groups;
+    int64_t off_s, off_hi, off_lo, off_partial;
+    int64_t bytes;
+};
+
+LayerPlan layer_plan(int64_t T, int64_t C);
+hipError_t launch_layer_fwd(const LayerPtrs& a, int64_t T, int64_t C, float eps,
+                            const SolverOpts& o, hipStream_t stream);
+hipError_t launch_layer_bwd(const LayerPtrs& a, int64_t T, int64_t C, hipStream_t stream);
+
 }  // namespace mhc

@@ -1,0 +1,684 @@
+// One mHC residual-layer step for n = 4 streams on gfx950 (forward and
+// backward), per token t:
+//
+//   r      = sqrt(mean(x_t^2) + eps) over the flattened 4C stream values
+//   l      = (x_t W^T) / r                     W [24, 4C], rows pre|post|res
+//   H_pre  = sigmoid(l[0:4]),  H_post = sigmoid(l[4:8]),  H_res = P(l[8:24])
+//   u      = sum_j H_pre[j] x_j                (read-mix, the layer input)
+//   x_out_i = H_post[i] f + sum_j H_res[i,j] x_j   (write-back)
+//
+// (forpes.ru mHC explainer, "Hyper-Connections" and "mHC" sections: n
+// parallel streams, projection to the model width before the layer function
+// and expansion after, sigmoid on the pre/post maps; kimiseek V4-Flash
+// article: the maps are generated from the input; neo-ai mHC summary: fused
+// RMSNorm + matmul + activation kernels, mixed precision.)
+//
+// Kernels (all HBM-streaming except the small solves):
+//   maps   x W^T on bf16 MFMA with the per-token sum of squares in the same
+//          pass; epilogue: 1/r scaling, sigmoids, Birkhoff projection
+//   mix    read-mix and write-back
+//   dots   per-token reductions dH_pre, dH_post, dH_res and grad_f; epilogue:
+//          sigmoid derivative and projection backward -> grad_logits
+//   dx     grad_x = H_res^T grad_x_out + H_pre grad_u + RMSNorm backward of
+//          grad_logits W, the latter on MFMA
+//   dw     grad_W partials = (grad_logits / r)^T x on MFMA, x transposed
+//          through LDS; then a fixed-order reduction over token groups
+//
+// Mixed precision: MFMA operands are bf16.  x and W are bf16 already (exact);
+// grad_logits is fp32 and enters MFMA as the sum of two bf16 halves (hi +
+// lo, about 16 significant bits), so its products keep fp32-level accuracy.
+// Accumulation is fp32 throughout.
+#include "kernels.h"
+#include "proj4.h"
+
+namespace mhc {
+
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kMaps = 24;            // n*n + 2n for n = 4
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+MHC_DEV uint32_t pack_bf16x2(float lo, float hi)
+{
+    bf16x2_t r;
+    r.x = (__bf16)lo;
+    r.y = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+MHC_DEV void unpack8(const uint4& q, float* f)
+{
+    f[0] = mhc_bf16_lo(q.x);
+    f[1] = mhc_bf16_hi(q.x);
+    f[2] = mhc_bf16_lo(q.y);
+    f[3] = mhc_bf16_hi(q.y);
+    f[4] = mhc_bf16_lo(q.z);
+    f[5] = mhc_bf16_hi(q.z);
+    f[6] = mhc_bf16_lo(q.w);
+    f[7] = mhc_bf16_hi(q.w);
+}
+
+MHC_DEV uint4 pack8(const float* f)
+{
+    return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                      pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+}
+
+MHC_DEV float sigmoid(float z) { return 1.f / (1.f + expf(-z)); }
+
+MHC_DEV bf16x8 as_bf16x8(const uint4& q) { return __builtin_bit_cast(bf16x8, q); }
+
+// Split 8 fp32 values into bf16 hi and lo parts with v ~= hi + lo.
+MHC_DEV void split8(const float* v, bf16x8& hi, bf16x8& lo)
+{
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const __bf16 h = (__bf16)v[e];
+        hi[e] = h;
+        lo[e] = (__bf16)(v[e] - (float)h);
+    }
+}
+
+// Sum 32 per-lane partials over a wave64 by butterfly halving; afterwards
+// lane l holds the total of value ((l >> 1) & 31).
+MHC_DEV float wave_sum32(float* v)
+{
+#pragma unroll
+    for (int m = 32, n = 32; m >= 2; m >>= 1, n >>= 1) {
+        const bool up = (threadIdx.x & m) != 0;
+        const int h = n / 2;
+#pragma unroll
+        for (int k = 0; k < h; ++k) {
+            const float keep = up ? v[k + h] : v[k];
+            const float send = up ? v[k] : v[k + h];
+            v[k] = keep + __shfl_xor(send, m);
+        }
+    }
+    return v[0] + __shfl_xor(v[0], 1);
+}
+
+// ---------------------------------------------------------------------------
+// maps: 64 tokens per workgroup; wave w handles stream w, i.e. the K range
+// [w C, (w+1) C) of the flattened token vector.  MFMA 16x16x32 bf16:
+//   A (16 tokens x 32 k): lane l holds x[token 16*tile + l%16][k0 + 8*(l/16) ..+7]
+//   B (32 k x 16 maps):   lane l holds W[map 16*ot + l%16][k0 + 8*(l/16) ..+7]
+//   D (16 x 16):          lane l, v -> token 4*(l/16)+v, map l%16
+// ---------------------------------------------------------------------------
+template <int SOLVER>
+__global__ __launch_bounds__(kBlock) void layer_maps_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, float* __restrict__ logits,
+    float* __restrict__ rms, float* __restrict__ Hpre, float* __restrict__ Hpost,
+    float* __restrict__ Hres, int64_t T, int64_t C, float eps, SolverOpts o)
+{
+    __shared__ float sRed[4][64][kMaps + 1];
+    __shared__ float sSsq[4][64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int row = lane & 15, kq = lane >> 4;
+    const int64_t t0 = (int64_t)blockIdx.x * 64;
+    const int64_t D = 4 * C;
+
+    const uint16_t* xa[4];
+    bool tok_ok[4];
+#pragma unroll
+    for (int tile = 0; tile < 4; ++tile) {
+        const int64_t t = t0 + 16 * tile + row;
+        tok_ok[tile] = t < T;
+        xa[tile] = x + ((tok_ok[tile] ? t : 0) * 4 + w) * C + 8 * kq;
+    }
+    const uint16_t* wb[2];
+    bool map_ok[2];
+#pragma unroll
+    for (int ot = 0; ot < 2; ++ot) {
+        const int m = 16 * ot + row;
+        map_ok[ot] = m < kMaps;
+        wb[ot] = W + (int64_t)(map_ok[ot] ? m : 0) * D + (int64_t)w * C + 8 * kq;
+    }
+    floatx4 acc[4][2];
+    float ssq[4];
+#pragma unroll
+    for (int tile = 0; tile < 4; ++tile) {
+        ssq[tile] = 0.f;
+#pragma unroll
+        for (int ot = 0; ot < 2; ++ot) acc[tile][ot] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+    const uint4 zero4 = make_uint4(0, 0, 0, 0);
+#pragma unroll 2
+    for (int64_t k = 0; k < C; k += 32) {
+        uint4 a[4], b[2];
+#pragma unroll
+        for (int tile = 0; tile < 4; ++tile) {
+            const uint4 q = *reinterpret_cast<const uint4*>(xa[tile] + k);
+            a[tile] = tok_ok[tile] ? q : zero4;
+        }
+#pragma unroll
+        for (int ot = 0; ot < 2; ++ot) {
+            const uint4 q = *reinterpret_cast<const uint4*>(wb[ot] + k);
+            b[ot] = map_ok[ot] ? q : zero4;
+        }
+#pragma unroll
+        for (int tile = 0; tile < 4; ++tile)
+#pragma unroll
+            for (int ot = 0; ot < 2; ++ot)
+                acc[tile][ot] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    as_bf16x8(a[tile]), as_bf16x8(b[ot]), acc[tile][ot], 0, 0, 0);
+#pragma unroll
+        for (int tile = 0; tile < 4; ++tile) {
+            float f[8];
+            unpack8(a[tile], f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ssq[tile] = __builtin_fmaf(f[e], f[e], ssq[tile]);
+        }
+    }
+#pragma unroll
+    for (int tile = 0; tile < 4; ++tile) {
+#pragma unroll
+        for (int ot = 0; ot < 2; ++ot) {
+            const int m = 16 * ot + row;
+            if (m < kMaps) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) sRed[w][16 * tile + 4 * kq + v][m] = acc[tile][ot][v];
+            }
+        }
+        float s = ssq[tile];
+        s += __shfl_xor(s, 16);
+        s += __shfl_xor(s, 32);
+        if (kq == 0) sSsq[w][16 * tile + row] = s;
+    }
+    __syncthreads();
+    if (w != 0) return;
+    const int64_t t = t0 + lane;
+    if (t >= T) return;
+    float l[kMaps];
+#pragma unroll
+    for (int m = 0; m < kMaps; ++m)
+        l[m] = (sRed[0][lane][m] + sRed[1][lane][m]) + (sRed[2][lane][m] + sRed[3][lane][m]);
+    const float ss = (sSsq[0][lane] + sSsq[1][lane]) + (sSsq[2][lane] + sSsq[3][lane]);
+    const float r = sqrtf(ss / (float)D + eps);
+    const float inv = 1.f / r;
+#pragma unroll
+    for (int m = 0; m < kMaps; ++m) l[m] *= inv;
+    rms[t] = r;
+    float4* lo = reinterpret_cast<float4*>(logits + kMaps * t);
+#pragma unroll
+    for (int q = 0; q < kMaps / 4; ++q) lo[q] = make_float4(l[4 * q], l[4 * q + 1], l[4 * q + 2], l[4 * q + 3]);
+    reinterpret_cast<float4*>(Hpre)[t] = make_float4(sigmoid(l[0]), sigmoid(l[1]), sigmoid(l[2]), sigmoid(l[3]));
+    reinterpret_cast<float4*>(Hpost)[t] = make_float4(sigmoid(l[4]), sigmoid(l[5]), sigmoid(l[6]), sigmoid(l[7]));
+    float h[16];
+    if (SOLVER == 0)
+        project_newton(l + 8, h, o);
+    else
+        project_sinkhorn(l + 8, h, o);
+    float4* ho = reinterpret_cast<float4*>(Hres + 16 * t);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ho[q] = make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
+}
+
+// ---------------------------------------------------------------------------
+// mix: read-mix u and write-back x_out, 16 tokens per workgroup.
+// ---------------------------------------------------------------------------
+constexpr int kMixTokens = 16;
+
+__global__ __launch_bounds__(kBlock) void layer_mix_kernel(
+    const uint4* __restrict__ x, const uint4* __restrict__ f, const float* __restrict__ Hpre,
+    const float* __restrict__ Hpost, const float* __restrict__ Hres, uint4* __restrict__ u,
+    uint4* __restrict__ xo, int64_t T, int64_t C8)
+{
+    __shared__ float sM[kMixTokens][kMaps];
+    const int64_t t0 = (int64_t)blockIdx.x * kMixTokens;
+    const int tid = threadIdx.x;
+    const int nt = (int)((T - t0) < kMixTokens ? (T - t0) : kMixTokens);
+    for (int p = tid; p < nt * kMaps; p += kBlock) {
+        const int tl = p / kMaps, m = p % kMaps;
+        const int64_t t = t0 + tl;
+        sM[tl][m] = m < 4 ? Hpre[4 * t + m] : (m < 8 ? Hpost[4 * t + m - 4] : Hres[16 * t + m - 8]);
+    }
+    __syncthreads();
+    for (int tl = 0; tl < nt; ++tl) {
+        float M[kMaps];
+#pragma unroll
+        for (int m = 0; m < kMaps; ++m) M[m] = sM[tl][m];
+        const int64_t t = t0 + tl;
+        for (int64_t c = tid; c < C8; c += kBlock) {
+            float xs[4][8], ff[8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) unpack8(x[(t * 4 + j) * C8 + c], xs[j]);
+            unpack8(f[t * C8 + c], ff);
+            float uu[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float s = M[0] * xs[0][e];
+                s = __builtin_fmaf(M[1], xs[1][e], s);
+                s = __builtin_fmaf(M[2], xs[2][e], s);
+                uu[e] = __builtin_fmaf(M[3], xs[3][e], s);
+            }
+            u[t * C8 + c] = pack8(uu);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float o8[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float s = M[4 + i] * ff[e];
+                    s = __builtin_fmaf(M[8 + 4 * i + 0], xs[0][e], s);
+                    s = __builtin_fmaf(M[8 + 4 * i + 1], xs[1][e], s);
+                    s = __builtin_fmaf(M[8 + 4 * i + 2], xs[2][e], s);
+                    o8[e] = __builtin_fmaf(M[8 + 4 * i + 3], xs[3][e], s);
+                }
+                xo[(t * 4 + i) * C8 + c] = pack8(o8);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dots: wave w of workgroup b handles tokens 64 b + 16 w + [0, 16), one token
+// at a time across the wave; lanes stride over the 8-column chunks.
+// Per token the 24 partial dots are wave-reduced into LDS; then lanes 0..15
+// each finish one token: sigmoid derivative, projection backward, the RMSNorm
+// coefficient s = <dl, l> / (4C), and the transposed, r-scaled bf16 hi/lo
+// copy of dl that the dW pass uses as an MFMA operand.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBlock) void layer_dots_kernel(
+    const uint4* __restrict__ x, const uint4* __restrict__ f, const uint4* __restrict__ gxo,
+    const uint4* __restrict__ gu, const float* __restrict__ Hpre, const float* __restrict__ Hpost,
+    const float* __restrict__ Hres, const float* __restrict__ logits, const float* __restrict__ rms,
+    uint4* __restrict__ gf, float* __restrict__ glogits, float* __restrict__ svec,
+    __bf16* __restrict__ dlT_hi, __bf16* __restrict__ dlT_lo, int64_t T, int64_t Tp, int64_t C8)
+{
+    __shared__ float sDots[4][16][kMaps];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t tb = (int64_t)blockIdx.x * 64 + 16 * w;
+    for (int tl = 0; tl < 16; ++tl) {
+        const int64_t t = tb + tl;
+        if (t < T) {
+            const float4 hq = reinterpret_cast<const float4*>(Hpost)[t];
+            const float ho[4] = {hq.x, hq.y, hq.z, hq.w};
+            float acc[32];
+#pragma unroll
+            for (int k = 0; k < 32; ++k) acc[k] = 0.f;
+            for (int64_t c = lane; c < C8; c += 64) {
+                float xs[4][8], gs[4][8], ff[8], uu[8];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    unpack8(x[(t * 4 + j) * C8 + c], xs[j]);
+                    unpack8(gxo[(t * 4 + j) * C8 + c], gs[j]);
+                }
+                unpack8(f[t * C8 + c], ff);
+                unpack8(gu[t * C8 + c], uu);
+                float df[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float s = ho[0] * gs[0][e];
+                    s = __builtin_fmaf(ho[1], gs[1][e], s);
+                    s = __builtin_fmaf(ho[2], gs[2][e], s);
+                    df[e] = __builtin_fmaf(ho[3], gs[3][e], s);
+                }
+                gf[t * C8 + c] = pack8(df);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[j] = __builtin_fmaf(uu[e], xs[j][e], acc[j]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[4 + i] = __builtin_fmaf(gs[i][e], ff[e], acc[4 + i]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            acc[8 + 4 * i + j] = __builtin_fmaf(gs[i][e], xs[j][e], acc[8 + 4 * i + j]);
+                }
+            }
+            const float s = wave_sum32(acc);
+            const int idx = (lane >> 1) & 31;
+            if ((lane & 1) == 0 && idx < kMaps) sDots[w][tl][idx] = s;
+        }
+    }
+    __syncthreads();
+    if (lane >= 16) return;
+    const int64_t t = tb + lane;
+    if (t >= Tp) return;
+    float dl[kMaps];
+    if (t < T) {
+        float d[kMaps];
+#pragma unroll
+        for (int m = 0; m < kMaps; ++m) d[m] = sDots[w][lane][m];
+        const float4 pq = reinterpret_cast<const float4*>(Hpre)[t];
+        const float4 oq = reinterpret_cast<const float4*>(Hpost)[t];
+        const float hp[4] = {pq.x, pq.y, pq.z, pq.w};
+        const float ho[4] = {oq.x, oq.y, oq.z, oq.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            dl[j] = d[j] * hp[j] * (1.f - hp[j]);
+            dl[4 + j] = d[4 + j] * ho[j] * (1.f - ho[j]);
+        }
+        float H[16];
+        const float4* hr = reinterpret_cast<const float4*>(Hres + 16 * t);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 v = hr[q];
+            H[4 * q] = v.x;
+            H[4 * q + 1] = v.y;
+            H[4 * q + 2] = v.z;
+            H[4 * q + 3] = v.w;
+        }
+        project_bwd(H, d + 8, dl + 8);
+        float s = 0.f;
+#pragma unroll
+        for (int m = 0; m < kMaps; ++m) s = __builtin_fmaf(dl[m], logits[kMaps * t + m], s);
+        svec[t] = s / (float)(32 * C8);
+        float4* go = reinterpret_cast<float4*>(glogits + kMaps * t);
+#pragma unroll
+        for (int q = 0; q < kMaps / 4; ++q) go[q] = make_float4(dl[4 * q], dl[4 * q + 1], dl[4 * q + 2], dl[4 * q + 3]);
+        const float inv = 1.f / rms[t];
+#pragma unroll
+        for (int m = 0; m < kMaps; ++m) dl[m] *= inv;
+    } else {
+#pragma unroll
+        for (int m = 0; m < kMaps; ++m) dl[m] = 0.f;
+    }
+#pragma unroll
+    for (int m = 0; m < kMaps; ++m) {
+        const __bf16 h = (__bf16)dl[m];
+        dlT_hi[m * Tp + t] = h;
+        dlT_lo[m * Tp + t] = (__bf16)(dl[m] - (float)h);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dx: workgroup = a slab of 32 columns (all 4 streams: 128 flattened k) and a
+// range of 256 tokens (each wave 4 tiles of 16).  The slab of W sits in LDS
+// as [k][map] so that MFMA B operands are 16-byte LDS reads:
+//   dxn (16 tokens x 16 k) = dl (16 x 32 maps, hi + lo) * W^T (32 maps x 16 k)
+// dxn goes through LDS to the element-wise layout: lane = (token, 8 columns).
+// ---------------------------------------------------------------------------
+constexpr int kDxCols = 32;              // columns per stream in a slab
+constexpr int kDxK = 4 * kDxCols;        // flattened k per slab
+constexpr int kDxTiles = 4;              // 16-token tiles per wave
+constexpr int kWPitch = 40;              // bf16 per LDS row of W (32 maps + pad)
+
+__global__ __launch_bounds__(kBlock) void layer_dx_kernel(
+    const uint4* __restrict__ x, const uint4* __restrict__ gxo, const uint4* __restrict__ gu,
+    const uint16_t* __restrict__ W, const float* __restrict__ Hpre, const float* __restrict__ Hres,
+    const float* __restrict__ rms, const float* __restrict__ glogits, const float* __restrict__ svec,
+    uint4* __restrict__ gx, int64_t T, int64_t C)
+{
+    __shared__ __attribute__((aligned(16))) __bf16 sW[kDxK][kWPitch];
+    __shared__ float sD[4][16][kDxK + 4];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t c0 = (int64_t)blockIdx.x * kDxCols;
+    const int64_t D = 4 * C;
+    const int64_t C8 = C / 8;
+    // W slab -> LDS, transposed: sW[j*32 + cc][m] = W[m][j*C + c0 + cc]
+    for (int p = threadIdx.x; p < 32 * 4 * (kDxCols / 8); p += kBlock) {
+        const int m = p / (4 * (kDxCols / 8));
+        const int rem = p % (4 * (kDxCols / 8));
+        const int j = rem / (kDxCols / 8), q = rem % (kDxCols / 8);
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (m < kMaps) v = *reinterpret_cast<const uint4*>(W + m * D + j * C + c0 + 8 * q);
+        const bf16x8 b = as_bf16x8(v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sW[j * kDxCols + 8 * q + e][m] = b[e];
+    }
+    __syncthreads();
+    const int row = lane & 15, kq = lane >> 4;
+    for (int tile = 0; tile < kDxTiles; ++tile) {
+        const int64_t tt0 = (int64_t)blockIdx.y * (4 * kDxTiles * 16) + (int64_t)(w * kDxTiles + tile) * 16;
+        // A operand: dl[token tt0 + row][maps 8 kq ..+7], split hi / lo
+        float a8[8];
+        const int64_t ta = tt0 + row;
+        const int m0 = 8 * kq;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a8[e] = 0.f;
+        if (ta < T && m0 < kMaps) {
+            const float4* src = reinterpret_cast<const float4*>(glogits + kMaps * ta + m0);
+            const float4 v0 = src[0], v1 = src[1];
+            a8[0] = v0.x; a8[1] = v0.y; a8[2] = v0.z; a8[3] = v0.w;
+            a8[4] = v1.x; a8[5] = v1.y; a8[6] = v1.z; a8[7] = v1.w;
+        }
+        bf16x8 ahi, alo;
+        split8(a8, ahi, alo);
+#pragma unroll
+        for (int nt = 0; nt < kDxK / 16; ++nt) {
+            const bf16x8 b = *reinterpret_cast<const bf16x8*>(&sW[nt * 16 + row][8 * kq]);
+            floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, b, acc, 0, 0, 0);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) sD[w][4 * kq + v][nt * 16 + row] = acc[v];
+        }
+        __syncthreads();
+        // element-wise: lane = (token tt0 + lane/4, columns c0 + 8 (lane%4) ..+7)
+        const int tl = lane >> 2, q = lane & 3;
+        const int64_t t = tt0 + tl;
+        if (t < T) {
+            const int64_t c8 = c0 / 8 + q;
+            float gs[4][8], xs[4][8], uu[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                unpack8(gxo[(t * 4 + i) * C8 + c8], gs[i]);
+                unpack8(x[(t * 4 + i) * C8 + c8], xs[i]);
+            }
+            unpack8(gu[t * C8 + c8], uu);
+            float H[16];
+            const float4* hr = reinterpret_cast<const float4*>(Hres + 16 * t);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float4 v = hr[k];
+                H[4 * k] = v.x;
+                H[4 * k + 1] = v.y;
+                H[4 * k + 2] = v.z;
+                H[4 * k + 3] = v.w;
+            }
+            const float4 pq = reinterpret_cast<const float4*>(Hpre)[t];
+            const float hp[4] = {pq.x, pq.y, pq.z, pq.w};
+            const float inv = 1.f / rms[t];
+            const float sr = svec[t] * inv;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float o8[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float s = H[j] * gs[0][e];
+                    s = __builtin_fmaf(H[4 + j], gs[1][e], s);
+                    s = __builtin_fmaf(H[8 + j], gs[2][e], s);
+                    s = __builtin_fmaf(H[12 + j], gs[3][e], s);
+                    s = __builtin_fmaf(hp[j], uu[e], s);
+                    const float dxn = sD[w][tl][j * kDxCols + 8 * q + e];
+                    o8[e] = __builtin_fmaf(__builtin_fmaf(-xs[j][e], sr, dxn), inv, s);
+                }
+                gx[(t * 4 + j) * C8 + c8] = pack8(o8);
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dw: workgroup = 64 flattened k (inside one stream) x one token group; wave w
+// takes every 4th 32-token chunk of the group.  Per chunk the x tile is
+// staged in LDS ([token][k]) and read back transposed for the MFMA B operand:
+//   dW^T tile (32 maps x 16 k) += dlT (32 maps x 32 tokens) * x (32 tokens x 16 k)
+// The four waves' partials are summed in LDS and one partial per token group
+// is written; layer_dw_reduce adds the groups in a fixed order.
+// ---------------------------------------------------------------------------
+constexpr int kDwK = 64;
+constexpr int kXPitch = kDwK + 8;
+
+__global__ __launch_bounds__(kBlock) void layer_dw_kernel(
+    const uint16_t* __restrict__ x, const __bf16* __restrict__ dlT_hi,
+    const __bf16* __restrict__ dlT_lo, float* __restrict__ partial, int64_t T, int64_t Tp,
+    int64_t C, int64_t group_tokens)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t sX[4][32][kXPitch];
+    __shared__ float sR[32][kDwK + 1];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int row = lane & 15, kq = lane >> 4;
+    const int64_t D = 4 * C;
+    const int64_t k0 = (int64_t)blockIdx.x * kDwK;
+    const int64_t g = blockIdx.y;
+    const int64_t tg0 = g * group_tokens;
+    int64_t tg1 = tg0 + group_tokens;
+    if (tg1 > Tp) tg1 = Tp;
+    floatx4 acc[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const uint4 zero4 = make_uint4(0, 0, 0, 0);
+    for (int64_t tc = tg0 + 32 * w; tc < tg1; tc += 128) {
+        // stage x[tc .. tc+31][k0 .. k0+63]: 256 16-byte pieces, 4 per lane
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int p = lane + 64 * i;
+            const int tok = p >> 3, q = p & 7;
+            const int64_t t = tc + tok;
+            uint4 v = zero4;
+            if (t < T) v = *reinterpret_cast<const uint4*>(x + t * D + k0 + 8 * q);
+            *reinterpret_cast<uint4*>(&sX[w][tok][8 * q]) = v;
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): LDS stores done
+        __builtin_amdgcn_wave_barrier();
+        bf16x8 ahi[2], alo[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            const int m = 16 * mt + row;
+            uint4 vh = zero4, vl = zero4;
+            if (m < kMaps) {
+                vh = *reinterpret_cast<const uint4*>(dlT_hi + m * Tp + tc + 8 * kq);
+                vl = *reinterpret_cast<const uint4*>(dlT_lo + m * Tp + tc + 8 * kq);
+            }
+            ahi[mt] = as_bf16x8(vh);
+            alo[mt] = as_bf16x8(vl);
+        }
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            bf16x8 b;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                b[e] = __builtin_bit_cast(__bf16, sX[w][8 * kq + e][16 * nt + row]);
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[mt], b, acc[mt][nt], 0, 0, 0);
+                acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[mt], b, acc[mt][nt], 0, 0, 0);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+    }
+    // sum the four waves' partials: wave 0 writes, the others add in turn
+    for (int ww = 0; ww < 4; ++ww) {
+        if (w == ww) {
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        float& dst = sR[16 * mt + 4 * kq + v][16 * nt + row];
+                        dst = (ww == 0 ? 0.f : dst) + acc[mt][nt][v];
+                    }
+        }
+        __syncthreads();
+    }
+    float* out = partial + g * (int64_t)kMaps * D;
+    for (int p = threadIdx.x; p < kMaps * kDwK; p += kBlock) {
+        const int m = p / kDwK, kk = p % kDwK;
+        out[m * D + k0 + kk] = sR[m][kk];
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void layer_dw_reduce_kernel(const float4* __restrict__ partial,
+                                                                 float4* __restrict__ gW,
+                                                                 int64_t n4, int64_t groups)
+{
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n4; i += (int64_t)gridDim.x * kBlock) {
+        float4 s = partial[i];
+        for (int64_t g = 1; g < groups; ++g) {
+            const float4 v = partial[g * n4 + i];
+            s.x += v.x;
+            s.y += v.y;
+            s.z += v.z;
+            s.w += v.w;
+        }
+        gW[i] = s;
+    }
+}
+
+}  // namespace
+
+LayerPlan layer_plan(int64_t T, int64_t C)
+{
+    LayerPlan p;
+    p.Tp = (T + 63) / 64 * 64;
+    const int64_t want_groups = 8;
+    int64_t gt = (p.Tp + want_groups - 1) / want_groups;
+    gt = (gt + 127) / 128 * 128;  // whole 4-wave x 32-token rounds
+    if (gt < 128) gt = 128;
+    p.group_tokens = gt;
+    p.groups = (p.Tp + gt - 1) / gt;
+    const int64_t D = 4 * C;
+    p.off_s = 0;
+    p.off_hi = (p.Tp * 4 + 255) / 256 * 256;
+    p.off_lo = p.off_hi + (p.Tp * kMaps * 2 + 255) / 256 * 256;
+    p.off_partial = p.off_lo + (p.Tp * kMaps * 2 + 255) / 256 * 256;
+    p.bytes = p.off_partial + p.groups * kMaps * D * 4;
+    return p;
+}
+
+hipError_t launch_layer_fwd(const LayerPtrs& a, int64_t T, int64_t C, float eps,
+                            const SolverOpts& o, hipStream_t stream)
+{
+    const dim3 g1((unsigned)((T + 63) / 64));
+    if (o.solver == 0)
+        hipLaunchKernelGGL(layer_maps_kernel<0>, g1, dim3(kBlock), 0, stream,
+                           (const uint16_t*)a.x, (const uint16_t*)a.W, a.logits, a.rms, a.H_pre,
+                           a.H_post, a.H_res, T, C, eps, o);
+    else
+        hipLaunchKernelGGL(layer_maps_kernel<1>, g1, dim3(kBlock), 0, stream,
+                           (const uint16_t*)a.x, (const uint16_t*)a.W, a.logits, a.rms, a.H_pre,
+                           a.H_post, a.H_res, T, C, eps, o);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 g2((unsigned)((T + kMixTokens - 1) / kMixTokens));
+    hipLaunchKernelGGL(layer_mix_kernel, g2, dim3(kBlock), 0, stream, (const uint4*)a.x,
+                       (const uint4*)a.f, a.H_pre, a.H_post, a.H_res, (uint4*)a.u,
+                       (uint4*)a.x_out, T, C / 8);
+    return hipGetLastError();
+}
+
+hipError_t launch_layer_bwd(const LayerPtrs& a, int64_t T, int64_t C, hipStream_t stream)
+{
+    const LayerPlan p = layer_plan(T, C);
+    char* ws = static_cast<char*>(a.workspace);
+    float* svec = reinterpret_cast<float*>(ws + p.off_s);
+    __bf16* dhi = reinterpret_cast<__bf16*>(ws + p.off_hi);
+    __bf16* dlo = reinterpret_cast<__bf16*>(ws + p.off_lo);
+    float* partial = reinterpret_cast<float*>(ws + p.off_partial);
+    const int64_t C8 = C / 8;
+    hipLaunchKernelGGL(layer_dots_kernel, dim3((unsigned)(p.Tp / 64)), dim3(kBlock), 0, stream,
+                       (const uint4*)a.x, (const uint4*)a.f, (const uint4*)a.grad_x_out,
+                       (const uint4*)a.grad_u, a.H_pre, a.H_post, a.H_res, a.logits, a.rms,
+                       (uint4*)a.grad_f, a.grad_logits, svec, dhi, dlo, T, p.Tp, C8);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 gdx((unsigned)(C / kDxCols), (unsigned)((T + 4 * kDxTiles * 16 - 1) / (4 * kDxTiles * 16)));
+    hipLaunchKernelGGL(layer_dx_kernel, gdx, dim3(kBlock), 0, stream, (const uint4*)a.x,
+                       (const uint4*)a.grad_x_out, (const uint4*)a.grad_u, (const uint16_t*)a.W,
+                       a.H_pre, a.H_res, a.rms, a.grad_logits, svec, (uint4*)a.grad_x, T, C);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 gdw((unsigned)(4 * C / kDwK), (unsigned)p.groups);
+    hipLaunchKernelGGL(layer_dw_kernel, gdw, dim3(kBlock), 0, stream, (const uint16_t*)a.x, dhi,
+                       dlo, partial, T, p.Tp, C, p.group_tokens);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t n4 = (int64_t)kMaps * 4 * C / 4;
+    hipLaunchKernelGGL(layer_dw_reduce_kernel, dim3((unsigned)((n4 + kBlock - 1) / kBlock)),
+                       dim3(kBlock), 0, stream, (const float4*)partial, (float4*)a.grad_W, n4,
+                       p.groups);
+    return hipGetLastError();
+}
+
+}  // namespace mhc

@@ -10,7 +10,7 @@ import ctypes
 
 import torch
 
-from ._lib import ProjOpts, check, lib
+from ._lib import LayerArgs, ProjOpts, check, lib
 
 SOLVERS = {"newton": 0, "sinkhorn": 1}
 
@@ -149,3 +149,76 @@ def stream_mix_bwd(x: torch.Tensor, H: torch.Tensor, grad_out: torch.Tensor):
         check(lib().mhc_stream_mix_bwd(_ptr(x), _ptr(H), _ptr(grad_out), _ptr(gx), _ptr(gH), T,
                                        n, C, _stream(x.device)))
     return gx, gH
+
+
+N_MAPS = 24  # n*n + 2n for n = 4
+
+
+def _layer_args(x, W, f, eps, opts):
+    _need(x, "x", torch.bfloat16)
+    if x.dim() != 3:
+        raise ValueError("x must be [T, n, C]")
+    T, n, C = x.shape
+    _need(W, "W", torch.bfloat16)
+    _need(f, "f", torch.bfloat16)
+    if tuple(W.shape) != (n * n + 2 * n, n * C) or tuple(f.shape) != (T, C):
+        raise ValueError("W must be [n*n+2n, n*C] and f [T, C]")
+    a = LayerArgs()
+    a.T, a.n, a.C, a.eps = T, n, C, float(eps)
+    a.proj = ctypes.pointer(opts) if opts is not None else None
+    a.x, a.W, a.f = x.data_ptr(), W.data_ptr(), f.data_ptr()
+    return a
+
+
+def layer_fwd(x, W, f, *, eps=1e-6, solver="newton", max_iters=None, tol=None,
+              warm_sweeps=None):
+    """Forward of one mHC layer step.  x [T,4,C], W [24,4C], f [T,C] bf16.
+    Returns dict(u, x_out, rms, logits, H_pre, H_post, H_res)."""
+    o = make_opts(solver, max_iters, tol, warm_sweeps)
+    a = _layer_args(x, W, f, eps, o)
+    T, n, C = x.shape
+    dev = x.device
+    out = dict(u=torch.empty((T, C), dtype=torch.bfloat16, device=dev),
+               x_out=torch.empty_like(x),
+               rms=torch.empty(T, dtype=torch.float32, device=dev),
+               logits=torch.empty((T, N_MAPS), dtype=torch.float32, device=dev),
+               H_pre=torch.empty((T, n), dtype=torch.float32, device=dev),
+               H_post=torch.empty((T, n), dtype=torch.float32, device=dev),
+               H_res=torch.empty((T, n, n), dtype=torch.float32, device=dev))
+    for k in ("u", "x_out", "rms", "logits", "H_pre", "H_post", "H_res"):
+        setattr(a, k, out[k].data_ptr())
+    with torch.cuda.device(dev):
+        check(lib().mhc_layer_fwd(ctypes.byref(a), _stream(dev)))
+    return out
+
+
+def layer_workspace(T, C, device, n=4):
+    nbytes = lib().mhc_layer_workspace_bytes(T, n, C)
+    if nbytes < 0:
+        raise ValueError("invalid layer shape")
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def layer_bwd(x, W, f, fwd, grad_x_out, grad_u, *, workspace=None, out=None):
+    """Backward of one mHC layer step given the forward's outputs ``fwd``.
+    Returns dict(grad_x, grad_f, grad_W, grad_logits)."""
+    a = _layer_args(x, W, f, 1e-6, None)
+    T, n, C = x.shape
+    dev = x.device
+    _need(grad_x_out, "grad_x_out", torch.bfloat16)
+    _need(grad_u, "grad_u", torch.bfloat16)
+    for k in ("rms", "logits", "H_pre", "H_post", "H_res"):
+        _need(fwd[k], k, torch.float32)
+        setattr(a, k, fwd[k].data_ptr())
+    a.grad_x_out, a.grad_u = grad_x_out.data_ptr(), grad_u.data_ptr()
+    if out is None:
+        out = dict(grad_x=torch.empty_like(x), grad_f=torch.empty_like(f),
+                   grad_W=torch.empty(W.shape, dtype=torch.float32, device=dev),
+                   grad_logits=torch.empty((T, N_MAPS), dtype=torch.float32, device=dev))
+    for k in ("grad_x", "grad_f", "grad_W", "grad_logits"):
+        setattr(a, k, out[k].data_ptr())
+    ws = layer_workspace(T, C, dev, n) if workspace is None else workspace
+    a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+    with torch.cuda.device(dev):
+        check(lib().mhc_layer_bwd(ctypes.byref(a), _stream(dev)))
+    return out

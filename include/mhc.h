@@ -164,6 +164,67 @@ mhc_status mhc_stream_mix_bwd(const void* x, const float* H, const void* grad_ou
                               void* grad_x, float* grad_H, int64_t T, int32_t n, int64_t C,
                               void* stream);
 
+/* One mHC residual-layer step for n = 4 streams of width C, per token t:
+ *   r = sqrt(mean over the 4C values of x_t^2 + eps)          (RMSNorm, no gain)
+ *   logits = (x_t W^T) / r                                     [24] per token
+ *   H_pre = sigmoid(logits[0:4]), H_post = sigmoid(logits[4:8])
+ *   H_res = Birkhoff projection of logits[8:24] (row-major 4x4)
+ *   u = sum_j H_pre[j] x_t[j]                                  (read-mix)
+ *   x_out[i] = H_post[i] f_t + sum_j H_res[i][j] x_t[j]        (write-back)
+ * forpes.ru explainer, "Hyper-Connections" (streams projected to the model
+ * width before the layer function F and expanded after) and "mHC" (sigmoid on
+ * the pre/post maps, projected residual map); kimiseek V4-Flash article (the
+ * maps are generated per token from the input); neo-ai summary (fused RMSNorm
+ * + matmul + activation, mixed precision).  Layouts are row-major; bf16 for
+ * the activations and W, fp32 for the small per-token tensors. */
+typedef struct {
+    int64_t T;        /* tokens, >= 0 */
+    int32_t n;        /* streams, must be 4 */
+    int64_t C;        /* stream width, a positive multiple of 64 */
+    float eps;        /* RMSNorm epsilon, > 0 (1e-6 in the reference workload) */
+    const mhc_proj_opts* proj;  /* H_res solver options, NULL = defaults */
+    /* inputs (device, bf16) */
+    const void* x;    /* [T, 4, C] */
+    const void* W;    /* [24, 4C]: rows pre 0:4 | post 4:8 | res 8:24 */
+    const void* f;    /* [T, C]   layer-function output (write-back input) */
+    /* forward outputs; rms, logits, H_pre, H_post and H_res are also inputs
+       of the backward (device) */
+    void* u;          /* [T, C] bf16 */
+    void* x_out;      /* [T, 4, C] bf16 */
+    float* rms;       /* [T] */
+    float* logits;    /* [T, 24], already divided by rms */
+    float* H_pre;     /* [T, 4] */
+    float* H_post;    /* [T, 4] */
+    float* H_res;     /* [T, 4, 4] */
+    /* backward inputs (device, bf16) */
+    const void* grad_x_out;  /* [T, 4, C] */
+    const void* grad_u;      /* [T, C] */
+    /* backward outputs (device) */
+    void* grad_x;        /* [T, 4, C] bf16 */
+    void* grad_f;        /* [T, C] bf16 */
+    float* grad_W;       /* [24, 4C] fp32 */
+    float* grad_logits;  /* [T, 24] fp32 */
+    void* workspace;     /* backward scratch, >= mhc_layer_workspace_bytes() bytes,
+                            256-byte aligned; contents need no initialisation */
+    int64_t workspace_bytes;
+} mhc_layer_args;
+
+/* Bytes of device workspace mhc_layer_bwd needs for (T, n, C); -1 if the
+ * shape is invalid. */
+int64_t mhc_layer_workspace_bytes(int64_t T, int32_t n, int64_t C);
+
+/* Forward of the layer step: fills u, x_out, rms, logits, H_pre, H_post,
+ * H_res.  No output may overlap another tensor.  Two kernels on `stream`. */
+mhc_status mhc_layer_fwd(const mhc_layer_args* a, void* stream);
+
+/* Backward of the layer step for upstream grad_x_out and grad_u, using x, W,
+ * f and the forward's rms, logits, H_pre, H_post, H_res: fills grad_x,
+ * grad_f, grad_W (overwritten, not accumulated) and grad_logits.  The
+ * projection's part is the implicit-differentiation backward of
+ * mhc_birkhoff_bwd.  Four kernels on `stream`; the workspace must not be in
+ * use by another call that overlaps on the device. */
+mhc_status mhc_layer_bwd(const mhc_layer_args* a, void* stream);
+
 const char* mhc_status_string(mhc_status s);
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char* mhc_last_error(void);

@@ -115,3 +115,60 @@ def test_python_binding_rejects_cpu_tensors():
         bp.birkhoff_fwd(torch.zeros(3, 4, 4))
     with pytest.raises(TypeError):
         bp.stream_mix(torch.zeros(3, 4, 8, dtype=torch.bfloat16), torch.zeros(3, 4, 4))
+
+
+def test_layer_struct_layout_matches_header(tmp_path):
+    """The ctypes mirror of mhc_layer_args has the C layout (offsets checked
+    with a C program compiled against include/mhc.h)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    fields = [f for f, _ in _lib.LayerArgs._fields_]
+    src = tmp_path / "off.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "mhc.h"\nint main(void){\n'
+                   + "".join(f'printf("%zu\\n", offsetof(mhc_layer_args, {f}));\n' for f in fields)
+                   + 'printf("%zu\\n", sizeof(mhc_layer_args));\nprintf("%zu\\n", sizeof(mhc_proj_opts));\nreturn 0;}\n')
+    exe = tmp_path / "off"
+    subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    want = [getattr(_lib.LayerArgs, f).offset for f in fields] + [ctypes.sizeof(_lib.LayerArgs), ctypes.sizeof(ProjOpts)]
+    assert got == want
+
+
+def test_layer_argument_errors(L):
+    a = _lib.LayerArgs()
+    a.T, a.n, a.C, a.eps = 4, 4, 64, 1e-6
+    names = ["x", "W", "f", "u", "x_out", "rms", "logits", "H_pre", "H_post", "H_res",
+             "grad_x_out", "grad_u", "grad_x", "grad_f", "grad_W", "grad_logits", "workspace"]
+    for i, nm in enumerate(names):
+        setattr(a, nm, FAKE + (i + 1) * (1 << 24))
+    a.workspace_bytes = L.mhc_layer_workspace_bytes(4, 4, 64)
+    assert a.workspace_bytes > 0
+    assert L.mhc_layer_workspace_bytes(4, 3, 64) == -1
+    assert L.mhc_layer_workspace_bytes(4, 4, 96) == -1
+    a.n = 3
+    assert L.mhc_layer_fwd(ctypes.byref(a), None) == UNSUPPORTED
+    a.n = 4
+    a.C = 96
+    assert L.mhc_layer_fwd(ctypes.byref(a), None) == INVALID
+    a.C = 64
+    a.eps = 0.0
+    assert L.mhc_layer_fwd(ctypes.byref(a), None) == INVALID
+    a.eps = 1e-6
+    a.x = None
+    assert L.mhc_layer_fwd(ctypes.byref(a), None) == INVALID
+    assert "x must not be NULL" in _err(L)
+    a.x = FAKE + (1 << 24)
+    a.u = a.x  # output overlapping an input
+    assert L.mhc_layer_fwd(ctypes.byref(a), None) == INVALID
+    assert "overlaps" in _err(L)
+    a.u = FAKE + 4 * (1 << 24)
+    a.workspace_bytes -= 1
+    assert L.mhc_layer_bwd(ctypes.byref(a), None) == INVALID
+    assert "workspace" in _err(L)
+    assert L.mhc_layer_fwd(None, None) == INVALID
+    a.T = 0
+    assert L.mhc_layer_fwd(ctypes.byref(a), None) == 0
+    assert L.mhc_layer_bwd(ctypes.byref(a), None) == 0
