@@ -182,12 +182,84 @@ def bench_projection(args, bp, torch, config):
     return out
 
 
+def _time_loop(torch, body, steps, warmup):
+    stream = torch.cuda.current_stream()
+    for k in range(warmup):
+        body(k)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for k in range(steps):
+        body(k)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def bench_mix(args, bp, torch):
+    """Fused projection + stream mix, T=16384, C=4096 (logits N(0,2^2))."""
+    import workloads as W
+    T, C = W.CONFIG4_SHAPE["T"], W.CONFIG4_SHAPE["C"]
+    x, logits = W.mix_inputs(T, C, seed=4)
+    y = torch.empty_like(x)
+    H = torch.empty_like(logits)
+    ms = _time_loop(torch, lambda k: bp.ops.stream_mix_into(x, logits, H, y), args.steps, args.warmup)
+    per_tok = 64 + 4 * C * 2 + 64 + 4 * C * 2
+    gbs = per_tok * T / (ms / 1e3) / 1e9
+    return {
+        "metric": "fused projection + stream mix tokens/s; achieved HBM GB/s vs peak",
+        "value": T / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"fused projection + stream mix, T={T}, n=4, C={C} bf16"},
+        "roofline": {"bound": "hbm", "kernel": "stream_mix_fwd (fused Newton)", "achieved": gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": None},
+    }
+
+
+def bench_layer(args, bp, torch):
+    """Full layer step fwd+bwd, T=65536, n=4, C=7168."""
+    import workloads as W
+    T, C = W.CONFIG5_SHAPE["T"], W.CONFIG5_SHAPE["C"]
+    inp = W.layer_inputs(T, C, seed=5)
+    x, Wt, f, dxo, du = inp["x"], inp["W"], inp["f"], inp["dx_out"], inp["du"]
+    fw = bp.layer_fwd(x, Wt, f)
+    ws = bp.layer_workspace(T, C, x.device)
+    bw = bp.layer_bwd(x, Wt, f, fw, dxo, du, workspace=ws)
+    torch.cuda.synchronize()
+    fwd_ms = _time_loop(torch, lambda k: bp.ops.layer_fwd_into(x, Wt, f, fw), args.steps, args.warmup)
+    bwd_ms = _time_loop(torch, lambda k: bp.layer_bwd(x, Wt, f, fw, dxo, du, workspace=ws, out=bw),
+                        args.steps, args.warmup)
+    ms = fwd_ms + bwd_ms
+    D = 4 * C
+    fwd_bytes = T * (2 * D + 2 * C + 2 * C + 2 * D + 196)      # maps: x; mix: x, f, u, x_out
+    bwd_bytes = T * (2 * D + 2 * D + 2 * C + 2 * C + 2 * C     # dots: x, dxo, f, du, df
+                     + 2 * D + 2 * D + 2 * C + 2 * D          # dx: dxo, x, du, dx
+                     + 2 * D)                                  # dw: x
+    gbs = (fwd_bytes + bwd_bytes) / (ms / 1e3) / 1e9
+    return {
+        "metric": "mHC layer step fwd+bwd tokens/s; achieved HBM GB/s vs peak",
+        "value": T / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"mHC layer step fwd+bwd, T={T}, n=4, C={C} bf16, W [24, {D}]"},
+        "roofline": {"bound": "hbm", "kernel": "whole step (6 kernels)", "achieved": gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": None},
+        "kernels": {"fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
+                    "fwd_GBs": fwd_bytes / (fwd_ms / 1e3) / 1e9,
+                    "bwd_GBs": bwd_bytes / (bwd_ms / 1e3) / 1e9},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3])
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--cpu-sample", type=int, default=524288,
                     help="matrices the oracle baseline processes (about 10-30 s of CPU work)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -207,7 +279,12 @@ def main():
     bp.lib()
     if args.copy_probe_mib:
         copy_probe(torch, args.copy_probe_mib)
-    out = bench_projection(args, bp, torch, args.config)
+    if args.config == 4:
+        out = bench_mix(args, bp, torch)
+    elif args.config == 5:
+        out = bench_layer(args, bp, torch)
+    else:
+        out = bench_projection(args, bp, torch, args.config)
     print(json.dumps(out), flush=True)
 
 

@@ -192,6 +192,27 @@ def layer_fwd(x, W, f, *, eps=1e-6, solver="newton", max_iters=None, tol=None,
     return out
 
 
+def layer_fwd_into(x, W, f, out, *, eps=1e-6, solver="newton"):
+    """layer_fwd writing into the tensors of a previous result dict ``out``."""
+    o = make_opts(solver)
+    a = _layer_args(x, W, f, eps, o)
+    for k in ("u", "x_out", "rms", "logits", "H_pre", "H_post", "H_res"):
+        setattr(a, k, out[k].data_ptr())
+    with torch.cuda.device(x.device):
+        check(lib().mhc_layer_fwd(ctypes.byref(a), _stream(x.device)))
+    return out
+
+
+def stream_mix_into(x, logits, H_out, out, solver="newton"):
+    """Fused projection + stream mix into preallocated H_out and out."""
+    T, n, C = x.shape
+    o = make_opts(solver)
+    with torch.cuda.device(x.device):
+        check(lib().mhc_stream_mix(_ptr(x), _ptr(logits), _ptr(H_out), _ptr(out), T, n, C,
+                                   ctypes.byref(o), _stream(x.device)))
+    return out
+
+
 def layer_workspace(T, C, device, n=4):
     nbytes = lib().mhc_layer_workspace_bytes(T, n, C)
     if nbytes < 0:
