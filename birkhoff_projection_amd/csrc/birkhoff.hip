@@ -6,7 +6,8 @@
 // the whole solve in VGPRs (proj4.h) and writes four 16-byte stores.  There is
 // no cross-lane communication, so a tail wave simply masks off the lanes past
 // B.  The forward is bound by VALU work (exp2/log2/rcp and the Newton solve);
-// the backward is straight-line and bound by HBM traffic (192 bytes/matrix).
+// the backward is straight-line and bound by HBM traffic (192 bytes/matrix),
+// so it uses one row per lane instead (see birkhoff_bwd_kernel).
 #include "kernels.h"
 #include "proj4.h"
 
@@ -52,17 +53,25 @@ __global__ __launch_bounds__(kBlock) void birkhoff_fwd_kernel(const float* logit
     if (iters != nullptr) iters[b] = (uint8_t)it;
 }
 
-__global__ __launch_bounds__(kBlock) void birkhoff_bwd_kernel(const float* __restrict__ P,
-                                                              const float* G, float* dA,
+// Backward: one row per lane (quad = one matrix, 64 matrices per 256-lane
+// workgroup), so loads and stores are contiguous 16-byte rows across lanes
+// and a launch has four times the waves of the forward.  Quads past B load
+// zeros (all-zero rows give a zero gradient) and skip the store, keeping every
+// quad fully active for the DPP reductions.
+__global__ __launch_bounds__(kBlock) void birkhoff_bwd_kernel(const float4* __restrict__ P,
+                                                              const float4* G, float4* dA,
                                                               int64_t B)
 {
-    const int64_t b = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    if (b >= B) return;
-    float p[16], g[16], d[16];
-    load16(P + 16 * b, p);
-    load16(G + 16 * b, g);
-    project_bwd(p, g, d);
-    store16(dA + 16 * b, d);
+    const int64_t r = (int64_t)blockIdx.x * kBlock + threadIdx.x;  // row 4 b + i
+    const bool ok = (r >> 2) < B;
+    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 p4 = ok ? P[r] : zero;
+    const float4 g4 = ok ? G[r] : zero;
+    const float p[4] = {p4.x, p4.y, p4.z, p4.w};
+    const float g[4] = {g4.x, g4.y, g4.z, g4.w};
+    float d[4];
+    project_bwd_row(p, g, d);
+    if (ok) dA[r] = make_float4(d[0], d[1], d[2], d[3]);
 }
 
 }  // namespace
@@ -83,8 +92,10 @@ hipError_t launch_birkhoff_fwd(const float* logits, float* P, uint8_t* iters, in
 hipError_t launch_birkhoff_bwd(const float* P, const float* G, float* dA, int64_t B,
                                hipStream_t stream)
 {
-    const dim3 grid((unsigned)((B + kBlock - 1) / kBlock));
-    hipLaunchKernelGGL(birkhoff_bwd_kernel, grid, dim3(kBlock), 0, stream, P, G, dA, B);
+    const dim3 grid((unsigned)((4 * B + kBlock - 1) / kBlock));
+    hipLaunchKernelGGL(birkhoff_bwd_kernel, grid, dim3(kBlock), 0, stream,
+                       reinterpret_cast<const float4*>(P), reinterpret_cast<const float4*>(G),
+                       reinterpret_cast<float4*>(dA), B);
     return hipGetLastError();
 }
 

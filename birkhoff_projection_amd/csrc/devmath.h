@@ -26,3 +26,25 @@ MHC_DEV float mhc_abs(float a) { return __builtin_fabsf(a); }
 // bf16 <-> fp32.  A bf16 is the top half of an fp32, so widening is a shift.
 MHC_DEV float mhc_bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 MHC_DEV float mhc_bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
+
+// Cross-lane reads inside a quad of 4 lanes (DPP quad_perm, no LDS).  With
+// bound_ctrl set, the compiler folds the move into the consuming VALU
+// instruction (v_add_f32_dpp), so a 4-lane sum costs two instructions.
+MHC_DEV float mhc_quad_xor1(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v),
+                                                              0xB1 /* quad_perm [1,0,3,2] */,
+                                                              0xF, 0xF, true));
+}
+MHC_DEV float mhc_quad_xor2(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v),
+                                                              0x4E /* quad_perm [2,3,0,1] */,
+                                                              0xF, 0xF, true));
+}
+// Sum over the 4 lanes of a quad; every lane of the quad gets the total.
+MHC_DEV float mhc_quad_sum(float v)
+{
+    v += mhc_quad_xor1(v);
+    return v + mhc_quad_xor2(v);
+}

@@ -44,9 +44,13 @@ constexpr float kFltEps = 1.1920928955078125e-07f;
 // units; starting the backtracking at this length instead saves the many
 // halvings that would otherwise be spent getting back down.
 constexpr float kMaxStep = 8.f;
-// The noise-floor stop below is only allowed once the column residual is this
-// small; farther out a step that does not lower the residual is backtracked.
-constexpr float kFlatResidual = 1e-4f;
+// Below this column residual (about 4x the fp32 rounding floor of a column
+// sum of four row-softmax entries) a trial is judged by the residual alone,
+// and one that does not lower it marks the noise floor and ends the solve.
+constexpr float kNoiseFloor = 4e-6f;
+// Curvature test of the line search: accept a trial whose directional
+// derivative is at most this fraction of the initial one's magnitude.
+constexpr float kCurvature = 0.9f;
 // Floor on a column mass before its logarithm is taken.
 constexpr float kMinMass = 7.8886091e-31f;  // 2^-100
 
@@ -58,19 +62,16 @@ struct SolverOpts {
     int warm_sweeps;  // log-domain Sinkhorn sweeps before Newton
 };
 
-// Value, column sums and row-softmax matrix of the semi-dual at g.
+// Column sums and row-softmax matrix of the semi-dual at g.
 struct Eval {
     float P[16];
     float c[4];
-    float psi;    // base-2 objective
-    float scale;  // sum of the magnitudes of the terms psi is summed from
-    float res;    // max_j |c_j - 1|
+    float res;  // max_j |c_j - 1|
 };
 
 // Row softmax of a + 1 g^T (g3 = 0) with the row max-shift before exp2.
 MHC_DEV void evaluate(const float* a, float g0, float g1, float g2, Eval& E)
 {
-    float lse = 0.f, lse_abs = 0.f;
     E.c[0] = E.c[1] = E.c[2] = E.c[3] = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -83,22 +84,16 @@ MHC_DEV void evaluate(const float* a, float g0, float g1, float g2, Eval& E)
         const float e1 = mhc_exp2(z1 - m);
         const float e2 = mhc_exp2(z2 - m);
         const float e3 = mhc_exp2(z3 - m);
-        const float s = (e0 + e1) + (e2 + e3);
-        const float r = mhc_rcp(s);
+        const float r = mhc_rcp((e0 + e1) + (e2 + e3));
         E.P[4 * i + 0] = e0 * r;
         E.P[4 * i + 1] = e1 * r;
         E.P[4 * i + 2] = e2 * r;
         E.P[4 * i + 3] = e3 * r;
-        const float l = m + mhc_log2(s);
-        lse += l;
-        lse_abs += mhc_abs(l);
         E.c[0] += E.P[4 * i + 0];
         E.c[1] += E.P[4 * i + 1];
         E.c[2] += E.P[4 * i + 2];
         E.c[3] += E.P[4 * i + 3];
     }
-    E.psi = lse - ((g0 + g1) + g2);
-    E.scale = lse_abs + (mhc_abs(g0) + mhc_abs(g1)) + mhc_abs(g2);
     E.res = mhc_max(mhc_max(mhc_abs(E.c[0] - 1.f), mhc_abs(E.c[1] - 1.f)),
                     mhc_max(mhc_abs(E.c[2] - 1.f), mhc_abs(E.c[3] - 1.f)));
 }
@@ -178,111 +173,157 @@ MHC_DEV float ridge(const Weights& w)
 constexpr uint32_t kNotConverged = 255u;
 MHC_DEV uint32_t iters_code(int n) { return n > 254 ? 254u : (uint32_t)n; }
 
-// Forward projection of one matrix by Newton's method on the semi-dual.
-//   a_nat : the 16 logits (natural units), row-major
-//   P_out : the projected matrix
-//   returns the Newton iteration count (warm sweeps not counted), or
-//   kNotConverged when max_iters or the line search ran out first.
-MHC_DEV uint32_t project_newton(const float* a_nat, float* P_out, const SolverOpts& o)
+// Newton's method on the semi-dual for one matrix, as a state machine:
+//
+//   init():  base-2 logits with each row shifted to maximum 0; evaluate at
+//            g = 0; warm_sweeps log-domain Sinkhorn sweeps (g_j -= log c_j,
+//            re-gauged so g3 = 0; a column whose entries all underflowed has
+//            its mass floored so the step stays finite); first Newton
+//            direction.
+//   step():  one trial point g + t d.  psi is convex along the line, so its
+//            derivative psi'(s) = (c(s) - 1) . d rises monotonically from
+//            psi'(0) = slope < 0; a trial is accepted when
+//            psi'(t) <= kCurvature |slope| (it has not overshot the line
+//            minimum by much), which needs only the column sums the
+//            evaluation already has -- no logarithms.  Near the fp32 noise
+//            floor (residual <= kNoiseFloor) a trial is accepted only if it
+//            lowers the residual, and one that does not ends the solve.  A
+//            rejected trial halves t.  Every trial reaching the tolerance is
+//            accepted.
+// The Newton direction solves the Laplacian system of the Hessian with a
+// relative ridge (Kron reduction); its first trial step is capped at kMaxStep.
+struct NewtonLane {
+    float a[16];         // base-2 logits, rows shifted to max 0
+    float g0, g1, g2;    // accepted potentials (g3 = 0)
+    float d0, d1, d2;    // direction (base 2)
+    float t, res, slope; // step length, residual, psi'(0) along d
+    int newton, trials;  // Newton directions taken, halvings this step
+    uint32_t code;       // result when done
+    bool done;
+};
+
+// Newton direction at E (natural-units solve, returned in base-2 units),
+// slope psi'(0) along it, and the capped first step length.
+MHC_DEV void newton_direction(const Eval& E, float& d0, float& d1, float& d2, float& slope,
+                              float& t)
 {
-    // base-2 logits, each row shifted so that its maximum is 0
-    float a[16];
+    const Weights w = laplacian_weights(E.P);
+    const float lam = ridge(w);
+    float n0, n1, n2;
+    laplacian_solve(w.w01, w.w02, w.w03, w.w12, w.w13, w.w23, lam, 1.f - E.c[0], 1.f - E.c[1],
+                    1.f - E.c[2], n0, n1, n2);
+    d0 = n0 * kLog2e;
+    d1 = n1 * kLog2e;
+    d2 = n2 * kLog2e;
+    slope = (E.c[0] - 1.f) * d0 + (E.c[1] - 1.f) * d1 + (E.c[2] - 1.f) * d2;
+    const float dmax = mhc_max(mhc_max(mhc_abs(d0), mhc_abs(d1)), mhc_abs(d2));
+    t = mhc_min(1.f, kMaxStep * mhc_rcp(dmax));
+}
+
+MHC_DEV void newton_take(NewtonLane& s, const Eval& E) { s.res = E.res; }
+
+MHC_DEV void newton_init(NewtonLane& s, const float* a_nat, const SolverOpts& o)
+{
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const float m = mhc_max(mhc_max(a_nat[4 * i], a_nat[4 * i + 1]),
                                 mhc_max(a_nat[4 * i + 2], a_nat[4 * i + 3]));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) a[4 * i + j] = (a_nat[4 * i + j] - m) * kLog2e;
+        for (int j = 0; j < 4; ++j) s.a[4 * i + j] = (a_nat[4 * i + j] - m) * kLog2e;
     }
-
-    float g0 = 0.f, g1 = 0.f, g2 = 0.f;     // accepted potentials
-    float d0 = 0.f, d1 = 0.f, d2 = 0.f;     // current direction (base 2)
-    float t = 0.f;                          // current step length
-    float psi = 0.f, res = 0.f, slope = 0.f;
-    int warm = o.warm_sweeps;
-    int newton = 0;                         // Newton directions taken
-    int trials = 0;                         // backtracking halvings this step
-    bool first = true;
-    bool in_warm = false;
+    s.g0 = s.g1 = s.g2 = 0.f;
+    s.newton = 0;
+    s.trials = 0;
     Eval E;
-
-    for (;;) {
-        const float t0 = g0 + t * d0, t1 = g1 + t * d1, t2 = g2 + t * d2;
-        evaluate(a, t0, t1, t2, E);
-
-        bool accept;
-        if (first || in_warm) {
-            accept = true;
-        } else {
-            // Armijo on the convex objective -- while it can judge the step.
-            // Close to the solution the change a Newton step predicts,
-            // |t slope|, falls below the fp32 rounding noise of the objective
-            // (set by the size of the terms it is summed from, not by its own
-            // size).  From there on the column-sum residual decides: a step
-            // that lowers it is taken; one that does not is backtracked, or,
-            // once the residual is already small, marks the fp32 noise floor
-            // and ends the solve at the better point.
-            const bool unresolved = t * mhc_abs(slope) <= 64.f * kFltEps * E.scale;
-            if (unresolved) {
-                accept = E.res < res;
-                if (!accept && res <= kFlatResidual) break;
-            } else {
-                accept = E.psi <= psi + 1e-4f * t * slope;
-            }
-        }
-
-        if (accept) {
-            first = false;
-            g0 = t0;
-            g1 = t1;
-            g2 = t2;
-            psi = E.psi;
-            res = E.res;
-            trials = 0;
-            if (res <= o.tol) {
-#pragma unroll
-                for (int k = 0; k < 16; ++k) P_out[k] = E.P[k];
-                return iters_code(newton);
-            }
-            if (warm > 0) {
-                // log-domain Sinkhorn sweep: scale every column to unit sum
-                // (g_j -= log c_j), re-gauged so that g3 stays 0.  A column
-                // whose entries all underflowed has c_j = 0; its mass is
-                // floored so that the step stays finite (a factor 2^100).
-                const float l3 = mhc_log2(mhc_max(E.c[3], kMinMass));
-                d0 = l3 - mhc_log2(mhc_max(E.c[0], kMinMass));
-                d1 = l3 - mhc_log2(mhc_max(E.c[1], kMinMass));
-                d2 = l3 - mhc_log2(mhc_max(E.c[2], kMinMass));
-                t = 1.f;
-                --warm;
-                in_warm = true;
-                continue;
-            }
-            in_warm = false;
-            if (newton >= o.max_iters) break;
-            ++newton;
-            const Weights w = laplacian_weights(E.P);
-            const float lam = ridge(w);
-            float n0, n1, n2;
-            laplacian_solve(w.w01, w.w02, w.w03, w.w12, w.w13, w.w23, lam,
-                            1.f - E.c[0], 1.f - E.c[1], 1.f - E.c[2], n0, n1, n2);
-            d0 = n0 * kLog2e;
-            d1 = n1 * kLog2e;
-            d2 = n2 * kLog2e;
-            slope = (E.c[0] - 1.f) * d0 + (E.c[1] - 1.f) * d1 + (E.c[2] - 1.f) * d2;
-            const float dmax = mhc_max(mhc_max(mhc_abs(d0), mhc_abs(d1)), mhc_abs(d2));
-            t = mhc_min(1.f, kMaxStep * mhc_rcp(dmax));
-        } else {
-            if (++trials > 30) break;
-            t *= 0.5f;
+    evaluate(s.a, 0.f, 0.f, 0.f, E);
+    newton_take(s, E);
+    s.done = s.res <= o.tol;
+    s.code = 0;
+    for (int w = 0; w < o.warm_sweeps; ++w) {
+        const float l3 = mhc_log2(mhc_max(E.c[3], kMinMass));
+        const float n0 = s.g0 + (l3 - mhc_log2(mhc_max(E.c[0], kMinMass)));
+        const float n1 = s.g1 + (l3 - mhc_log2(mhc_max(E.c[1], kMinMass)));
+        const float n2 = s.g2 + (l3 - mhc_log2(mhc_max(E.c[2], kMinMass)));
+        Eval F;
+        evaluate(s.a, n0, n1, n2, F);
+        if (!s.done) {
+            s.g0 = n0;
+            s.g1 = n1;
+            s.g2 = n2;
+            newton_take(s, F);
+            E = F;
+            s.done = s.res <= o.tol;
         }
     }
-    // Stopped at the noise floor, by max_iters or by the line search:
-    // hand back the row-stochastic P of the best accepted point.
-    evaluate(a, g0, g1, g2, E);
+    newton_direction(E, s.d0, s.d1, s.d2, s.slope, s.t);
+    if (!s.done && o.max_iters < 1) {
+        s.done = true;
+        s.code = kNotConverged;
+    }
+    s.newton = 1;
+}
+
+// One trial of a lane that is not done (the caller guarantees !s.done).
+MHC_DEV void newton_step(NewtonLane& s, const SolverOpts& o)
+{
+    const float t0 = s.g0 + s.t * s.d0, t1 = s.g1 + s.t * s.d1, t2 = s.g2 + s.t * s.d2;
+    Eval E;
+    evaluate(s.a, t0, t1, t2, E);
+    float nd0, nd1, nd2, nslope, nt;
+    newton_direction(E, nd0, nd1, nd2, nslope, nt);
+
+    const float dphi = (E.c[0] - 1.f) * s.d0 + (E.c[1] - 1.f) * s.d1 + (E.c[2] - 1.f) * s.d2;
+    const bool near_floor = s.res <= kNoiseFloor;
+    const bool accept = E.res <= o.tol ||
+                        (near_floor ? E.res < s.res : dphi <= kCurvature * mhc_abs(s.slope));
+    const bool floor = !accept && near_floor;
+
+    if (accept) {
+        s.g0 = t0;
+        s.g1 = t1;
+        s.g2 = t2;
+        newton_take(s, E);
+        s.d0 = nd0;
+        s.d1 = nd1;
+        s.d2 = nd2;
+        s.slope = nslope;
+        s.t = nt;
+        s.trials = 0;
+        if (s.res <= o.tol) {
+            s.done = true;
+            s.code = iters_code(s.newton);
+        } else if (s.newton >= o.max_iters) {
+            s.done = true;
+            s.code = kNotConverged;
+        } else {
+            ++s.newton;
+        }
+    } else {
+        s.t *= 0.5f;
+        ++s.trials;
+        if (floor || s.trials > 30) {
+            s.done = true;
+            s.code = kNotConverged;
+        }
+    }
+}
+
+// Forward projection of one matrix by Newton's method on the semi-dual.
+//   a_nat : the 16 logits (natural units), row-major
+//   P_out : the projected matrix (row-stochastic; doubly stochastic to tol)
+//   returns the Newton iteration count (warm sweeps not counted), or
+//   kNotConverged when max_iters, the noise floor or the line search stopped it.
+MHC_DEV uint32_t project_newton(const float* a_nat, float* P_out, const SolverOpts& o)
+{
+    NewtonLane s;
+    newton_init(s, a_nat, o);
+    while (!s.done) newton_step(s, o);
+    // P of the accepted point (the same arithmetic as when it was accepted)
+    Eval E;
+    evaluate(s.a, s.g0, s.g1, s.g2, E);
 #pragma unroll
     for (int k = 0; k < 16; ++k) P_out[k] = E.P[k];
-    return E.res <= o.tol ? iters_code(newton) : kNotConverged;
+    return s.code;
 }
 
 // Forward projection of one matrix by Sinkhorn-Knopp sweeps (each sweep:
@@ -383,6 +424,35 @@ MHC_DEV void project_bwd(const float* P, const float* G, float* dA)
 #pragma unroll
         for (int j = 0; j < 4; ++j) dA[4 * i + j] = P[4 * i + j] * hc[j];
     }
+}
+
+// The same backward with one ROW per lane: the 4 lanes of a quad hold the 4
+// rows of one matrix (p, g = row i of P and G), column sums over rows are
+// quad DPP reductions, and the 3x3 solve is repeated in the 4 lanes.  Returns
+// row i of dA.  All four lanes of a quad must be active.
+MHC_DEV void project_bwd_row(const float* p, const float* g, float* da)
+{
+    float gc[4];
+    centred_row(p, g, gc);
+    const float rhs0 = mhc_quad_sum(p[0] * gc[0]);
+    const float rhs1 = mhc_quad_sum(p[1] * gc[1]);
+    const float rhs2 = mhc_quad_sum(p[2] * gc[2]);
+    Weights w;
+    w.w01 = mhc_quad_sum(p[0] * p[1]);
+    w.w02 = mhc_quad_sum(p[0] * p[2]);
+    w.w03 = mhc_quad_sum(p[0] * p[3]);
+    w.w12 = mhc_quad_sum(p[1] * p[2]);
+    w.w13 = mhc_quad_sum(p[1] * p[3]);
+    w.w23 = mhc_quad_sum(p[2] * p[3]);
+    const float lam = ridge(w);
+    float be0, be1, be2;
+    laplacian_solve(w.w01, w.w02, w.w03, w.w12, w.w13, w.w23, lam, rhs0, rhs1, rhs2, be0, be1,
+                    be2);
+    const float h[4] = {g[0] - be0, g[1] - be1, g[2] - be2, g[3]};
+    float hc[4];
+    centred_row(p, h, hc);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) da[j] = p[j] * hc[j];
 }
 
 }  // namespace mhc
