@@ -23,6 +23,16 @@ MHC_DEV float mhc_max(float a, float b) { return __builtin_fmaxf(a, b); }
 MHC_DEV float mhc_min(float a, float b) { return __builtin_fminf(a, b); }
 MHC_DEV float mhc_abs(float a) { return __builtin_fabsf(a); }
 
+// Makes a value opaque to the optimizer; emits no instruction.  The butterfly
+// reductions pass both candidates of a per-lane select through it, so the
+// select is not folded into one dynamically indexed array load (which the
+// backend lowers to a compare-and-select chain over the whole array).
+MHC_DEV float mhc_opaque(float x)
+{
+    asm("" : "+v"(x));
+    return x;
+}
+
 // bf16 <-> fp32.  A bf16 is the top half of an fp32, so widening is a shift.
 MHC_DEV float mhc_bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 MHC_DEV float mhc_bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }

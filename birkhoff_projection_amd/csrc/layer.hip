@@ -68,6 +68,11 @@ MHC_DEV uint4 pack8(const float* f)
                       pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
 }
 
+MHC_DEV uint32_t word(const uint4& q, int i)
+{
+    return i == 0 ? q.x : (i == 1 ? q.y : (i == 2 ? q.z : q.w));
+}
+
 MHC_DEV float sigmoid(float z) { return 1.f / (1.f + expf(-z)); }
 
 MHC_DEV bf16x8 as_bf16x8(const uint4& q) { return __builtin_bit_cast(bf16x8, q); }
@@ -93,8 +98,9 @@ MHC_DEV float wave_sum32(float* v)
         const int h = n / 2;
 #pragma unroll
         for (int k = 0; k < h; ++k) {
-            const float keep = up ? v[k + h] : v[k];
-            const float send = up ? v[k] : v[k + h];
+            const float lo = mhc_opaque(v[k]), hi = mhc_opaque(v[k + h]);
+            const float keep = up ? hi : lo;
+            const float send = up ? lo : hi;
             v[k] = keep + __shfl_xor(send, m);
         }
     }
@@ -146,18 +152,23 @@ __global__ __launch_bounds__(kBlock) void layer_maps_kernel(
         for (int ot = 0; ot < 2; ++ot) acc[tile][ot] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
     const uint4 zero4 = make_uint4(0, 0, 0, 0);
-#pragma unroll 2
+    // register double buffer over the K loop
+    uint4 na[4], nb[2];
+#pragma unroll
+    for (int tile = 0; tile < 4; ++tile) na[tile] = *reinterpret_cast<const uint4*>(xa[tile]);
+#pragma unroll
+    for (int ot = 0; ot < 2; ++ot) nb[ot] = *reinterpret_cast<const uint4*>(wb[ot]);
     for (int64_t k = 0; k < C; k += 32) {
         uint4 a[4], b[2];
 #pragma unroll
-        for (int tile = 0; tile < 4; ++tile) {
-            const uint4 q = *reinterpret_cast<const uint4*>(xa[tile] + k);
-            a[tile] = tok_ok[tile] ? q : zero4;
-        }
+        for (int tile = 0; tile < 4; ++tile) a[tile] = tok_ok[tile] ? na[tile] : zero4;
 #pragma unroll
-        for (int ot = 0; ot < 2; ++ot) {
-            const uint4 q = *reinterpret_cast<const uint4*>(wb[ot] + k);
-            b[ot] = map_ok[ot] ? q : zero4;
+        for (int ot = 0; ot < 2; ++ot) b[ot] = map_ok[ot] ? nb[ot] : zero4;
+        if (k + 32 < C) {
+#pragma unroll
+            for (int tile = 0; tile < 4; ++tile) na[tile] = *reinterpret_cast<const uint4*>(xa[tile] + k + 32);
+#pragma unroll
+            for (int ot = 0; ot < 2; ++ot) nb[ot] = *reinterpret_cast<const uint4*>(wb[ot] + k + 32);
         }
 #pragma unroll
         for (int tile = 0; tile < 4; ++tile)
@@ -299,36 +310,68 @@ __global__ __launch_bounds__(kBlock) void layer_dots_kernel(
             float acc[32];
 #pragma unroll
             for (int k = 0; k < 32; ++k) acc[k] = 0.f;
-            for (int64_t c = lane; c < C8; c += 64) {
-                float xs[4][8], gs[4][8], ff[8], uu[8];
+            // register double buffer: the next chunk's loads are in flight
+            // while the current chunk is reduced
+            uint4 nx[4], ng[4], nf, nu;
+            int64_t c = lane;
+            if (c < C8) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    unpack8(x[(t * 4 + j) * C8 + c], xs[j]);
-                    unpack8(gxo[(t * 4 + j) * C8 + c], gs[j]);
+                    nx[j] = x[(t * 4 + j) * C8 + c];
+                    ng[j] = gxo[(t * 4 + j) * C8 + c];
                 }
-                unpack8(f[t * C8 + c], ff);
-                unpack8(gu[t * C8 + c], uu);
-                float df[8];
+                nf = f[t * C8 + c];
+                nu = gu[t * C8 + c];
+            }
+            for (; c < C8; c += 64) {
+                const uint4 cx[4] = {nx[0], nx[1], nx[2], nx[3]};
+                const uint4 cg[4] = {ng[0], ng[1], ng[2], ng[3]};
+                const uint4 cf = nf, cu = nu;
+                const int64_t cn = c + 64;
+                if (cn < C8) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float s = ho[0] * gs[0][e];
-                    s = __builtin_fmaf(ho[1], gs[1][e], s);
-                    s = __builtin_fmaf(ho[2], gs[2][e], s);
-                    df[e] = __builtin_fmaf(ho[3], gs[3][e], s);
+                    for (int j = 0; j < 4; ++j) {
+                        nx[j] = x[(t * 4 + j) * C8 + cn];
+                        ng[j] = gxo[(t * 4 + j) * C8 + cn];
+                    }
+                    nf = f[t * C8 + cn];
+                    nu = gu[t * C8 + cn];
                 }
-                gf[t * C8 + c] = pack8(df);
+                uint32_t dfw[4];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
+                for (int q = 0; q < 4; ++q) {  // one 32-bit word = 2 columns
+                    float xs[4][2], gs[4][2], ff[2], uu[2];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) acc[j] = __builtin_fmaf(uu[e], xs[j][e], acc[j]);
+                    for (int j = 0; j < 4; ++j) {
+                        xs[j][0] = mhc_bf16_lo(word(cx[j], q));
+                        xs[j][1] = mhc_bf16_hi(word(cx[j], q));
+                        gs[j][0] = mhc_bf16_lo(word(cg[j], q));
+                        gs[j][1] = mhc_bf16_hi(word(cg[j], q));
+                    }
+                    ff[0] = mhc_bf16_lo(word(cf, q));
+                    ff[1] = mhc_bf16_hi(word(cf, q));
+                    uu[0] = mhc_bf16_lo(word(cu, q));
+                    uu[1] = mhc_bf16_hi(word(cu, q));
+                    float df[2];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[4 + i] = __builtin_fmaf(gs[i][e], ff[e], acc[4 + i]);
+                    for (int e = 0; e < 2; ++e) {
+                        float s = ho[0] * gs[0][e];
+                        s = __builtin_fmaf(ho[1], gs[1][e], s);
+                        s = __builtin_fmaf(ho[2], gs[2][e], s);
+                        df[e] = __builtin_fmaf(ho[3], gs[3][e], s);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
+                        for (int j = 0; j < 4; ++j) acc[j] = __builtin_fmaf(uu[e], xs[j][e], acc[j]);
 #pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            acc[8 + 4 * i + j] = __builtin_fmaf(gs[i][e], xs[j][e], acc[8 + 4 * i + j]);
+                        for (int i = 0; i < 4; ++i) acc[4 + i] = __builtin_fmaf(gs[i][e], ff[e], acc[4 + i]);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+                                acc[8 + 4 * i + j] = __builtin_fmaf(gs[i][e], xs[j][e], acc[8 + 4 * i + j]);
+                    }
+                    dfw[q] = pack_bf16x2(df[0], df[1]);
                 }
+                gf[t * C8 + c] = make_uint4(dfw[0], dfw[1], dfw[2], dfw[3]);
             }
             const float s = wave_sum32(acc);
             const int idx = (lane >> 1) & 31;
@@ -387,13 +430,17 @@ __global__ __launch_bounds__(kBlock) void layer_dots_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// dx: workgroup = a slab of 32 columns (all 4 streams: 128 flattened k) and a
-// range of 256 tokens (each wave 4 tiles of 16).  The slab of W sits in LDS
-// as [k][map] so that MFMA B operands are 16-byte LDS reads:
+// dx: workgroup = a slab of 64 columns (all 4 streams: 256 flattened k, and
+// whole 128-byte lines of every stream row, so no line is shared with a
+// workgroup on another XCD) and a range of 256 tokens (each wave 4 tiles of
+// 16).  The slab of W sits in LDS as [k][map] so MFMA B operands are 16-byte
+// LDS reads:
 //   dxn (16 tokens x 16 k) = dl (16 x 32 maps, hi + lo) * W^T (32 maps x 16 k)
-// dxn goes through LDS to the element-wise layout: lane = (token, 8 columns).
+// Each tile is done in two column halves: 8 k-tiles (4 streams x 32 columns)
+// of dxn go through LDS to the element-wise layout, lane = (token, 8 columns).
 // ---------------------------------------------------------------------------
-constexpr int kDxCols = 32;              // columns per stream in a slab
+constexpr int kDxCols = 64;              // columns per stream in a slab
+constexpr int kDxHalf = kDxCols / 2;     // columns per element-wise pass
 constexpr int kDxK = 4 * kDxCols;        // flattened k per slab
 constexpr int kDxTiles = 4;              // 16-token tiles per wave
 constexpr int kWPitch = 40;              // bf16 per LDS row of W (32 maps + pad)
@@ -405,16 +452,17 @@ __global__ __launch_bounds__(kBlock) void layer_dx_kernel(
     uint4* __restrict__ gx, int64_t T, int64_t C)
 {
     __shared__ __attribute__((aligned(16))) __bf16 sW[kDxK][kWPitch];
-    __shared__ float sD[4][16][kDxK + 4];
+    __shared__ float sD[4][16][4 * kDxHalf + 4];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int64_t c0 = (int64_t)blockIdx.x * kDxCols;
     const int64_t D = 4 * C;
     const int64_t C8 = C / 8;
-    // W slab -> LDS, transposed: sW[j*32 + cc][m] = W[m][j*C + c0 + cc]
-    for (int p = threadIdx.x; p < 32 * 4 * (kDxCols / 8); p += kBlock) {
-        const int m = p / (4 * (kDxCols / 8));
-        const int rem = p % (4 * (kDxCols / 8));
-        const int j = rem / (kDxCols / 8), q = rem % (kDxCols / 8);
+    // W slab -> LDS, transposed: sW[j*64 + cc][m] = W[m][j*C + c0 + cc]
+    constexpr int kPieces = kDxCols / 8;
+    for (int p = threadIdx.x; p < 32 * 4 * kPieces; p += kBlock) {
+        const int m = p / (4 * kPieces);
+        const int rem = p % (4 * kPieces);
+        const int j = rem / kPieces, q = rem % kPieces;
         uint4 v = make_uint4(0, 0, 0, 0);
         if (m < kMaps) v = *reinterpret_cast<const uint4*>(W + m * D + j * C + c0 + 8 * q);
         const bf16x8 b = as_bf16x8(v);
@@ -423,6 +471,7 @@ __global__ __launch_bounds__(kBlock) void layer_dx_kernel(
     }
     __syncthreads();
     const int row = lane & 15, kq = lane >> 4;
+    const int tl = lane >> 2, q = lane & 3;  // element-wise: token, 8-column chunk
     for (int tile = 0; tile < kDxTiles; ++tile) {
         const int64_t tt0 = (int64_t)blockIdx.y * (4 * kDxTiles * 16) + (int64_t)(w * kDxTiles + tile) * 16;
         // A operand: dl[token tt0 + row][maps 8 kq ..+7], split hi / lo
@@ -439,29 +488,11 @@ __global__ __launch_bounds__(kBlock) void layer_dx_kernel(
         }
         bf16x8 ahi, alo;
         split8(a8, ahi, alo);
-#pragma unroll
-        for (int nt = 0; nt < kDxK / 16; ++nt) {
-            const bf16x8 b = *reinterpret_cast<const bf16x8*>(&sW[nt * 16 + row][8 * kq]);
-            floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, b, acc, 0, 0, 0);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) sD[w][4 * kq + v][nt * 16 + row] = acc[v];
-        }
-        __syncthreads();
-        // element-wise: lane = (token tt0 + lane/4, columns c0 + 8 (lane%4) ..+7)
-        const int tl = lane >> 2, q = lane & 3;
+        // per-token element-wise factors of this lane's token
         const int64_t t = tt0 + tl;
-        if (t < T) {
-            const int64_t c8 = c0 / 8 + q;
-            float gs[4][8], xs[4][8], uu[8];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                unpack8(gxo[(t * 4 + i) * C8 + c8], gs[i]);
-                unpack8(x[(t * 4 + i) * C8 + c8], xs[i]);
-            }
-            unpack8(gu[t * C8 + c8], uu);
-            float H[16];
+        const bool tok = t < T;
+        float H[16], hp[4], inv = 0.f, sr = 0.f;
+        if (tok) {
             const float4* hr = reinterpret_cast<const float4*>(Hres + 16 * t);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
@@ -472,26 +503,72 @@ __global__ __launch_bounds__(kBlock) void layer_dx_kernel(
                 H[4 * k + 3] = v.w;
             }
             const float4 pq = reinterpret_cast<const float4*>(Hpre)[t];
-            const float hp[4] = {pq.x, pq.y, pq.z, pq.w};
-            const float inv = 1.f / rms[t];
-            const float sr = svec[t] * inv;
+            hp[0] = pq.x; hp[1] = pq.y; hp[2] = pq.z; hp[3] = pq.w;
+            inv = 1.f / rms[t];
+            sr = svec[t] * inv;
+        }
+        for (int h = 0; h < 2; ++h) {
+            // issue this half's stream loads first; their latency overlaps
+            // the MFMA and LDS work below
+            const int64_t c8 = (c0 + h * kDxHalf) / 8 + q;
+            const int64_t tc = tok ? t : 0;
+            uint4 lg[4], lx[4], lu;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                lg[i] = gxo[(tc * 4 + i) * C8 + c8];
+                lx[i] = x[(tc * 4 + i) * C8 + c8];
+            }
+            lu = gu[tc * C8 + c8];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                float o8[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float s = H[j] * gs[0][e];
-                    s = __builtin_fmaf(H[4 + j], gs[1][e], s);
-                    s = __builtin_fmaf(H[8 + j], gs[2][e], s);
-                    s = __builtin_fmaf(H[12 + j], gs[3][e], s);
-                    s = __builtin_fmaf(hp[j], uu[e], s);
-                    const float dxn = sD[w][tl][j * kDxCols + 8 * q + e];
-                    o8[e] = __builtin_fmaf(__builtin_fmaf(-xs[j][e], sr, dxn), inv, s);
+                for (int s = 0; s < kDxHalf / 16; ++s) {
+                    const int kk = j * kDxCols + h * kDxHalf + 16 * s;  // k-tile start in the slab
+                    const bf16x8 b = *reinterpret_cast<const bf16x8*>(&sW[kk + row][8 * kq]);
+                    floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, b, acc, 0, 0, 0);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) sD[w][4 * kq + v][j * kDxHalf + 16 * s + row] = acc[v];
                 }
-                gx[(t * 4 + j) * C8 + c8] = pack8(o8);
             }
+            __syncthreads();
+            if (tok) {
+                uint32_t ow[4][4];
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {  // one 32-bit word = 2 columns
+                    float gs[4][2], xs[4][2], uu[2];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        gs[i][0] = mhc_bf16_lo(word(lg[i], qq));
+                        gs[i][1] = mhc_bf16_hi(word(lg[i], qq));
+                        xs[i][0] = mhc_bf16_lo(word(lx[i], qq));
+                        xs[i][1] = mhc_bf16_hi(word(lx[i], qq));
+                    }
+                    uu[0] = mhc_bf16_lo(word(lu, qq));
+                    uu[1] = mhc_bf16_hi(word(lu, qq));
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        float o2[2];
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) {
+                            float s = H[j] * gs[0][e];
+                            s = __builtin_fmaf(H[4 + j], gs[1][e], s);
+                            s = __builtin_fmaf(H[8 + j], gs[2][e], s);
+                            s = __builtin_fmaf(H[12 + j], gs[3][e], s);
+                            s = __builtin_fmaf(hp[j], uu[e], s);
+                            const float dxn = sD[w][tl][j * kDxHalf + 8 * q + 2 * qq + e];
+                            o2[e] = __builtin_fmaf(__builtin_fmaf(-xs[j][e], sr, dxn), inv, s);
+                        }
+                        ow[j][qq] = pack_bf16x2(o2[0], o2[1]);
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    gx[(t * 4 + j) * C8 + c8] = make_uint4(ow[j][0], ow[j][1], ow[j][2], ow[j][3]);
+            }
+            __syncthreads();
         }
-        __syncthreads();
     }
 }
 
@@ -527,17 +604,28 @@ __global__ __launch_bounds__(kBlock) void layer_dw_kernel(
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
     const uint4 zero4 = make_uint4(0, 0, 0, 0);
+    // x chunk [32 tokens][64 k] = 256 16-byte pieces, 4 per lane, fetched one
+    // chunk ahead (register double buffer)
+    // lane's four pieces: rows (lane >> 3) + 8 i, 16-byte column (lane & 7)
+    const int pr = lane >> 3, pc = 8 * (lane & 7);
+    // branch-free: rows past the group or past T load row min(t, T - 1) and
+    // are replaced by zeros
+    auto piece = [&](int64_t t) -> uint4 {
+        const uint4 v = *reinterpret_cast<const uint4*>(x + (t < T ? t : T - 1) * D + k0 + pc);
+        return (t < T && t < tg1) ? v : zero4;
+    };
+    int64_t tf = tg0 + 32 * w + pr;
+    uint4 n0 = piece(tf), n1 = piece(tf + 8), n2 = piece(tf + 16), n3 = piece(tf + 24);
     for (int64_t tc = tg0 + 32 * w; tc < tg1; tc += 128) {
-        // stage x[tc .. tc+31][k0 .. k0+63]: 256 16-byte pieces, 4 per lane
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int p = lane + 64 * i;
-            const int tok = p >> 3, q = p & 7;
-            const int64_t t = tc + tok;
-            uint4 v = zero4;
-            if (t < T) v = *reinterpret_cast<const uint4*>(x + t * D + k0 + 8 * q);
-            *reinterpret_cast<uint4*>(&sX[w][tok][8 * q]) = v;
-        }
+        *reinterpret_cast<uint4*>(&sX[w][pr][pc]) = n0;
+        *reinterpret_cast<uint4*>(&sX[w][pr + 8][pc]) = n1;
+        *reinterpret_cast<uint4*>(&sX[w][pr + 16][pc]) = n2;
+        *reinterpret_cast<uint4*>(&sX[w][pr + 24][pc]) = n3;
+        tf += 128;
+        n0 = piece(tf);
+        n1 = piece(tf + 8);
+        n2 = piece(tf + 16);
+        n3 = piece(tf + 24);
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): LDS stores done
         __builtin_amdgcn_wave_barrier();
         bf16x8 ahi[2], alo[2];

@@ -146,8 +146,9 @@ MHC_DEV float wave_sum16(float* v)
         const int h = n / 2;
 #pragma unroll
         for (int k = 0; k < h; ++k) {
-            const float keep = up ? v[k + h] : v[k];
-            const float send = up ? v[k] : v[k + h];
+            const float lo = mhc_opaque(v[k]), hi = mhc_opaque(v[k + h]);
+            const float keep = up ? hi : lo;
+            const float send = up ? lo : hi;
             v[k] = keep + __shfl_xor(send, m);
         }
     }
