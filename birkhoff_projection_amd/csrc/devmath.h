@@ -33,6 +33,16 @@ MHC_DEV float mhc_opaque(float x)
     return x;
 }
 
+// Workgroup barrier that orders LDS traffic only: waits for this wave's LDS
+// operations, then s_barrier.  Unlike __syncthreads it does not drain the
+// wave's outstanding global loads and stores, so a streaming loop keeps its
+// HBM requests in flight across the barrier.  The memory clobber keeps the
+// compiler from moving memory accesses across it.
+MHC_DEV void mhc_lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // bf16 <-> fp32.  A bf16 is the top half of an fp32, so widening is a shift.
 MHC_DEV float mhc_bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 MHC_DEV float mhc_bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }

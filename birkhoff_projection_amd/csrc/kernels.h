@@ -41,12 +41,13 @@ struct LayerPtrs {
 };
 
 // Backward workspace layout: s[Tp] fp32 | dl^T hi [24][Tp] bf16 | dl^T lo
-// [24][Tp] bf16 | grad_W partials [groups][24][4C] fp32 (each 256-byte aligned).
+// [24][Tp] bf16 | W^T [4C][24] bf16 | grad_W partials [groups][24][4C] fp32
+// (each 256-byte aligned).
 struct LayerPlan {
     int64_t Tp;            // T rounded up to 64
     int64_t group_tokens;  // tokens per grad_W partial
     int64_t groups;
-    int64_t off_s, off_hi, off_lo, off_partial;
+    int64_t off_s, off_hi, off_lo, off_wt, off_partial;
     int64_t bytes;
 };
 

@@ -430,145 +430,194 @@ __global__ __launch_bounds__(kBlock) void layer_dots_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// dx: workgroup = a slab of 64 columns (all 4 streams: 256 flattened k, and
-// whole 128-byte lines of every stream row, so no line is shared with a
-// workgroup on another XCD) and a range of 256 tokens (each wave 4 tiles of
-// 16).  The slab of W sits in LDS as [k][map] so MFMA B operands are 16-byte
-// LDS reads:
-//   dxn (16 tokens x 16 k) = dl (16 x 32 maps, hi + lo) * W^T (32 maps x 16 k)
-// Each tile is done in two column halves: 8 k-tiles (4 streams x 32 columns)
-// of dxn go through LDS to the element-wise layout, lane = (token, 8 columns).
+// Wt = W transposed to [4C][24] bf16 (48 bytes per k), so that an MFMA
+// fragment of 8 maps at one k is a single 16-byte load in the dx pass.
 // ---------------------------------------------------------------------------
-constexpr int kDxCols = 64;              // columns per stream in a slab
-constexpr int kDxHalf = kDxCols / 2;     // columns per element-wise pass
-constexpr int kDxK = 4 * kDxCols;        // flattened k per slab
-constexpr int kDxTiles = 4;              // 16-token tiles per wave
-constexpr int kWPitch = 40;              // bf16 per LDS row of W (32 maps + pad)
+__global__ __launch_bounds__(kBlock) void layer_wt_kernel(const uint16_t* __restrict__ W,
+                                                          uint4* __restrict__ Wt, int64_t D)
+{
+    const int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (k >= D) return;
+    uint32_t v[kMaps / 2];
+#pragma unroll
+    for (int q = 0; q < kMaps / 2; ++q)
+        v[q] = (uint32_t)W[(2 * q) * D + k] | ((uint32_t)W[(2 * q + 1) * D + k] << 16);
+#pragma unroll
+    for (int q = 0; q < 3; ++q) Wt[3 * k + q] = make_uint4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+}
 
-__global__ __launch_bounds__(kBlock) void layer_dx_kernel(
+// ---------------------------------------------------------------------------
+// dx: workgroup = 16 tokens x all columns, in chunks of 128 columns of every
+// stream (512 flattened k).  Per chunk:
+//  1. wave w forms dxn = dl W for stream w on MFMA, transposed so that the
+//     tokens are the N dimension:
+//       dxn^T (16 k x 16 tokens) = Wt (16 k x 32 maps) * dl^T (32 maps x 16 tokens)
+//     A is a 16-byte load of Wt (lanes of maps 24..31 supply zeros), B is dl
+//     split into bf16 hi + lo and fixed for the workgroup.  A lane's D holds
+//     4 consecutive k of one token and goes to LDS as one 16-byte write.
+//  2. element-wise pass: wave w takes tokens 4w..4w+3 with lane = (token,
+//     8 columns), so each global access covers 4 rows x 256 contiguous bytes
+//     (row-contiguous access runs much closer to the HBM peak than many short
+//     row segments per instruction, which is what the MFMA layout would give).
+// Software pipeline: the vector-memory counter retires in order, so waiting
+// for any load also waits for every older load and store.  All loads of
+// chunk i+1 (Wt fragments and stream rows) are therefore issued before chunk
+// i is consumed, into the other of two register sets, and the LDS buffer is
+// double-buffered so that one barrier per chunk suffices.
+// ---------------------------------------------------------------------------
+constexpr int kDxTok = 16;                    // tokens per workgroup (MFMA N)
+constexpr int kDxChunk = 128;                 // columns per stream per chunk
+constexpr int kDxTiles = kDxChunk / 16;       // k-tiles per wave per chunk
+constexpr int kDxPitch = 4 * kDxChunk + 4;    // floats per LDS row (bank spread)
+
+struct DxLoads {
+    uint4 a[kDxTiles];  // Wt fragments of this wave's k-tiles
+    uint4 g[4], x[4], u;  // grad_x_out, x, grad_u of the lane's token and columns
+};
+
+struct DxLane {
+    const uint4* x;
+    const uint4* gxo;
+    const uint4* gu;
+    const uint4* Wt;
+    uint4* gx;
+    int64_t C, C8;
+    int64_t tr;      // token row of the element-wise lane (clamped into range)
+    bool tok;        // that token exists
+    int w, row, kq, cl;
+    float H[16], hp[4], inv, sr;
+    bf16x8 bhi, blo;
+};
+
+MHC_DEV void dx_issue(const DxLane& L, DxLoads& d, int64_t c0)
+{
+    // Wt rows past C (a ragged last chunk) are clamped; their products land
+    // in LDS columns that the element-wise pass never reads.  Lanes kq = 3
+    // (maps 24..31, which do not exist) load the piece of maps 0..7.
+    const int kqc = L.kq < 3 ? L.kq : 0;
+#pragma unroll
+    for (int s = 0; s < kDxTiles; ++s) {
+        int64_t c = c0 + 16 * s + L.row;
+        c = c < L.C ? c : L.C - 1;
+        d.a[s] = L.Wt[3 * (L.w * L.C + c) + kqc];
+    }
+    const bool col = c0 + 8 * L.cl < L.C;
+    const int64_t c8 = col ? c0 / 8 + L.cl : L.C8 - 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        d.g[i] = L.gxo[(L.tr * 4 + i) * L.C8 + c8];
+        d.x[i] = L.x[(L.tr * 4 + i) * L.C8 + c8];
+    }
+    d.u = L.gu[L.tr * L.C8 + c8];
+}
+
+MHC_DEV void dx_consume(const DxLane& L, const DxLoads& d, float (*sD)[kDxPitch], int64_t c0)
+{
+#pragma unroll
+    for (int s = 0; s < kDxTiles; ++s) {
+        // lanes kq = 3 hold a finite piece of another map range: their B
+        // (maps 24..31) is zero, so they add nothing
+        const bf16x8 a = as_bf16x8(d.a[s]);
+        floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, L.bhi, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, L.blo, acc, 0, 0, 0);
+        *reinterpret_cast<floatx4*>(&sD[L.row][L.w * kDxChunk + 16 * s + 4 * L.kq]) = acc;
+    }
+    mhc_lds_barrier();
+    const bool col = c0 + 8 * L.cl < L.C;
+    if (!(L.tok && col)) return;
+    const int tl = 4 * L.w + (L.kq);  // element-wise token of this lane (lane >> 4)
+    const int64_t c8 = c0 / 8 + L.cl;
+    float gs[4][8], uu[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) unpack8(d.g[i], gs[i]);
+    unpack8(d.u, uu);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float xs[8], dn[8], o8[8];
+        unpack8(d.x[j], xs);
+        const floatx4 d0 = *reinterpret_cast<const floatx4*>(&sD[tl][j * kDxChunk + 8 * L.cl]);
+        const floatx4 d1 = *reinterpret_cast<const floatx4*>(&sD[tl][j * kDxChunk + 8 * L.cl + 4]);
+        dn[0] = d0[0]; dn[1] = d0[1]; dn[2] = d0[2]; dn[3] = d0[3];
+        dn[4] = d1[0]; dn[5] = d1[1]; dn[6] = d1[2]; dn[7] = d1[3];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float sm = L.H[j] * gs[0][e];
+            sm = __builtin_fmaf(L.H[4 + j], gs[1][e], sm);
+            sm = __builtin_fmaf(L.H[8 + j], gs[2][e], sm);
+            sm = __builtin_fmaf(L.H[12 + j], gs[3][e], sm);
+            sm = __builtin_fmaf(L.hp[j], uu[e], sm);
+            o8[e] = __builtin_fmaf(__builtin_fmaf(-xs[e], L.sr, dn[e]), L.inv, sm);
+        }
+        L.gx[(L.tr * 4 + j) * L.C8 + c8] = pack8(o8);
+    }
+}
+
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void layer_dx_kernel(
     const uint4* __restrict__ x, const uint4* __restrict__ gxo, const uint4* __restrict__ gu,
-    const uint16_t* __restrict__ W, const float* __restrict__ Hpre, const float* __restrict__ Hres,
+    const uint4* __restrict__ Wt, const float* __restrict__ Hpre, const float* __restrict__ Hres,
     const float* __restrict__ rms, const float* __restrict__ glogits, const float* __restrict__ svec,
     uint4* __restrict__ gx, int64_t T, int64_t C)
 {
-    __shared__ __attribute__((aligned(16))) __bf16 sW[kDxK][kWPitch];
-    __shared__ float sD[4][16][4 * kDxHalf + 4];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int64_t c0 = (int64_t)blockIdx.x * kDxCols;
-    const int64_t D = 4 * C;
-    const int64_t C8 = C / 8;
-    // W slab -> LDS, transposed: sW[j*64 + cc][m] = W[m][j*C + c0 + cc]
-    constexpr int kPieces = kDxCols / 8;
-    for (int p = threadIdx.x; p < 32 * 4 * kPieces; p += kBlock) {
-        const int m = p / (4 * kPieces);
-        const int rem = p % (4 * kPieces);
-        const int j = rem / kPieces, q = rem % kPieces;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (m < kMaps) v = *reinterpret_cast<const uint4*>(W + m * D + j * C + c0 + 8 * q);
-        const bf16x8 b = as_bf16x8(v);
+    __shared__ __attribute__((aligned(16))) float sD[2][kDxTok][kDxPitch];
+    DxLane L;
+    const int lane = threadIdx.x & 63;
+    L.x = x; L.gxo = gxo; L.gu = gu; L.Wt = Wt; L.gx = gx;
+    L.C = C; L.C8 = C / 8;
+    L.w = threadIdx.x >> 6;
+    L.row = lane & 15;
+    L.kq = lane >> 4;
+    L.cl = lane & 15;
+    const int64_t t0 = (int64_t)blockIdx.x * kDxTok;
+    // B operand: dl[token t0 + row][maps 8 kq ..+7], split hi / lo
+    {
+        float b8[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sW[j * kDxCols + 8 * q + e][m] = b[e];
-    }
-    __syncthreads();
-    const int row = lane & 15, kq = lane >> 4;
-    const int tl = lane >> 2, q = lane & 3;  // element-wise: token, 8-column chunk
-    for (int tile = 0; tile < kDxTiles; ++tile) {
-        const int64_t tt0 = (int64_t)blockIdx.y * (4 * kDxTiles * 16) + (int64_t)(w * kDxTiles + tile) * 16;
-        // A operand: dl[token tt0 + row][maps 8 kq ..+7], split hi / lo
-        float a8[8];
-        const int64_t ta = tt0 + row;
-        const int m0 = 8 * kq;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a8[e] = 0.f;
-        if (ta < T && m0 < kMaps) {
-            const float4* src = reinterpret_cast<const float4*>(glogits + kMaps * ta + m0);
+        for (int e = 0; e < 8; ++e) b8[e] = 0.f;
+        if (t0 + L.row < T && L.kq < 3) {
+            const float4* src = reinterpret_cast<const float4*>(glogits + kMaps * (t0 + L.row) + 8 * L.kq);
             const float4 v0 = src[0], v1 = src[1];
-            a8[0] = v0.x; a8[1] = v0.y; a8[2] = v0.z; a8[3] = v0.w;
-            a8[4] = v1.x; a8[5] = v1.y; a8[6] = v1.z; a8[7] = v1.w;
+            b8[0] = v0.x; b8[1] = v0.y; b8[2] = v0.z; b8[3] = v0.w;
+            b8[4] = v1.x; b8[5] = v1.y; b8[6] = v1.z; b8[7] = v1.w;
         }
-        bf16x8 ahi, alo;
-        split8(a8, ahi, alo);
-        // per-token element-wise factors of this lane's token
-        const int64_t t = tt0 + tl;
-        const bool tok = t < T;
-        float H[16], hp[4], inv = 0.f, sr = 0.f;
-        if (tok) {
-            const float4* hr = reinterpret_cast<const float4*>(Hres + 16 * t);
+        split8(b8, L.bhi, L.blo);
+    }
+    // element-wise token of this lane: 4w + (lane >> 4)
+    {
+        const int64_t t = t0 + 4 * L.w + L.kq;
+        L.tok = t < T;
+        L.tr = L.tok ? t : T - 1;
+        const float4* hr = reinterpret_cast<const float4*>(Hres + 16 * L.tr);
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float4 v = hr[k];
-                H[4 * k] = v.x;
-                H[4 * k + 1] = v.y;
-                H[4 * k + 2] = v.z;
-                H[4 * k + 3] = v.w;
-            }
-            const float4 pq = reinterpret_cast<const float4*>(Hpre)[t];
-            hp[0] = pq.x; hp[1] = pq.y; hp[2] = pq.z; hp[3] = pq.w;
-            inv = 1.f / rms[t];
-            sr = svec[t] * inv;
+        for (int k = 0; k < 4; ++k) {
+            const float4 v = hr[k];
+            L.H[4 * k] = v.x;
+            L.H[4 * k + 1] = v.y;
+            L.H[4 * k + 2] = v.z;
+            L.H[4 * k + 3] = v.w;
         }
-        for (int h = 0; h < 2; ++h) {
-            // issue this half's stream loads first; their latency overlaps
-            // the MFMA and LDS work below
-            const int64_t c8 = (c0 + h * kDxHalf) / 8 + q;
-            const int64_t tc = tok ? t : 0;
-            uint4 lg[4], lx[4], lu;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                lg[i] = gxo[(tc * 4 + i) * C8 + c8];
-                lx[i] = x[(tc * 4 + i) * C8 + c8];
-            }
-            lu = gu[tc * C8 + c8];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-#pragma unroll
-                for (int s = 0; s < kDxHalf / 16; ++s) {
-                    const int kk = j * kDxCols + h * kDxHalf + 16 * s;  // k-tile start in the slab
-                    const bf16x8 b = *reinterpret_cast<const bf16x8*>(&sW[kk + row][8 * kq]);
-                    floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b, acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, b, acc, 0, 0, 0);
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) sD[w][4 * kq + v][j * kDxHalf + 16 * s + row] = acc[v];
-                }
-            }
-            __syncthreads();
-            if (tok) {
-                uint32_t ow[4][4];
-#pragma unroll
-                for (int qq = 0; qq < 4; ++qq) {  // one 32-bit word = 2 columns
-                    float gs[4][2], xs[4][2], uu[2];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        gs[i][0] = mhc_bf16_lo(word(lg[i], qq));
-                        gs[i][1] = mhc_bf16_hi(word(lg[i], qq));
-                        xs[i][0] = mhc_bf16_lo(word(lx[i], qq));
-                        xs[i][1] = mhc_bf16_hi(word(lx[i], qq));
-                    }
-                    uu[0] = mhc_bf16_lo(word(lu, qq));
-                    uu[1] = mhc_bf16_hi(word(lu, qq));
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        float o2[2];
-#pragma unroll
-                        for (int e = 0; e < 2; ++e) {
-                            float s = H[j] * gs[0][e];
-                            s = __builtin_fmaf(H[4 + j], gs[1][e], s);
-                            s = __builtin_fmaf(H[8 + j], gs[2][e], s);
-                            s = __builtin_fmaf(H[12 + j], gs[3][e], s);
-                            s = __builtin_fmaf(hp[j], uu[e], s);
-                            const float dxn = sD[w][tl][j * kDxHalf + 8 * q + 2 * qq + e];
-                            o2[e] = __builtin_fmaf(__builtin_fmaf(-xs[j][e], sr, dxn), inv, s);
-                        }
-                        ow[j][qq] = pack_bf16x2(o2[0], o2[1]);
-                    }
-                }
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    gx[(t * 4 + j) * C8 + c8] = make_uint4(ow[j][0], ow[j][1], ow[j][2], ow[j][3]);
-            }
-            __syncthreads();
-        }
+        const float4 pq = reinterpret_cast<const float4*>(Hpre)[L.tr];
+        L.hp[0] = pq.x; L.hp[1] = pq.y; L.hp[2] = pq.z; L.hp[3] = pq.w;
+        L.inv = 1.f / rms[L.tr];
+        L.sr = svec[L.tr] * L.inv;
+    }
+    // Branch-free pipeline (a conditional issue would make the compiler's
+    // wait at the join drain every load): the chunk count is padded to even,
+    // chunks past C load clamped addresses and do no element-wise work.
+    const int64_t n = (C + kDxChunk - 1) / kDxChunk;
+    DxLoads d0, d1;
+    // (the scheduling barriers keep the compiler from starting a chunk's
+    // consumption, and with it the waits, before the next chunk is issued)
+    dx_issue(L, d0, 0);
+    for (int64_t ci = 0; ci < n; ci += 2) {
+        dx_issue(L, d1, (ci + 1) * kDxChunk);
+        __builtin_amdgcn_sched_barrier(0);
+        dx_consume(L, d0, sD[0], ci * kDxChunk);
+        __builtin_amdgcn_sched_barrier(0);
+        dx_issue(L, d0, (ci + 2) * kDxChunk);
+        __builtin_amdgcn_sched_barrier(0);
+        dx_consume(L, d1, sD[1], (ci + 1) * kDxChunk);
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -710,7 +759,8 @@ LayerPlan layer_plan(int64_t T, int64_t C)
     p.off_s = 0;
     p.off_hi = (p.Tp * 4 + 255) / 256 * 256;
     p.off_lo = p.off_hi + (p.Tp * kMaps * 2 + 255) / 256 * 256;
-    p.off_partial = p.off_lo + (p.Tp * kMaps * 2 + 255) / 256 * 256;
+    p.off_wt = p.off_lo + (p.Tp * kMaps * 2 + 255) / 256 * 256;
+    p.off_partial = p.off_wt + (D * kMaps * 2 + 255) / 256 * 256;
     p.bytes = p.off_partial + p.groups * kMaps * D * 4;
     return p;
 }
@@ -751,10 +801,15 @@ hipError_t launch_layer_bwd(const LayerPtrs& a, int64_t T, int64_t C, hipStream_
                        (uint4*)a.grad_f, a.grad_logits, svec, dhi, dlo, T, p.Tp, C8);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 gdx((unsigned)(C / kDxCols), (unsigned)((T + 4 * kDxTiles * 16 - 1) / (4 * kDxTiles * 16)));
-    hipLaunchKernelGGL(layer_dx_kernel, gdx, dim3(kBlock), 0, stream, (const uint4*)a.x,
-                       (const uint4*)a.grad_x_out, (const uint4*)a.grad_u, (const uint16_t*)a.W,
-                       a.H_pre, a.H_res, a.rms, a.grad_logits, svec, (uint4*)a.grad_x, T, C);
+    uint4* wt = reinterpret_cast<uint4*>(ws + p.off_wt);
+    hipLaunchKernelGGL(layer_wt_kernel, dim3((unsigned)((4 * C + kBlock - 1) / kBlock)), dim3(kBlock),
+                       0, stream, (const uint16_t*)a.W, wt, 4 * C);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(layer_dx_kernel, dim3((unsigned)((T + kDxTok - 1) / kDxTok)), dim3(kBlock), 0,
+                       stream, (const uint4*)a.x, (const uint4*)a.grad_x_out, (const uint4*)a.grad_u,
+                       (const uint4*)wt, a.H_pre, a.H_res, a.rms, a.grad_logits, svec,
+                       (uint4*)a.grad_x, T, C);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 gdw((unsigned)(4 * C / kDwK), (unsigned)p.groups);

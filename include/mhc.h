@@ -221,7 +221,7 @@ mhc_status mhc_layer_fwd(const mhc_layer_args* a, void* stream);
  * f and the forward's rms, logits, H_pre, H_post, H_res: fills grad_x,
  * grad_f, grad_W (overwritten, not accumulated) and grad_logits.  The
  * projection's part is the implicit-differentiation backward of
- * mhc_birkhoff_bwd.  Four kernels on `stream`; the workspace must not be in
+ * mhc_birkhoff_bwd.  Five kernels on `stream`; the workspace must not be in
  * use by another call that overlaps on the device. */
 mhc_status mhc_layer_bwd(const mhc_layer_args* a, void* stream);
 
