@@ -109,83 +109,141 @@ MHC_DEV float wave_sum32(float* v)
 
 // ---------------------------------------------------------------------------
 // maps: 64 tokens per workgroup; wave w handles stream w, i.e. the K range
-// [w C, (w+1) C) of the flattened token vector.  MFMA 16x16x32 bf16:
+// [w C, (w+1) C) of the flattened token vector, in stages of 64 k.
+// MFMA 16x16x32 bf16:
 //   A (16 tokens x 32 k): lane l holds x[token 16*tile + l%16][k0 + 8*(l/16) ..+7]
 //   B (32 k x 16 maps):   lane l holds W[map 16*ot + l%16][k0 + 8*(l/16) ..+7]
 //   D (16 x 16):          lane l, v -> token 4*(l/16)+v, map l%16
+// Loading A straight from HBM in that layout would make every load
+// instruction touch 16 rows with 64 bytes each; instead each stage of x
+// (64 tokens x 128 bytes) is loaded with 8 rows x 128 contiguous bytes per
+// instruction into the wave's own LDS tile and A is read from there.  The
+// tile is private to the wave, so the K loop needs no workgroup barrier.
+// Every workgroup reads all of W as B fragments (from L2), so 64 tokens per
+// workgroup keeps that traffic at half the x traffic.
+// Pipeline as in the dx pass: stage i+1's loads (W fragments, x rows) are
+// issued into the other register set before stage i is consumed.
 // ---------------------------------------------------------------------------
+constexpr int kMapTok = 64;                 // tokens per workgroup
+constexpr int kMapTiles = kMapTok / 16;     // MFMA token tiles
+constexpr int kMapK = 64;                   // k per stage
+constexpr int kMapSteps = kMapK / 32;       // MFMA k-steps per stage
+constexpr int kMapPitch = kMapK + 8;        // bf16 per LDS row (bank spread)
+constexpr int kMapRowPieces = kMapK / 8;    // 16-byte pieces per row per stage
+constexpr int kMapRowsPerLoad = 64 / kMapRowPieces;
+constexpr int kMapPieces = kMapTok / kMapRowsPerLoad;  // x pieces per lane per stage
+
+struct MapLoads {
+    uint4 b[kMapSteps][2];  // W fragments
+    uint4 xr[kMapPieces];   // x rows: piece q -> token 8q + lane/8, 16 bytes at lane%8
+};
+
+struct MapLane {
+    const uint16_t* xrow[kMapPieces];  // stream-w row start of the piece's token (clamped)
+    const uint16_t* wrow[2];           // W row of map 16 ot + row (clamped), stream w
+    int64_t C;
+    int row, kq, pc, pr;               // piece column (lane % 8) and row (lane / 8)
+};
+
+MHC_DEV void maps_issue(const MapLane& L, MapLoads& d, int64_t k0)
+{
+    // k past C (ragged last stage) is clamped; those k-steps are skipped
+#pragma unroll
+    for (int s = 0; s < kMapSteps; ++s) {
+        int64_t k = k0 + 32 * s + 8 * L.kq;
+        k = k < L.C ? k : L.C - 8;
+#pragma unroll
+        for (int ot = 0; ot < 2; ++ot) d.b[s][ot] = *reinterpret_cast<const uint4*>(L.wrow[ot] + k);
+    }
+    int64_t k = k0 + 8 * L.pc;
+    k = k < L.C ? k : L.C - 8;
+#pragma unroll
+    for (int q = 0; q < kMapPieces; ++q) d.xr[q] = *reinterpret_cast<const uint4*>(L.xrow[q] + k);
+}
+
+MHC_DEV void maps_consume(const MapLane& L, const MapLoads& d, uint16_t (*sX)[kMapPitch],
+                          floatx4 (&acc)[kMapTiles][2], float (&ssq)[kMapTiles], int64_t k0)
+{
+#pragma unroll
+    for (int q = 0; q < kMapPieces; ++q)
+        *reinterpret_cast<uint4*>(&sX[kMapRowsPerLoad * q + L.pr][8 * L.pc]) = d.xr[q];
+    // the tile is read only by this wave and LDS is in order within a wave
+    const int64_t left = (L.C - k0) / 32;
+    const int ns = left < kMapSteps ? (int)left : kMapSteps;
+#pragma unroll
+    for (int s = 0; s < kMapSteps; ++s) {
+        if (s < ns) {
+#pragma unroll
+            for (int tile = 0; tile < kMapTiles; ++tile) {
+                const uint4 a = *reinterpret_cast<const uint4*>(&sX[16 * tile + L.row][32 * s + 8 * L.kq]);
+#pragma unroll
+                for (int ot = 0; ot < 2; ++ot)
+                    acc[tile][ot] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        as_bf16x8(a), as_bf16x8(d.b[s][ot]), acc[tile][ot], 0, 0, 0);
+                float f[8];
+                unpack8(a, f);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ssq[tile] = __builtin_fmaf(f[e], f[e], ssq[tile]);
+            }
+        }
+    }
+}
+
 template <int SOLVER>
 __global__ __launch_bounds__(kBlock) void layer_maps_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, float* __restrict__ logits,
     float* __restrict__ rms, float* __restrict__ Hpre, float* __restrict__ Hpost,
     float* __restrict__ Hres, int64_t T, int64_t C, float eps, SolverOpts o)
 {
-    __shared__ float sRed[4][64][kMaps + 1];
-    __shared__ float sSsq[4][64];
+    __shared__ __attribute__((aligned(16))) uint16_t sX[4][kMapTok][kMapPitch];
+    __shared__ float sRed[4][kMapTok][kMaps + 1];
+    __shared__ float sSsq[4][kMapTok];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int row = lane & 15, kq = lane >> 4;
-    const int64_t t0 = (int64_t)blockIdx.x * 64;
+    const int64_t t0 = (int64_t)blockIdx.x * kMapTok;
     const int64_t D = 4 * C;
-
-    const uint16_t* xa[4];
-    bool tok_ok[4];
+    MapLane L;
+    L.C = C;
+    L.row = lane & 15;
+    L.kq = lane >> 4;
+    L.pc = lane % kMapRowPieces;
+    L.pr = lane / kMapRowPieces;
 #pragma unroll
-    for (int tile = 0; tile < 4; ++tile) {
-        const int64_t t = t0 + 16 * tile + row;
-        tok_ok[tile] = t < T;
-        xa[tile] = x + ((tok_ok[tile] ? t : 0) * 4 + w) * C + 8 * kq;
+    for (int q = 0; q < kMapPieces; ++q) {
+        int64_t t = t0 + kMapRowsPerLoad * q + L.pr;
+        t = t < T ? t : T - 1;
+        L.xrow[q] = x + (t * 4 + w) * C;
     }
-    const uint16_t* wb[2];
-    bool map_ok[2];
 #pragma unroll
     for (int ot = 0; ot < 2; ++ot) {
-        const int m = 16 * ot + row;
-        map_ok[ot] = m < kMaps;
-        wb[ot] = W + (int64_t)(map_ok[ot] ? m : 0) * D + (int64_t)w * C + 8 * kq;
+        const int m = 16 * ot + L.row;
+        L.wrow[ot] = W + (int64_t)(m < kMaps ? m : kMaps - 1) * D + (int64_t)w * C;
     }
-    floatx4 acc[4][2];
-    float ssq[4];
+    floatx4 acc[kMapTiles][2];
+    float ssq[kMapTiles];
 #pragma unroll
-    for (int tile = 0; tile < 4; ++tile) {
+    for (int tile = 0; tile < kMapTiles; ++tile) {
         ssq[tile] = 0.f;
 #pragma unroll
         for (int ot = 0; ot < 2; ++ot) acc[tile][ot] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
-    const uint4 zero4 = make_uint4(0, 0, 0, 0);
-    // register double buffer over the K loop
-    uint4 na[4], nb[2];
-#pragma unroll
-    for (int tile = 0; tile < 4; ++tile) na[tile] = *reinterpret_cast<const uint4*>(xa[tile]);
-#pragma unroll
-    for (int ot = 0; ot < 2; ++ot) nb[ot] = *reinterpret_cast<const uint4*>(wb[ot]);
-    for (int64_t k = 0; k < C; k += 32) {
-        uint4 a[4], b[2];
-#pragma unroll
-        for (int tile = 0; tile < 4; ++tile) a[tile] = tok_ok[tile] ? na[tile] : zero4;
-#pragma unroll
-        for (int ot = 0; ot < 2; ++ot) b[ot] = map_ok[ot] ? nb[ot] : zero4;
-        if (k + 32 < C) {
-#pragma unroll
-            for (int tile = 0; tile < 4; ++tile) na[tile] = *reinterpret_cast<const uint4*>(xa[tile] + k + 32);
-#pragma unroll
-            for (int ot = 0; ot < 2; ++ot) nb[ot] = *reinterpret_cast<const uint4*>(wb[ot] + k + 32);
-        }
-#pragma unroll
-        for (int tile = 0; tile < 4; ++tile)
-#pragma unroll
-            for (int ot = 0; ot < 2; ++ot)
-                acc[tile][ot] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    as_bf16x8(a[tile]), as_bf16x8(b[ot]), acc[tile][ot], 0, 0, 0);
-#pragma unroll
-        for (int tile = 0; tile < 4; ++tile) {
-            float f[8];
-            unpack8(a[tile], f);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ssq[tile] = __builtin_fmaf(f[e], f[e], ssq[tile]);
-        }
+    // branch-free ping-pong over an even number of stages; a stage past C
+    // loads clamped addresses and does no MFMA
+    const int64_t n = (C + kMapK - 1) / kMapK;
+    MapLoads d0, d1;
+    maps_issue(L, d0, 0);
+    for (int64_t si = 0; si < n; si += 2) {
+        maps_issue(L, d1, (si + 1) * kMapK);
+        __builtin_amdgcn_sched_barrier(0);
+        maps_consume(L, d0, sX[w], acc, ssq, si * kMapK);
+        __builtin_amdgcn_sched_barrier(0);
+        maps_issue(L, d0, (si + 2) * kMapK);
+        __builtin_amdgcn_sched_barrier(0);
+        maps_consume(L, d1, sX[w], acc, ssq, (si + 1) * kMapK);
+        __builtin_amdgcn_sched_barrier(0);
     }
+    const int row = L.row, kq = L.kq;
 #pragma unroll
-    for (int tile = 0; tile < 4; ++tile) {
+    for (int tile = 0; tile < kMapTiles; ++tile) {
 #pragma unroll
         for (int ot = 0; ot < 2; ++ot) {
             const int m = 16 * ot + row;
@@ -768,7 +826,7 @@ LayerPlan layer_plan(int64_t T, int64_t C)
 hipError_t launch_layer_fwd(const LayerPtrs& a, int64_t T, int64_t C, float eps,
                             const SolverOpts& o, hipStream_t stream)
 {
-    const dim3 g1((unsigned)((T + 63) / 64));
+    const dim3 g1((unsigned)((T + kMapTok - 1) / kMapTok));
     if (o.solver == 0)
         hipLaunchKernelGGL(layer_maps_kernel<0>, g1, dim3(kBlock), 0, stream,
                            (const uint16_t*)a.x, (const uint16_t*)a.W, a.logits, a.rms, a.H_pre,
