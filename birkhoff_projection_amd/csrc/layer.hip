@@ -680,15 +680,78 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
 }
 
 // ---------------------------------------------------------------------------
-// dw: workgroup = 64 flattened k (inside one stream) x one token group; wave w
-// takes every 4th 32-token chunk of the group.  Per chunk the x tile is
-// staged in LDS ([token][k]) and read back transposed for the MFMA B operand:
+// dw: workgroup = 128 flattened k x one token group; wave w takes every 4th
+// 32-token chunk of the group.  Per chunk the x tile is staged in the wave's
+// own LDS region ([token][k], loaded as 4 rows x 256 bytes per instruction)
+// and read back transposed for the MFMA B operand:
 //   dW^T tile (32 maps x 16 k) += dlT (32 maps x 32 tokens) * x (32 tokens x 16 k)
-// The four waves' partials are summed in LDS and one partial per token group
-// is written; layer_dw_reduce adds the groups in a fixed order.
+// The chunk's dlT fragments (A, from L2) and x rows are issued together, one
+// chunk ahead, into the other of two register sets (the vector-memory
+// counter retires in order, so A loads issued after a prefetch would make
+// the MFMA wait for the prefetch).  The four waves' partials are summed in
+// LDS and one partial per token group is written; layer_dw_reduce adds the
+// groups in a fixed order.
 // ---------------------------------------------------------------------------
-constexpr int kDwK = 64;
-constexpr int kXPitch = kDwK + 8;
+constexpr int kDwK = 128;                   // flattened k per workgroup
+constexpr int kDwNt = kDwK / 16;            // 16-column MFMA tiles
+constexpr int kXPitch = kDwK + 8;           // bf16 per LDS row
+constexpr int kDwPieces = 32 * kDwK / 8 / 64;  // 16-byte x pieces per lane per chunk
+
+struct DwLoads {
+    uint4 ahi[2], alo[2];  // dlT fragments: maps 16 mt + row, tokens 8 kq ..+7
+    uint4 xr[kDwPieces];   // x: piece q -> token 4q + lane/16, 16 bytes at lane%16
+};
+
+MHC_DEV void dw_issue(DwLoads& d, const uint16_t* __restrict__ x, const __bf16* __restrict__ dlT_hi,
+                      const __bf16* __restrict__ dlT_lo, int64_t tc, int64_t T, int64_t Tp,
+                      int64_t tg1, int64_t D, int64_t k0, int lane)
+{
+    const int row = lane & 15, kq = lane >> 4;
+    // chunks past the group read a clamped chunk; their A is zeroed on use
+    const int64_t ta = tc + 32 < Tp ? tc : Tp - 32;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+        const int m = 16 * mt + row < kMaps ? 16 * mt + row : kMaps - 1;
+        d.ahi[mt] = *reinterpret_cast<const uint4*>(dlT_hi + m * Tp + ta + 8 * kq);
+        d.alo[mt] = *reinterpret_cast<const uint4*>(dlT_lo + m * Tp + ta + 8 * kq);
+    }
+#pragma unroll
+    for (int q = 0; q < kDwPieces; ++q) {
+        int64_t t = tc + 4 * q + (lane >> 4);
+        t = t < T ? t : T - 1;
+        d.xr[q] = *reinterpret_cast<const uint4*>(x + t * D + k0 + 8 * (lane & 15));
+    }
+}
+
+MHC_DEV void dw_consume(const DwLoads& d, uint16_t (*sX)[kXPitch], floatx4 (&acc)[2][kDwNt],
+                        bool live, int lane)
+{
+    const int row = lane & 15, kq = lane >> 4;
+#pragma unroll
+    for (int q = 0; q < kDwPieces; ++q)
+        *reinterpret_cast<uint4*>(&sX[4 * q + (lane >> 4)][8 * (lane & 15)]) = d.xr[q];
+    // the region is this wave's own and LDS is in order within a wave
+    if (!live) return;
+    bf16x8 ahi[2], alo[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+        // A rows 24..31 repeat map 23 (clamped load); they only feed D rows
+        // 24..31, which are never stored
+        ahi[mt] = as_bf16x8(d.ahi[mt]);
+        alo[mt] = as_bf16x8(d.alo[mt]);
+    }
+#pragma unroll
+    for (int nt = 0; nt < kDwNt; ++nt) {
+        bf16x8 b;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) b[e] = __builtin_bit_cast(__bf16, sX[8 * kq + e][16 * nt + row]);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[mt], b, acc[mt][nt], 0, 0, 0);
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[mt], b, acc[mt][nt], 0, 0, 0);
+        }
+    }
+}
 
 __global__ __launch_bounds__(kBlock) void layer_dw_kernel(
     const uint16_t* __restrict__ x, const __bf16* __restrict__ dlT_hi,
@@ -705,62 +768,26 @@ __global__ __launch_bounds__(kBlock) void layer_dw_kernel(
     const int64_t tg0 = g * group_tokens;
     int64_t tg1 = tg0 + group_tokens;
     if (tg1 > Tp) tg1 = Tp;
-    floatx4 acc[2][4];
+    floatx4 acc[2][kDwNt];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    const uint4 zero4 = make_uint4(0, 0, 0, 0);
-    // x chunk [32 tokens][64 k] = 256 16-byte pieces, 4 per lane, fetched one
-    // chunk ahead (register double buffer)
-    // lane's four pieces: rows (lane >> 3) + 8 i, 16-byte column (lane & 7)
-    const int pr = lane >> 3, pc = 8 * (lane & 7);
-    // branch-free: rows past the group or past T load row min(t, T - 1) and
-    // are replaced by zeros
-    auto piece = [&](int64_t t) -> uint4 {
-        const uint4 v = *reinterpret_cast<const uint4*>(x + (t < T ? t : T - 1) * D + k0 + pc);
-        return (t < T && t < tg1) ? v : zero4;
-    };
-    int64_t tf = tg0 + 32 * w + pr;
-    uint4 n0 = piece(tf), n1 = piece(tf + 8), n2 = piece(tf + 16), n3 = piece(tf + 24);
-    for (int64_t tc = tg0 + 32 * w; tc < tg1; tc += 128) {
-        *reinterpret_cast<uint4*>(&sX[w][pr][pc]) = n0;
-        *reinterpret_cast<uint4*>(&sX[w][pr + 8][pc]) = n1;
-        *reinterpret_cast<uint4*>(&sX[w][pr + 16][pc]) = n2;
-        *reinterpret_cast<uint4*>(&sX[w][pr + 24][pc]) = n3;
-        tf += 128;
-        n0 = piece(tf);
-        n1 = piece(tf + 8);
-        n2 = piece(tf + 16);
-        n3 = piece(tf + 24);
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): LDS stores done
-        __builtin_amdgcn_wave_barrier();
-        bf16x8 ahi[2], alo[2];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            const int m = 16 * mt + row;
-            uint4 vh = zero4, vl = zero4;
-            if (m < kMaps) {
-                vh = *reinterpret_cast<const uint4*>(dlT_hi + m * Tp + tc + 8 * kq);
-                vl = *reinterpret_cast<const uint4*>(dlT_lo + m * Tp + tc + 8 * kq);
-            }
-            ahi[mt] = as_bf16x8(vh);
-            alo[mt] = as_bf16x8(vl);
-        }
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-            bf16x8 b;
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                b[e] = __builtin_bit_cast(__bf16, sX[w][8 * kq + e][16 * nt + row]);
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[mt], b, acc[mt][nt], 0, 0, 0);
-                acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[mt], b, acc[mt][nt], 0, 0, 0);
-            }
-        }
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        __builtin_amdgcn_wave_barrier();
+        for (int nt = 0; nt < kDwNt; ++nt) acc[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // wave w: chunks tg0 + 32 (w + 4 i); the pair loop is branch-free (a chunk
+    // past the group loads clamped addresses and is not accumulated), so the
+    // compiler's waits stay one chunk behind the issue
+    DwLoads d0, d1;
+    const int64_t first = tg0 + 32 * w;
+    dw_issue(d0, x, dlT_hi, dlT_lo, first, T, Tp, tg1, D, k0, lane);
+    for (int64_t tc = first; tc < tg1; tc += 256) {
+        dw_issue(d1, x, dlT_hi, dlT_lo, tc + 128, T, Tp, tg1, D, k0, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        dw_consume(d0, sX[w], acc, true, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        dw_issue(d0, x, dlT_hi, dlT_lo, tc + 256, T, Tp, tg1, D, k0, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        dw_consume(d1, sX[w], acc, tc + 128 < tg1, lane);
+        __builtin_amdgcn_sched_barrier(0);
     }
     // sum the four waves' partials: wave 0 writes, the others add in turn
     for (int ww = 0; ww < 4; ++ww) {
@@ -768,7 +795,7 @@ __global__ __launch_bounds__(kBlock) void layer_dw_kernel(
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt)
+                for (int nt = 0; nt < kDwNt; ++nt)
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
                         float& dst = sR[16 * mt + 4 * kq + v][16 * nt + row];
@@ -807,7 +834,7 @@ LayerPlan layer_plan(int64_t T, int64_t C)
 {
     LayerPlan p;
     p.Tp = (T + 63) / 64 * 64;
-    const int64_t want_groups = 8;
+    const int64_t want_groups = 16;
     int64_t gt = (p.Tp + want_groups - 1) / want_groups;
     gt = (gt + 127) / 128 * 128;  // whole 4-wave x 32-token rounds
     if (gt < 128) gt = 128;
