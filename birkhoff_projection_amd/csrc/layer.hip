@@ -17,10 +17,11 @@
 //   maps   x W^T on bf16 MFMA with the per-token sum of squares in the same
 //          pass; epilogue: 1/r scaling, sigmoids, Birkhoff projection
 //   mix    read-mix and write-back
-//   dots   per-token reductions dH_pre, dH_post, dH_res and grad_f; epilogue:
+//   dots   per-token reductions dH_pre, dH_post, dH_res (read only); epilogue:
 //          sigmoid derivative and projection backward -> grad_logits
+//   wt     W transposed to [4C][24] for the dx pass
 //   dx     grad_x = H_res^T grad_x_out + H_pre grad_u + RMSNorm backward of
-//          grad_logits W, the latter on MFMA
+//          grad_logits W, the latter on MFMA; grad_f = H_post^T grad_x_out
 //   dw     grad_W partials = (grad_logits / r)^T x on MFMA, x transposed
 //          through LDS; then a fixed-order reduction over token groups
 //
@@ -344,97 +345,122 @@ __global__ __launch_bounds__(kBlock) void layer_mix_kernel(
 
 // ---------------------------------------------------------------------------
 // dots: wave w of workgroup b handles tokens 64 b + 16 w + [0, 16), one token
-// at a time across the wave; lanes stride over the 8-column chunks.
-// Per token the 24 partial dots are wave-reduced into LDS; then lanes 0..15
-// each finish one token: sigmoid derivative, projection backward, the RMSNorm
-// coefficient s = <dl, l> / (4C), and the transposed, r-scaled bf16 hi/lo
-// copy of dl that the dW pass uses as an MFMA operand.
+// at a time across the wave; lanes stride over the 8-column chunks.  The pass
+// only reads (grad_f, which needs grad_x_out alone, is written by the dx pass:
+// a small write stream mixed into this read stream costs far more than its
+// bytes).  The
+// (token, chunk) steps of a wave form one software pipeline: step i+1's loads
+// are issued into the other register set before step i is consumed, across
+// token boundaries too.  At a token's last chunk the 24 partial dots are
+// wave-reduced into LDS; then lanes 0..15 each finish one token: sigmoid
+// derivative, projection backward, the RMSNorm coefficient s = <dl, l> / (4C),
+// and the transposed, r-scaled bf16 hi/lo copy of dl that the dW pass uses as
+// an MFMA operand.
 // ---------------------------------------------------------------------------
+struct DotsLoads {
+    uint4 x[4], g[4], f, u;
+};
+
+struct DotsLane {
+    const uint4* x;
+    const uint4* f;
+    const uint4* gxo;
+    const uint4* gu;
+    int64_t T, C8, nch, tb;
+    int lane;
+};
+
+MHC_DEV void dots_issue(const DotsLane& L, DotsLoads& d, int64_t i)
+{
+    // steps past the wave's last one read clamped addresses and are never consumed
+    int64_t tl = i / L.nch;
+    tl = tl < 16 ? tl : 15;
+    int64_t t = L.tb + tl;
+    t = t < L.T ? t : L.T - 1;
+    int64_t c = L.lane + 64 * (i % L.nch);
+    c = c < L.C8 ? c : L.C8 - 1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        d.x[j] = L.x[(t * 4 + j) * L.C8 + c];
+        d.g[j] = L.gxo[(t * 4 + j) * L.C8 + c];
+    }
+    d.f = L.f[t * L.C8 + c];
+    d.u = L.gu[t * L.C8 + c];
+}
+
+MHC_DEV void dots_consume(const DotsLane& L, const DotsLoads& d, int64_t i, float (&acc)[32],
+                          float (*sDots)[kMaps])
+{
+    const int64_t tl = i / L.nch, ci = i % L.nch;
+    const int64_t t = L.tb + tl;
+    const int64_t c = L.lane + 64 * ci;
+    if (t < L.T && c < L.C8) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {  // one 32-bit word = 2 columns
+            float xs[4][2], gs[4][2], ff[2], uu[2];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                xs[j][0] = mhc_bf16_lo(word(d.x[j], q));
+                xs[j][1] = mhc_bf16_hi(word(d.x[j], q));
+                gs[j][0] = mhc_bf16_lo(word(d.g[j], q));
+                gs[j][1] = mhc_bf16_hi(word(d.g[j], q));
+            }
+            ff[0] = mhc_bf16_lo(word(d.f, q));
+            ff[1] = mhc_bf16_hi(word(d.f, q));
+            uu[0] = mhc_bf16_lo(word(d.u, q));
+            uu[1] = mhc_bf16_hi(word(d.u, q));
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[j] = __builtin_fmaf(uu[e], xs[j][e], acc[j]);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) acc[4 + k] = __builtin_fmaf(gs[k][e], ff[e], acc[4 + k]);
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[8 + 4 * k + j] = __builtin_fmaf(gs[k][e], xs[j][e], acc[8 + 4 * k + j]);
+            }
+        }
+    }
+    if (ci == L.nch - 1) {  // the token's last chunk: reduce its dots
+        const float sm = wave_sum32(acc);
+        const int idx = (L.lane >> 1) & 31;
+        if ((L.lane & 1) == 0 && idx < kMaps) sDots[tl][idx] = sm;
+#pragma unroll
+        for (int k = 0; k < 32; ++k) acc[k] = 0.f;
+    }
+}
+
 __global__ __launch_bounds__(kBlock) void layer_dots_kernel(
     const uint4* __restrict__ x, const uint4* __restrict__ f, const uint4* __restrict__ gxo,
     const uint4* __restrict__ gu, const float* __restrict__ Hpre, const float* __restrict__ Hpost,
     const float* __restrict__ Hres, const float* __restrict__ logits, const float* __restrict__ rms,
-    uint4* __restrict__ gf, float* __restrict__ glogits, float* __restrict__ svec,
-    __bf16* __restrict__ dlT_hi, __bf16* __restrict__ dlT_lo, int64_t T, int64_t Tp, int64_t C8)
+    float* __restrict__ glogits, float* __restrict__ svec, __bf16* __restrict__ dlT_hi,
+    __bf16* __restrict__ dlT_lo, int64_t T, int64_t Tp, int64_t C8)
 {
     __shared__ float sDots[4][16][kMaps];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int64_t tb = (int64_t)blockIdx.x * 64 + 16 * w;
-    for (int tl = 0; tl < 16; ++tl) {
-        const int64_t t = tb + tl;
-        if (t < T) {
-            const float4 hq = reinterpret_cast<const float4*>(Hpost)[t];
-            const float ho[4] = {hq.x, hq.y, hq.z, hq.w};
-            float acc[32];
+    DotsLane L;
+    L.x = x; L.f = f; L.gxo = gxo; L.gu = gu;
+    L.T = T; L.C8 = C8; L.nch = (C8 + 63) / 64; L.tb = tb; L.lane = lane;
+    float acc[32];
 #pragma unroll
-            for (int k = 0; k < 32; ++k) acc[k] = 0.f;
-            // register double buffer: the next chunk's loads are in flight
-            // while the current chunk is reduced
-            uint4 nx[4], ng[4], nf, nu;
-            int64_t c = lane;
-            if (c < C8) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    nx[j] = x[(t * 4 + j) * C8 + c];
-                    ng[j] = gxo[(t * 4 + j) * C8 + c];
-                }
-                nf = f[t * C8 + c];
-                nu = gu[t * C8 + c];
-            }
-            for (; c < C8; c += 64) {
-                const uint4 cx[4] = {nx[0], nx[1], nx[2], nx[3]};
-                const uint4 cg[4] = {ng[0], ng[1], ng[2], ng[3]};
-                const uint4 cf = nf, cu = nu;
-                const int64_t cn = c + 64;
-                if (cn < C8) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        nx[j] = x[(t * 4 + j) * C8 + cn];
-                        ng[j] = gxo[(t * 4 + j) * C8 + cn];
-                    }
-                    nf = f[t * C8 + cn];
-                    nu = gu[t * C8 + cn];
-                }
-                uint32_t dfw[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {  // one 32-bit word = 2 columns
-                    float xs[4][2], gs[4][2], ff[2], uu[2];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        xs[j][0] = mhc_bf16_lo(word(cx[j], q));
-                        xs[j][1] = mhc_bf16_hi(word(cx[j], q));
-                        gs[j][0] = mhc_bf16_lo(word(cg[j], q));
-                        gs[j][1] = mhc_bf16_hi(word(cg[j], q));
-                    }
-                    ff[0] = mhc_bf16_lo(word(cf, q));
-                    ff[1] = mhc_bf16_hi(word(cf, q));
-                    uu[0] = mhc_bf16_lo(word(cu, q));
-                    uu[1] = mhc_bf16_hi(word(cu, q));
-                    float df[2];
-#pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        float s = ho[0] * gs[0][e];
-                        s = __builtin_fmaf(ho[1], gs[1][e], s);
-                        s = __builtin_fmaf(ho[2], gs[2][e], s);
-                        df[e] = __builtin_fmaf(ho[3], gs[3][e], s);
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) acc[j] = __builtin_fmaf(uu[e], xs[j][e], acc[j]);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) acc[4 + i] = __builtin_fmaf(gs[i][e], ff[e], acc[4 + i]);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-#pragma unroll
-                            for (int j = 0; j < 4; ++j)
-                                acc[8 + 4 * i + j] = __builtin_fmaf(gs[i][e], xs[j][e], acc[8 + 4 * i + j]);
-                    }
-                    dfw[q] = pack_bf16x2(df[0], df[1]);
-                }
-                gf[t * C8 + c] = make_uint4(dfw[0], dfw[1], dfw[2], dfw[3]);
-            }
-            const float s = wave_sum32(acc);
-            const int idx = (lane >> 1) & 31;
-            if ((lane & 1) == 0 && idx < kMaps) sDots[w][tl][idx] = s;
-        }
+    for (int k = 0; k < 32; ++k) acc[k] = 0.f;
+    // 16 tokens x nch chunks: always an even number of steps
+    const int64_t steps = 16 * L.nch;
+    DotsLoads d0, d1;
+    dots_issue(L, d0, 0);
+    for (int64_t i = 0; i < steps; i += 2) {
+        dots_issue(L, d1, i + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        dots_consume(L, d0, i, acc, sDots[w]);
+        __builtin_amdgcn_sched_barrier(0);
+        dots_issue(L, d0, i + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        dots_consume(L, d1, i + 1, acc, sDots[w]);
+        __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
     if (lane >= 16) return;
@@ -514,7 +540,9 @@ __global__ __launch_bounds__(kBlock) void layer_wt_kernel(const uint16_t* __rest
 //     split into bf16 hi + lo and fixed for the workgroup.  A lane's D holds
 //     4 consecutive k of one token and goes to LDS as one 16-byte write.
 //  2. element-wise pass: wave w takes tokens 4w..4w+3 with lane = (token,
-//     8 columns), so each global access covers 4 rows x 256 contiguous bytes
+//     8 columns); it also writes grad_f = sum_i H_post[i] grad_x_out_i from
+//     the same grad_x_out loads.  Each global access covers 4 rows x 256
+//     contiguous bytes
 //     (row-contiguous access runs much closer to the HBM peak than many short
 //     row segments per instruction, which is what the MFMA layout would give).
 // Software pipeline: the vector-memory counter retires in order, so waiting
@@ -539,11 +567,12 @@ struct DxLane {
     const uint4* gu;
     const uint4* Wt;
     uint4* gx;
+    uint4* gf;
     int64_t C, C8;
     int64_t tr;      // token row of the element-wise lane (clamped into range)
     bool tok;        // that token exists
     int w, row, kq, cl;
-    float H[16], hp[4], inv, sr;
+    float H[16], hp[4], ho[4], inv, sr;
     bf16x8 bhi, blo;
 };
 
@@ -590,6 +619,17 @@ MHC_DEV void dx_consume(const DxLane& L, const DxLoads& d, float (*sD)[kDxPitch]
 #pragma unroll
     for (int i = 0; i < 4; ++i) unpack8(d.g[i], gs[i]);
     unpack8(d.u, uu);
+    {
+        float g8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float sm = L.ho[0] * gs[0][e];
+            sm = __builtin_fmaf(L.ho[1], gs[1][e], sm);
+            sm = __builtin_fmaf(L.ho[2], gs[2][e], sm);
+            g8[e] = __builtin_fmaf(L.ho[3], gs[3][e], sm);
+        }
+        L.gf[L.tr * L.C8 + c8] = pack8(g8);
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         float xs[8], dn[8], o8[8];
@@ -613,14 +653,15 @@ MHC_DEV void dx_consume(const DxLane& L, const DxLoads& d, float (*sD)[kDxPitch]
 
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void layer_dx_kernel(
     const uint4* __restrict__ x, const uint4* __restrict__ gxo, const uint4* __restrict__ gu,
-    const uint4* __restrict__ Wt, const float* __restrict__ Hpre, const float* __restrict__ Hres,
-    const float* __restrict__ rms, const float* __restrict__ glogits, const float* __restrict__ svec,
-    uint4* __restrict__ gx, int64_t T, int64_t C)
+    const uint4* __restrict__ Wt, const float* __restrict__ Hpre, const float* __restrict__ Hpost,
+    const float* __restrict__ Hres, const float* __restrict__ rms, const float* __restrict__ glogits,
+    const float* __restrict__ svec, uint4* __restrict__ gx, uint4* __restrict__ gf, int64_t T,
+    int64_t C)
 {
     __shared__ __attribute__((aligned(16))) float sD[2][kDxTok][kDxPitch];
     DxLane L;
     const int lane = threadIdx.x & 63;
-    L.x = x; L.gxo = gxo; L.gu = gu; L.Wt = Wt; L.gx = gx;
+    L.x = x; L.gxo = gxo; L.gu = gu; L.Wt = Wt; L.gx = gx; L.gf = gf;
     L.C = C; L.C8 = C / 8;
     L.w = threadIdx.x >> 6;
     L.row = lane & 15;
@@ -656,6 +697,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         }
         const float4 pq = reinterpret_cast<const float4*>(Hpre)[L.tr];
         L.hp[0] = pq.x; L.hp[1] = pq.y; L.hp[2] = pq.z; L.hp[3] = pq.w;
+        const float4 oq = reinterpret_cast<const float4*>(Hpost)[L.tr];
+        L.ho[0] = oq.x; L.ho[1] = oq.y; L.ho[2] = oq.z; L.ho[3] = oq.w;
         L.inv = 1.f / rms[L.tr];
         L.sr = svec[L.tr] * L.inv;
     }
@@ -883,7 +926,7 @@ hipError_t launch_layer_bwd(const LayerPtrs& a, int64_t T, int64_t C, hipStream_
     hipLaunchKernelGGL(layer_dots_kernel, dim3((unsigned)(p.Tp / 64)), dim3(kBlock), 0, stream,
                        (const uint4*)a.x, (const uint4*)a.f, (const uint4*)a.grad_x_out,
                        (const uint4*)a.grad_u, a.H_pre, a.H_post, a.H_res, a.logits, a.rms,
-                       (uint4*)a.grad_f, a.grad_logits, svec, dhi, dlo, T, p.Tp, C8);
+                       a.grad_logits, svec, dhi, dlo, T, p.Tp, C8);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     uint4* wt = reinterpret_cast<uint4*>(ws + p.off_wt);
@@ -893,8 +936,8 @@ hipError_t launch_layer_bwd(const LayerPtrs& a, int64_t T, int64_t C, hipStream_
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(layer_dx_kernel, dim3((unsigned)((T + kDxTok - 1) / kDxTok)), dim3(kBlock), 0,
                        stream, (const uint4*)a.x, (const uint4*)a.grad_x_out, (const uint4*)a.grad_u,
-                       (const uint4*)wt, a.H_pre, a.H_res, a.rms, a.grad_logits, svec,
-                       (uint4*)a.grad_x, T, C);
+                       (const uint4*)wt, a.H_pre, a.H_post, a.H_res, a.rms, a.grad_logits, svec,
+                       (uint4*)a.grad_x, (uint4*)a.grad_f, T, C);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 gdw((unsigned)(4 * C / kDwK), (unsigned)p.groups);
