@@ -51,6 +51,16 @@ constexpr float kNoiseFloor = 4e-6f;
 // Curvature test of the line search: accept a trial whose directional
 // derivative is at most this fraction of the initial one's magnitude.
 constexpr float kCurvature = 0.9f;
+// Step growth: an accepted full first trial whose directional derivative
+// still has at least this fraction of its initial magnitude shows that the
+// line minimum lies well beyond the Newton step (the objective is locally
+// exponential, not quadratic, along d), so the next iteration's first trial
+// is twice as long, up to kMaxGrow times the Newton step.
+constexpr float kFar = 0.25f;
+constexpr float kMaxGrow = 64.f;
+// Growth stops once the residual is below kGrowMinRes, where the iteration is
+// in its quadratic phase and an overshoot would only cost trials.
+constexpr float kGrowMinRes = 1e-4f;
 // Floor on a column mass before its logarithm is taken.
 constexpr float kMinMass = 7.8886091e-31f;  // 2^-100
 
@@ -197,15 +207,16 @@ struct NewtonLane {
     float g0, g1, g2;    // accepted potentials (g3 = 0)
     float d0, d1, d2;    // direction (base 2)
     float t, res, slope; // step length, residual, psi'(0) along d
+    float grow;          // first-trial multiple of the Newton step (>= 1)
     int newton, trials;  // Newton directions taken, halvings this step
     uint32_t code;       // result when done
     bool done;
 };
 
 // Newton direction at E (natural-units solve, returned in base-2 units),
-// slope psi'(0) along it, and the capped first step length.
+// slope psi'(0) along it, and the longest first step kMaxStep / max|d|.
 MHC_DEV void newton_direction(const Eval& E, float& d0, float& d1, float& d2, float& slope,
-                              float& t)
+                              float& tcap)
 {
     const Weights w = laplacian_weights(E.P);
     const float lam = ridge(w);
@@ -217,7 +228,7 @@ MHC_DEV void newton_direction(const Eval& E, float& d0, float& d1, float& d2, fl
     d2 = n2 * kLog2e;
     slope = (E.c[0] - 1.f) * d0 + (E.c[1] - 1.f) * d1 + (E.c[2] - 1.f) * d2;
     const float dmax = mhc_max(mhc_max(mhc_abs(d0), mhc_abs(d1)), mhc_abs(d2));
-    t = mhc_min(1.f, kMaxStep * mhc_rcp(dmax));
+    tcap = kMaxStep * mhc_rcp(dmax);
 }
 
 MHC_DEV void newton_take(NewtonLane& s, const Eval& E) { s.res = E.res; }
@@ -255,7 +266,10 @@ MHC_DEV void newton_init(NewtonLane& s, const float* a_nat, const SolverOpts& o)
             s.done = s.res <= o.tol;
         }
     }
-    newton_direction(E, s.d0, s.d1, s.d2, s.slope, s.t);
+    float tcap;
+    newton_direction(E, s.d0, s.d1, s.d2, s.slope, tcap);
+    s.grow = 1.f;
+    s.t = mhc_min(1.f, tcap);
     if (!s.done && o.max_iters < 1) {
         s.done = true;
         s.code = kNotConverged;
@@ -269,8 +283,8 @@ MHC_DEV void newton_step(NewtonLane& s, const SolverOpts& o)
     const float t0 = s.g0 + s.t * s.d0, t1 = s.g1 + s.t * s.d1, t2 = s.g2 + s.t * s.d2;
     Eval E;
     evaluate(s.a, t0, t1, t2, E);
-    float nd0, nd1, nd2, nslope, nt;
-    newton_direction(E, nd0, nd1, nd2, nslope, nt);
+    float nd0, nd1, nd2, nslope, ncap;
+    newton_direction(E, nd0, nd1, nd2, nslope, ncap);
 
     const float dphi = (E.c[0] - 1.f) * s.d0 + (E.c[1] - 1.f) * s.d1 + (E.c[2] - 1.f) * s.d2;
     const bool near_floor = s.res <= kNoiseFloor;
@@ -279,6 +293,11 @@ MHC_DEV void newton_step(NewtonLane& s, const SolverOpts& o)
     const bool floor = !accept && near_floor;
 
     if (accept) {
+        // a full first trial that stayed far from the line minimum doubles the
+        // next first trial; anything else resets it to the Newton step
+        const bool far = s.trials == 0 && s.t >= s.grow && dphi <= kFar * s.slope &&
+                         E.res > kGrowMinRes;
+        s.grow = far ? mhc_min(2.f * s.grow, kMaxGrow) : 1.f;
         s.g0 = t0;
         s.g1 = t1;
         s.g2 = t2;
@@ -287,7 +306,7 @@ MHC_DEV void newton_step(NewtonLane& s, const SolverOpts& o)
         s.d1 = nd1;
         s.d2 = nd2;
         s.slope = nslope;
-        s.t = nt;
+        s.t = mhc_min(s.grow, ncap);
         s.trials = 0;
         if (s.res <= o.tol) {
             s.done = true;
