@@ -80,7 +80,7 @@ struct Eval {
 };
 
 // Row softmax of a + 1 g^T (g3 = 0) with the row max-shift before exp2.
-MHC_DEV void evaluate(const float* a, float g0, float g1, float g2, Eval& E)
+MHC_DEV void evaluate_shifted(const float* a, float g0, float g1, float g2, Eval& E)
 {
     E.c[0] = E.c[1] = E.c[2] = E.c[3] = 0.f;
 #pragma unroll
@@ -103,6 +103,56 @@ MHC_DEV void evaluate(const float* a, float g0, float g1, float g2, Eval& E)
         E.c[1] += E.P[4 * i + 1];
         E.c[2] += E.P[4 * i + 2];
         E.c[3] += E.P[4 * i + 3];
+    }
+    E.res = mhc_max(mhc_max(mhc_abs(E.c[0] - 1.f), mhc_abs(E.c[1] - 1.f)),
+                    mhc_max(mhc_abs(E.c[2] - 1.f), mhc_abs(E.c[3] - 1.f)));
+}
+
+// The same row softmax from k = 2^a (a's rows have maximum 0, so k <= 1 with
+// one entry 1 per row): P_ij = k_ij u_j / sum_l k_il u_l with u_j = 2^g_j,
+// three exponentials instead of sixteen and no max-shift.  It is used when
+//  * every a_ij >= -126 (kfast, fixed per matrix): each k_ij is a normal
+//    float, so each product k_ij u_j carries the relative accuracy of its
+//    factors whatever u_j is, or under/overflows outright; and
+//  * every row sum is finite and at least 2^-60: a product that underflowed
+//    (2^(a+g) < 2^-126, since k <= 1) is then below 2^-66 of its row, and an
+//    overflow or a NaN shows up in the sum.
+// Otherwise the lane takes the max-shifted form.
+constexpr float kRowLo = 8.6736174e-19f;  // 2^-60
+constexpr float kRowHi = 3.4028235e38f;   // largest finite float
+constexpr float kMinLogit = -126.f;
+
+MHC_DEV void evaluate(const float* a, const float* k, bool kfast, float g0, float g1, float g2,
+                      Eval& E)
+{
+    if (!kfast) {
+        evaluate_shifted(a, g0, g1, g2, E);
+        return;
+    }
+    const float u0 = mhc_exp2(g0), u1 = mhc_exp2(g1), u2 = mhc_exp2(g2);
+    E.c[0] = E.c[1] = E.c[2] = E.c[3] = 0.f;
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float e0 = k[4 * i + 0] * u0;
+        const float e1 = k[4 * i + 1] * u1;
+        const float e2 = k[4 * i + 2] * u2;
+        const float e3 = k[4 * i + 3];
+        const float sum = (e0 + e1) + (e2 + e3);
+        ok = ok && sum >= kRowLo && sum <= kRowHi;
+        const float r = mhc_rcp(sum);
+        E.P[4 * i + 0] = e0 * r;
+        E.P[4 * i + 1] = e1 * r;
+        E.P[4 * i + 2] = e2 * r;
+        E.P[4 * i + 3] = e3 * r;
+        E.c[0] += E.P[4 * i + 0];
+        E.c[1] += E.P[4 * i + 1];
+        E.c[2] += E.P[4 * i + 2];
+        E.c[3] += E.P[4 * i + 3];
+    }
+    if (!ok) {
+        evaluate_shifted(a, g0, g1, g2, E);
+        return;
     }
     E.res = mhc_max(mhc_max(mhc_abs(E.c[0] - 1.f), mhc_abs(E.c[1] - 1.f)),
                     mhc_max(mhc_abs(E.c[2] - 1.f), mhc_abs(E.c[3] - 1.f)));
@@ -204,6 +254,8 @@ MHC_DEV uint32_t iters_code(int n) { return n > 254 ? 254u : (uint32_t)n; }
 // relative ridge (Kron reduction); its first trial step is capped at kMaxStep.
 struct NewtonLane {
     float a[16];         // base-2 logits, rows shifted to max 0
+    float k[16];         // 2^a
+    bool kfast;          // every a_ij >= kMinLogit: the factored evaluation applies
     float g0, g1, g2;    // accepted potentials (g3 = 0)
     float d0, d1, d2;    // direction (base 2)
     float t, res, slope; // step length, residual, psi'(0) along d
@@ -242,11 +294,17 @@ MHC_DEV void newton_init(NewtonLane& s, const float* a_nat, const SolverOpts& o)
 #pragma unroll
         for (int j = 0; j < 4; ++j) s.a[4 * i + j] = (a_nat[4 * i + j] - m) * kLog2e;
     }
+    float amin = s.a[0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) amin = mhc_min(amin, s.a[j]);
+    s.kfast = amin >= kMinLogit;  // (a NaN entry fails the row-sum test instead)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s.k[j] = mhc_exp2(s.a[j]);
     s.g0 = s.g1 = s.g2 = 0.f;
     s.newton = 0;
     s.trials = 0;
     Eval E;
-    evaluate(s.a, 0.f, 0.f, 0.f, E);
+    evaluate(s.a, s.k, s.kfast, 0.f, 0.f, 0.f, E);
     newton_take(s, E);
     s.done = s.res <= o.tol;
     s.code = 0;
@@ -256,7 +314,7 @@ MHC_DEV void newton_init(NewtonLane& s, const float* a_nat, const SolverOpts& o)
         const float n1 = s.g1 + (l3 - mhc_log2(mhc_max(E.c[1], kMinMass)));
         const float n2 = s.g2 + (l3 - mhc_log2(mhc_max(E.c[2], kMinMass)));
         Eval F;
-        evaluate(s.a, n0, n1, n2, F);
+        evaluate(s.a, s.k, s.kfast, n0, n1, n2, F);
         if (!s.done) {
             s.g0 = n0;
             s.g1 = n1;
@@ -282,7 +340,7 @@ MHC_DEV void newton_step(NewtonLane& s, const SolverOpts& o)
 {
     const float t0 = s.g0 + s.t * s.d0, t1 = s.g1 + s.t * s.d1, t2 = s.g2 + s.t * s.d2;
     Eval E;
-    evaluate(s.a, t0, t1, t2, E);
+    evaluate(s.a, s.k, s.kfast, t0, t1, t2, E);
     float nd0, nd1, nd2, nslope, ncap;
     newton_direction(E, nd0, nd1, nd2, nslope, ncap);
 
@@ -339,7 +397,7 @@ MHC_DEV uint32_t project_newton(const float* a_nat, float* P_out, const SolverOp
     while (!s.done) newton_step(s, o);
     // P of the accepted point (the same arithmetic as when it was accepted)
     Eval E;
-    evaluate(s.a, s.g0, s.g1, s.g2, E);
+    evaluate(s.a, s.k, s.kfast, s.g0, s.g1, s.g2, E);
 #pragma unroll
     for (int k = 0; k < 16; ++k) P_out[k] = E.P[k];
     return s.code;
