@@ -9,8 +9,13 @@ reads from HBM rather than from the 256 MB last-level cache.
 
 Prints one JSON line:
   value        projections per second (fwd+bwd), whole job
-  roofline     for the dominant kernel (the forward solve): algorithmic bytes
-               per launch / its average HIP-event duration, against 8 TB/s
+  roofline     for the dominant kernel, the forward solve, which is bound by
+               vector-ALU issue: its VALU issue slots per launch (from the
+               counter run of this kernel on this workload) / its average
+               HIP-event duration, against the fp32 vector peak
+  hbm          algorithmic GB/s of fwd, bwd and the step against 8 TB/s, and
+               the counter-measured HBM bytes per launch
+  iters        Newton iterations per matrix and per wave (divergence)
   cpu_baseline the float64 oracle (fwd+bwd) on the host cores, on a bounded
                sample of the same batch
 
@@ -31,31 +36,48 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# Vector ALU issue peak of MI355X: the published fp32 vector rate, 157.3
+# TFLOP/s, is 157.3e12 / (64 lanes x 2 flops) = 1.229e12 wave64 FMA
+# instructions per second; every VALU instruction takes one such issue slot
+# and a transcendental (exp2, log2, rcp) four (quarter rate, measured).
+VALU_PEAK_SLOTS = 157.3e12 / 128.0
+TRANS_SLOTS = 4
 FWD_BYTES = 128   # per matrix: 64 B logits in, 64 B P out
 BWD_BYTES = 192   # per matrix: P and dL/dP in, dL/dA out
 
-# HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled
-# by a plain copy of known size; see profiles/), valid only for the kernel
-# sources they were taken on: (files hashed, sha256 prefix, bytes per launch).
-MEASURED_TRAFFIC = {
-    "birkhoff_fwd_131072": (("proj4.h", "birkhoff.hip", "devmath.h"), "82b261e5a4cee8f8", 16.84e6),
+# Per-launch figures from rocprofv3 counter runs (profiles/ holds the
+# summaries and the commands): HBM bytes from FETCH_SIZE and WRITE_SIZE, each
+# scaled by what the counter reads for a plain copy of known size, and VALU
+# instructions (SQ_INSTS_VALU, of which SQ_INSTS_VALU_TRANS_F32 are
+# transcendental).  They hold only for the kernel sources they were taken on:
+# every file under csrc/ is hashed, and a mismatch reports them as null.
+MEASURED_SHA = "29a314bed313c3f4"
+MEASURED = {
+    "birkhoff_fwd_131072_cfg2": {"fetch": 8518690, "write": 8391656, "valu": 4660875, "trans": 310826},
+    "birkhoff_bwd_131072_cfg2": {"fetch": 16807927, "write": 8388608, "valu": 1097728, "trans": 24576},
+    "birkhoff_fwd_1048576_cfg3": {"fetch": 67232773, "write": 67133270, "valu": 34852146, "trans": 2344256},
+    "birkhoff_bwd_1048576_cfg3": {"fetch": 134234025, "write": 67108864, "valu": 8781824, "trans": 196608},
+    "stream_mix_fwd_16384x4x4096": {"fetch": 538009366, "write": 537919599, "valu": 25959846, "trans": 87602},
+    "layer_step_65536x4x7168": {"fetch": 30868240718, "write": 9469111757},
 }
 
 
-def _sources_sha(files):
+def _sources_sha():
     import hashlib
     h = hashlib.sha256()
-    for f in files:
-        with open(os.path.join(ROOT, "birkhoff_projection_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    d = os.path.join(ROOT, "birkhoff_projection_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(key):
-    files, sha, nbytes = MEASURED_TRAFFIC.get(key, ((), None, None))
-    if not files or _sources_sha(files) != sha:
+def measured(key):
+    """Counter-derived per-launch figures for `key`, or None if the kernel
+    sources changed since they were taken."""
+    if MEASURED_SHA is None or _sources_sha() != MEASURED_SHA:
         return None
-    return nbytes
+    return MEASURED.get(key)
 
 
 def _cpu_worker(args):
@@ -86,10 +108,17 @@ def cpu_baseline_projection(A, G, n_sample, label):
 
 
 def time_projection(bp, torch, A_np, G_np, steps, warmup, solver="newton"):
-    """Rotate over buffer sets; time `steps` fwd+bwd steps back to back, then
-    `steps` forward launches alone and `steps` backward launches alone (HIP
-    events on the launch stream around each loop only, so a kernel's average
-    is its duration plus the dispatch gap, comparable with a kernel trace)."""
+    """Rotate over buffer sets and time `steps` fwd+bwd steps back to back,
+    then `steps` forward launches alone and `steps` backward launches alone.
+
+    Each timed sequence is captured once into a HIP graph and replayed: at
+    this size a kernel takes 7-15 us, about what one call through the Python
+    binding costs on the host, so eager launches would time the host.  Before
+    timing, the step graph is replayed twice with eager work in between and
+    every buffer set's P and dA are compared bit for bit with the same
+    projections run eagerly.  The eager rate is reported too.  HIP events on
+    the replay stream bracket each replay, so a kernel's average is its
+    duration plus the inter-kernel gap, comparable with a kernel trace."""
     B = A_np.shape[0]
     set_bytes = B * 64 * 4
     nsets = max(2, int(np.ceil(600e6 / set_bytes)))
@@ -98,7 +127,6 @@ def time_projection(bp, torch, A_np, G_np, steps, warmup, solver="newton"):
     sets = []
     for _ in range(nsets):
         sets.append((A0.clone(), torch.empty_like(A0), G0.clone(), torch.empty_like(A0)))
-    stream = torch.cuda.current_stream()
 
     def fwd(k):
         A, P, G, dA = sets[k % nsets]
@@ -108,24 +136,66 @@ def time_projection(bp, torch, A_np, G_np, steps, warmup, solver="newton"):
         A, P, G, dA = sets[k % nsets]
         bp.birkhoff_bwd(P, G, out=dA)
 
-    def timed(body):
-        start = torch.cuda.Event(enable_timing=True)
-        stop = torch.cuda.Event(enable_timing=True)
+    def step(k):
+        fwd(k)
+        bwd(k)
+
+    def events():
+        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def eager(body):
+        start, stop = events()
         torch.cuda.synchronize()
-        start.record(stream)
+        start.record()
         for k in range(steps):
             body(k)
-        stop.record(stream)
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop)
+
+    def capture(body):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for k in range(steps):
+                body(k)
+        torch.cuda.synchronize()
+        return g
+
+    def replay(g):
+        start, stop = events()
+        torch.cuda.synchronize()
+        start.record()
+        g.replay()
+        stop.record()
         torch.cuda.synchronize()
         return start.elapsed_time(stop)
 
     for k in range(warmup):
-        fwd(k)
-        bwd(k)
-    total_ms = timed(lambda k: (fwd(k), bwd(k)))
-    fwd_ms = timed(fwd) / steps
-    bwd_ms = timed(bwd) / steps
-    return dict(total_ms=total_ms, fwd_ms=fwd_ms, bwd_ms=bwd_ms, nsets=nsets)
+        step(k)
+    eager_ms = eager(step)
+    g_step, g_fwd, g_bwd = capture(step), capture(fwd), capture(bwd)
+    # replays must reproduce the eager results exactly (deterministic kernels)
+    ref = []
+    for A, P, G, dA in sets:
+        Pe = bp.birkhoff_fwd(A, solver=solver)
+        ref.append((Pe, bp.birkhoff_bwd(Pe, G)))
+    for _ in range(2):
+        for A, P, G, dA in sets:
+            P.zero_()
+            dA.zero_()
+        g_step.replay()
+        torch.cuda.synchronize()
+        for (A, P, G, dA), (Pe, dAe) in zip(sets, ref):
+            if not (torch.equal(P, Pe) and torch.equal(dA, dAe)):
+                raise RuntimeError("graph replay differs from eager results")
+        bp.birkhoff_fwd(sets[0][0], solver=solver)  # eager work between replays
+    for _ in range(2):  # warm replays
+        g_step.replay()
+    total_ms = replay(g_step)
+    fwd_ms = replay(g_fwd) / steps
+    bwd_ms = replay(g_bwd) / steps
+    return dict(total_ms=total_ms, fwd_ms=fwd_ms, bwd_ms=bwd_ms, nsets=nsets,
+                eager_ms_per_step=eager_ms / steps)
 
 
 def copy_probe(torch, mib):
@@ -137,6 +207,23 @@ def copy_probe(torch, mib):
     y.copy_(x)
     torch.cuda.synchronize()
     del x, y
+
+
+def iteration_stats(bp, torch, A_np):
+    """Newton iterations per matrix (the kernel's own count) and the mean over
+    waves of the largest count among a wave's 64 consecutive matrices: a wave
+    runs until its slowest lane is done, so their ratio is the share of
+    issued lane-work that is useful."""
+    A = torch.from_numpy(A_np).cuda()
+    _, it = bp.birkhoff_fwd(A, return_iters=True)
+    it = it.cpu().numpy().astype(np.int64)
+    ok = it != 255
+    itc = np.where(ok, it, 30)
+    n = (len(itc) // 64) * 64
+    wave_max = itc[:n].reshape(-1, 64).max(axis=1)
+    return {"mean": float(itc.mean()), "wave_max_mean": float(wave_max.mean()),
+            "useful_frac": float(itc[:n].mean() / wave_max.mean()) if wave_max.mean() > 0 else 1.0,
+            "not_converged": int((~ok).sum())}
 
 
 def bench_projection(args, bp, torch, config):
@@ -160,6 +247,24 @@ def bench_projection(args, bp, torch, config):
     fwd_gbs = FWD_BYTES * B / (fwd_avg / 1e3) / 1e9
     bwd_gbs = BWD_BYTES * B / (bwd_avg / 1e3) / 1e9
     step_gbs = (FWD_BYTES + BWD_BYTES) * B / (ms / 1e3) / 1e9
+    m_fwd = measured(f"birkhoff_fwd_{B}_cfg{config}")
+    m_bwd = measured(f"birkhoff_bwd_{B}_cfg{config}")
+    # the forward solve is bound by vector-ALU issue (transcendental-heavy
+    # Newton iterations), not by its 128 bytes per matrix
+    if m_fwd is not None:
+        slots = m_fwd["valu"] + (TRANS_SLOTS - 1) * m_fwd["trans"]
+        achieved = slots / (fwd_avg / 1e3)
+        roofline = {"bound": "alu", "kernel": "birkhoff_fwd (Newton)", "achieved": achieved,
+                    "peak": VALU_PEAK_SLOTS, "unit": "wave64 VALU issue slots/s",
+                    "frac": achieved / VALU_PEAK_SLOTS,
+                    "traffic": m_fwd["fetch"] + m_fwd["write"]}
+        valu = {"instructions_per_launch": m_fwd["valu"], "transcendental": m_fwd["trans"],
+                "issue_slots_per_launch": slots, "slots_per_matrix": slots / B}
+    else:
+        roofline = {"bound": "alu", "kernel": "birkhoff_fwd (Newton)", "achieved": None,
+                    "peak": VALU_PEAK_SLOTS, "unit": "wave64 VALU issue slots/s", "frac": None,
+                    "traffic": None, "note": "kernel changed since its counters were taken"}
+        valu = None
     out = {
         "metric": "4x4 projections/sec fwd+bwd at 128K batch; achieved HBM GB/s vs peak",
         "value": value, "unit": "projections/s", "n_gpus": 1, "steps": args.steps,
@@ -168,14 +273,15 @@ def bench_projection(args, bp, torch, config):
         "config": {"workload": f"birkhoff fwd+bwd, {B} 4x4 fp32 matrices {label}",
                    "batch": B, "solver": "newton", "tol": 1e-6,
                    "buffer_sets": r["nsets"]},
-        "roofline": {"bound": "hbm", "kernel": "birkhoff_fwd (Newton)",
-                     "achieved": fwd_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": fwd_gbs / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(f"birkhoff_fwd_{B}")},
-        "kernels": {"fwd_us": fwd_avg * 1e3, "bwd_us": bwd_avg * 1e3,
-                    "fwd_GBs": fwd_gbs, "bwd_GBs": bwd_gbs,
-                    "bwd_frac_hbm": bwd_gbs / HBM_PEAK_GBS,
-                    "step_GBs": step_gbs, "step_frac_hbm": step_gbs / HBM_PEAK_GBS},
+        "roofline": roofline,
+        "hbm": {"fwd_GBs": fwd_gbs, "bwd_GBs": bwd_gbs, "step_GBs": step_gbs,
+                "step_frac": step_gbs / HBM_PEAK_GBS, "bwd_frac": bwd_gbs / HBM_PEAK_GBS,
+                "fwd_traffic": m_fwd["fetch"] + m_fwd["write"] if m_fwd else None,
+                "bwd_traffic": m_bwd["fetch"] + m_bwd["write"] if m_bwd else None},
+        "kernels": {"fwd_us": fwd_avg * 1e3, "bwd_us": bwd_avg * 1e3, "launch": "hip graph replay",
+                    "eager_us_per_step": r["eager_ms_per_step"] * 1e3},
+        "valu": valu,
+        "iters": iteration_stats(bp, torch, A),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_projection(A, G, args.cpu_sample, label)
@@ -207,6 +313,7 @@ def bench_mix(args, bp, torch):
     ms = _time_loop(torch, lambda k: bp.ops.stream_mix_into(x, logits, H, y), args.steps, args.warmup)
     per_tok = 64 + 4 * C * 2 + 64 + 4 * C * 2
     gbs = per_tok * T / (ms / 1e3) / 1e9
+    m = measured(f"stream_mix_fwd_{T}x4x{C}")
     return {
         "metric": "fused projection + stream mix tokens/s; achieved HBM GB/s vs peak",
         "value": T / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -215,7 +322,7 @@ def bench_mix(args, bp, torch):
         "config": {"workload": f"fused projection + stream mix, T={T}, n=4, C={C} bf16"},
         "roofline": {"bound": "hbm", "kernel": "stream_mix_fwd (fused Newton)", "achieved": gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                     "traffic": None},
+                     "traffic": m["fetch"] + m["write"] if m else None},
     }
 
 
@@ -235,19 +342,21 @@ def bench_layer(args, bp, torch):
     ms = fwd_ms + bwd_ms
     D = 4 * C
     fwd_bytes = T * (2 * D + 2 * C + 2 * C + 2 * D + 196)      # maps: x; mix: x, f, u, x_out
-    bwd_bytes = T * (2 * D + 2 * D + 2 * C + 2 * C + 2 * C     # dots: x, dxo, f, du, df
-                     + 2 * D + 2 * D + 2 * C + 2 * D          # dx: dxo, x, du, dx
+    bwd_bytes = T * (2 * D + 2 * D + 2 * C + 2 * C             # dots: x, dxo, f, du
+                     + 2 * D + 2 * D + 2 * C + 2 * D + 2 * C  # dx: dxo, x, du; dx, df
                      + 2 * D)                                  # dw: x
     gbs = (fwd_bytes + bwd_bytes) / (ms / 1e3) / 1e9
+    m = measured(f"layer_step_{T}x4x{C}")
     return {
         "metric": "mHC layer step fwd+bwd tokens/s; achieved HBM GB/s vs peak",
         "value": T / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"mHC layer step fwd+bwd, T={T}, n=4, C={C} bf16, W [24, {D}]"},
-        "roofline": {"bound": "hbm", "kernel": "whole step (6 kernels)", "achieved": gbs,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                     "traffic": None},
+        "roofline": {"bound": "hbm", "kernel": "whole step (2 forward + 5 backward kernels)",
+                     "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": m["fetch"] + m["write"] if m else None},
         "kernels": {"fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
                     "fwd_GBs": fwd_bytes / (fwd_ms / 1e3) / 1e9,
                     "bwd_GBs": bwd_bytes / (bwd_ms / 1e3) / 1e9},
@@ -260,7 +369,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--cpu-sample", type=int, default=524288,
+    ap.add_argument("--cpu-sample", type=int, default=2097152,
                     help="matrices the oracle baseline processes (about 10-30 s of CPU work)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain copy of this size first (counter calibration)")

@@ -53,25 +53,77 @@ __global__ __launch_bounds__(kBlock) void birkhoff_fwd_kernel(const float* logit
     if (iters != nullptr) iters[b] = (uint8_t)it;
 }
 
-// Backward: one row per lane (quad = one matrix, 64 matrices per 256-lane
-// workgroup), so loads and stores are contiguous 16-byte rows across lanes
-// and a launch has four times the waves of the forward.  Quads past B load
-// zeros (all-zero rows give a zero gradient) and skip the store, keeping every
-// quad fully active for the DPP reductions.
+// Backward: one row per lane (quad = one matrix), so loads and stores are
+// contiguous 16-byte rows across lanes.  A single generation of waves would
+// load everything, compute, then store everything, leaving reads and writes
+// in separate phases; instead a grid of kBwdWgPerCu workgroups per CU strides
+// over the rows, and the rows of the next stride are loaded (into the other
+// of two register sets) before the current ones are reduced and stored, so
+// one stride's stores overlap the next one's loads.  Quads past B load a
+// clamped row, compute on zeros and skip the store, which keeps every quad
+// whole for the DPP reductions (the stride is a multiple of 4).
+constexpr int kBwdWgPerCu = 2;
+constexpr int kCus = 256;
+
+struct BwdRows {
+    float4 p, g;
+};
+
+MHC_DEV void bwd_issue(const float4* P, const float4* G, int64_t r, int64_t rows, BwdRows& d)
+{
+    const int64_t rc = r < rows ? r : rows - 1;
+    d.p = P[rc];
+    d.g = G[rc];
+}
+
+MHC_DEV void bwd_consume(const BwdRows& d, float4* dA, int64_t r)
+{
+    const float p[4] = {d.p.x, d.p.y, d.p.z, d.p.w};
+    const float g[4] = {d.g.x, d.g.y, d.g.z, d.g.w};
+    float o[4];
+    project_bwd_row(p, g, o);
+    dA[r] = make_float4(o[0], o[1], o[2], o[3]);
+}
+
+MHC_DEV void bwd_consume_tail(const BwdRows& d, float4* dA, int64_t r, int64_t rows)
+{
+    const bool ok = r < rows;
+    const float p[4] = {ok ? d.p.x : 0.f, ok ? d.p.y : 0.f, ok ? d.p.z : 0.f, ok ? d.p.w : 0.f};
+    const float g[4] = {ok ? d.g.x : 0.f, ok ? d.g.y : 0.f, ok ? d.g.z : 0.f, ok ? d.g.w : 0.f};
+    float o[4];
+    project_bwd_row(p, g, o);
+    if (ok) dA[r] = make_float4(o[0], o[1], o[2], o[3]);
+}
+
 __global__ __launch_bounds__(kBlock) void birkhoff_bwd_kernel(const float4* __restrict__ P,
                                                               const float4* G, float4* dA,
                                                               int64_t B)
 {
-    const int64_t r = (int64_t)blockIdx.x * kBlock + threadIdx.x;  // row 4 b + i
-    const bool ok = (r >> 2) < B;
-    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
-    const float4 p4 = ok ? P[r] : zero;
-    const float4 g4 = ok ? G[r] : zero;
-    const float p[4] = {p4.x, p4.y, p4.z, p4.w};
-    const float g[4] = {g4.x, g4.y, g4.z, g4.w};
-    float d[4];
-    project_bwd_row(p, g, d);
-    if (ok) dA[r] = make_float4(d[0], d[1], d[2], d[3]);
+    const int64_t rows = 4 * B;
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    int64_t r = (int64_t)blockIdx.x * kBlock + threadIdx.x;  // row 4 b + i
+    // Pairs of strides that lie wholly inside the batch store without a
+    // check (a conditional store would make the compiler's wait for the next
+    // loads also wait for that store); the last, partial pair is checked.
+    const int64_t full = rows / (2 * stride);
+    BwdRows d0, d1;
+    bwd_issue(P, G, r, rows, d0);
+    for (int64_t k = 0; k < full; ++k) {
+        bwd_issue(P, G, r + stride, rows, d1);
+        __builtin_amdgcn_sched_barrier(0);
+        bwd_consume(d0, dA, r);
+        __builtin_amdgcn_sched_barrier(0);
+        bwd_issue(P, G, r + 2 * stride, rows, d0);
+        __builtin_amdgcn_sched_barrier(0);
+        bwd_consume(d1, dA, r + stride);
+        __builtin_amdgcn_sched_barrier(0);
+        r += 2 * stride;
+    }
+    if (full * 2 * stride < rows) {
+        bwd_issue(P, G, r + stride, rows, d1);
+        bwd_consume_tail(d0, dA, r, rows);
+        bwd_consume_tail(d1, dA, r + stride, rows);
+    }
 }
 
 }  // namespace
@@ -92,7 +144,9 @@ hipError_t launch_birkhoff_fwd(const float* logits, float* P, uint8_t* iters, in
 hipError_t launch_birkhoff_bwd(const float* P, const float* G, float* dA, int64_t B,
                                hipStream_t stream)
 {
-    const dim3 grid((unsigned)((4 * B + kBlock - 1) / kBlock));
+    const int64_t need = (4 * B + kBlock - 1) / kBlock;
+    const int64_t cap = (int64_t)kCus * kBwdWgPerCu;
+    const dim3 grid((unsigned)(need < cap ? need : cap));
     hipLaunchKernelGGL(birkhoff_bwd_kernel, grid, dim3(kBlock), 0, stream,
                        reinterpret_cast<const float4*>(P), reinterpret_cast<const float4*>(G),
                        reinterpret_cast<float4*>(dA), B);
