@@ -122,13 +122,10 @@ constexpr float kRowLo = 8.6736174e-19f;  // 2^-60
 constexpr float kRowHi = 3.4028235e38f;   // largest finite float
 constexpr float kMinLogit = -126.f;
 
-MHC_DEV void evaluate(const float* a, const float* k, bool kfast, float g0, float g1, float g2,
-                      Eval& E)
+// Factored form only; returns false (E then unusable) when a row sum is out
+// of range.
+MHC_DEV bool evaluate_factored(const float* k, float g0, float g1, float g2, Eval& E)
 {
-    if (!kfast) {
-        evaluate_shifted(a, g0, g1, g2, E);
-        return;
-    }
     const float u0 = mhc_exp2(g0), u1 = mhc_exp2(g1), u2 = mhc_exp2(g2);
     E.c[0] = E.c[1] = E.c[2] = E.c[3] = 0.f;
     bool ok = true;
@@ -150,12 +147,16 @@ MHC_DEV void evaluate(const float* a, const float* k, bool kfast, float g0, floa
         E.c[2] += E.P[4 * i + 2];
         E.c[3] += E.P[4 * i + 3];
     }
-    if (!ok) {
-        evaluate_shifted(a, g0, g1, g2, E);
-        return;
-    }
     E.res = mhc_max(mhc_max(mhc_abs(E.c[0] - 1.f), mhc_abs(E.c[1] - 1.f)),
                     mhc_max(mhc_abs(E.c[2] - 1.f), mhc_abs(E.c[3] - 1.f)));
+    return ok;
+}
+
+// Factored form where it applies, max-shifted form otherwise.
+MHC_DEV void evaluate(const float* a, const float* k, bool kfast, float g0, float g1, float g2,
+                      Eval& E)
+{
+    if (!(kfast && evaluate_factored(k, g0, g1, g2, E))) evaluate_shifted(a, g0, g1, g2, E);
 }
 
 // Solve L d = b for the Laplacian L of the complete graph on {0,1,2,3} with
@@ -256,6 +257,7 @@ struct NewtonLane {
     float a[16];         // base-2 logits, rows shifted to max 0
     float k[16];         // 2^a
     bool kfast;          // every a_ij >= kMinLogit: the factored evaluation applies
+    bool slow;           // the lane has left the factored evaluation for good
     float g0, g1, g2;    // accepted potentials (g3 = 0)
     float d0, d1, d2;    // direction (base 2)
     float t, res, slope; // step length, residual, psi'(0) along d
@@ -298,6 +300,7 @@ MHC_DEV void newton_init(NewtonLane& s, const float* a_nat, const SolverOpts& o)
 #pragma unroll
     for (int j = 1; j < 16; ++j) amin = mhc_min(amin, s.a[j]);
     s.kfast = amin >= kMinLogit;  // (a NaN entry fails the row-sum test instead)
+    s.slow = !s.kfast;
 #pragma unroll
     for (int j = 0; j < 16; ++j) s.k[j] = mhc_exp2(s.a[j]);
     s.g0 = s.g1 = s.g2 = 0.f;
@@ -335,54 +338,58 @@ MHC_DEV void newton_init(NewtonLane& s, const float* a_nat, const SolverOpts& o)
     s.newton = 1;
 }
 
-// One trial of a lane that is not done (the caller guarantees !s.done).
+// One trial of a lane that is not done (the caller guarantees !s.done and,
+// for FACTORED, !s.slow).  Written without branches so that the whole trial
+// is one basic block the compiler can schedule across.  With FACTORED a trial
+// whose factored evaluation is out of range changes nothing but s.slow; the
+// lane then repeats it, and continues, with the max-shifted form.
+template <bool FACTORED>
 MHC_DEV void newton_step(NewtonLane& s, const SolverOpts& o)
 {
     const float t0 = s.g0 + s.t * s.d0, t1 = s.g1 + s.t * s.d1, t2 = s.g2 + s.t * s.d2;
     Eval E;
-    evaluate(s.a, s.k, s.kfast, t0, t1, t2, E);
+    bool ok = true;
+    if (FACTORED)
+        ok = evaluate_factored(s.k, t0, t1, t2, E);
+    else
+        evaluate_shifted(s.a, t0, t1, t2, E);
     float nd0, nd1, nd2, nslope, ncap;
     newton_direction(E, nd0, nd1, nd2, nslope, ncap);
 
     const float dphi = (E.c[0] - 1.f) * s.d0 + (E.c[1] - 1.f) * s.d1 + (E.c[2] - 1.f) * s.d2;
+    // (bitwise & and | on bools: no short-circuit branches)
     const bool near_floor = s.res <= kNoiseFloor;
-    const bool accept = E.res <= o.tol ||
-                        (near_floor ? E.res < s.res : dphi <= kCurvature * mhc_abs(s.slope));
-    const bool floor = !accept && near_floor;
+    const bool lower = E.res < s.res;
+    const bool curved = dphi <= kCurvature * mhc_abs(s.slope);
+    const bool conv_t = E.res <= o.tol;
+    const bool pass = conv_t | (near_floor & lower) | (!near_floor & curved);
+    const bool accept = ok & pass;
+    const bool reject = ok & !pass;
+    // a full first trial that stayed far from the line minimum doubles the
+    // next first trial; any other accepted trial resets it to the Newton step
+    const bool far = (s.trials == 0) & (s.t >= s.grow) & (dphi <= kFar * s.slope) &
+                     (E.res > kGrowMinRes);
+    const float grow = far ? mhc_min(2.f * s.grow, kMaxGrow) : 1.f;
+    const bool conv = accept & conv_t;
+    const bool maxed = accept & !conv & (s.newton >= o.max_iters);
+    const int trials = s.trials + 1;
+    const bool stuck = reject & (near_floor | (trials > 30));
 
-    if (accept) {
-        // a full first trial that stayed far from the line minimum doubles the
-        // next first trial; anything else resets it to the Newton step
-        const bool far = s.trials == 0 && s.t >= s.grow && dphi <= kFar * s.slope &&
-                         E.res > kGrowMinRes;
-        s.grow = far ? mhc_min(2.f * s.grow, kMaxGrow) : 1.f;
-        s.g0 = t0;
-        s.g1 = t1;
-        s.g2 = t2;
-        newton_take(s, E);
-        s.d0 = nd0;
-        s.d1 = nd1;
-        s.d2 = nd2;
-        s.slope = nslope;
-        s.t = mhc_min(s.grow, ncap);
-        s.trials = 0;
-        if (s.res <= o.tol) {
-            s.done = true;
-            s.code = iters_code(s.newton);
-        } else if (s.newton >= o.max_iters) {
-            s.done = true;
-            s.code = kNotConverged;
-        } else {
-            ++s.newton;
-        }
-    } else {
-        s.t *= 0.5f;
-        ++s.trials;
-        if (floor || s.trials > 30) {
-            s.done = true;
-            s.code = kNotConverged;
-        }
-    }
+    s.g0 = accept ? t0 : s.g0;
+    s.g1 = accept ? t1 : s.g1;
+    s.g2 = accept ? t2 : s.g2;
+    s.res = accept ? E.res : s.res;
+    s.d0 = accept ? nd0 : s.d0;
+    s.d1 = accept ? nd1 : s.d1;
+    s.d2 = accept ? nd2 : s.d2;
+    s.slope = accept ? nslope : s.slope;
+    s.grow = accept ? grow : s.grow;
+    s.t = accept ? mhc_min(grow, ncap) : (reject ? 0.5f * s.t : s.t);
+    s.trials = accept ? 0 : (reject ? trials : s.trials);
+    s.newton += (accept & !conv & !maxed) ? 1 : 0;
+    s.code = conv ? iters_code(s.newton) : ((maxed | stuck) ? kNotConverged : s.code);
+    s.done = s.done | conv | maxed | stuck;
+    s.slow = s.slow | !ok;
 }
 
 // Forward projection of one matrix by Newton's method on the semi-dual.
@@ -394,7 +401,8 @@ MHC_DEV uint32_t project_newton(const float* a_nat, float* P_out, const SolverOp
 {
     NewtonLane s;
     newton_init(s, a_nat, o);
-    while (!s.done) newton_step(s, o);
+    while (!s.done && !s.slow) newton_step<true>(s, o);
+    while (!s.done) newton_step<false>(s, o);
     // P of the accepted point (the same arithmetic as when it was accepted)
     Eval E;
     evaluate(s.a, s.k, s.kfast, s.g0, s.g1, s.g2, E);
