@@ -51,14 +51,14 @@ BWD_BYTES = 192   # per matrix: P and dL/dP in, dL/dA out
 # instructions (SQ_INSTS_VALU, of which SQ_INSTS_VALU_TRANS_F32 are
 # transcendental).  They hold only for the kernel sources they were taken on:
 # every file under csrc/ is hashed, and a mismatch reports them as null.
-MEASURED_SHA = "29a314bed313c3f4"
+MEASURED_SHA = "9386592a405d01d5"
 MEASURED = {
-    "birkhoff_fwd_131072_cfg2": {"fetch": 8518690, "write": 8391656, "valu": 4660875, "trans": 310826},
-    "birkhoff_bwd_131072_cfg2": {"fetch": 16807927, "write": 8388608, "valu": 1097728, "trans": 24576},
-    "birkhoff_fwd_1048576_cfg3": {"fetch": 67232773, "write": 67133270, "valu": 34852146, "trans": 2344256},
-    "birkhoff_bwd_1048576_cfg3": {"fetch": 134234025, "write": 67108864, "valu": 8781824, "trans": 196608},
-    "stream_mix_fwd_16384x4x4096": {"fetch": 538009366, "write": 537919599, "valu": 25959846, "trans": 87602},
-    "layer_step_65536x4x7168": {"fetch": 30868240718, "write": 9469111757},
+    "birkhoff_fwd_131072_cfg2": {"fetch": 8499427, "write": 8389412, "valu": 4716769, "trans": 310834},
+    "birkhoff_bwd_131072_cfg2": {"fetch": 16848680, "write": 8388608, "valu": 976896, "trans": 26624},
+    "birkhoff_fwd_1048576_cfg3": {"fetch": 67216021, "write": 67115951, "valu": 35271807, "trans": 2344295},
+    "birkhoff_bwd_1048576_cfg3": {"fetch": 134274854, "write": 67108864, "valu": 7485440, "trans": 198656},
+    "stream_mix_fwd_16384x4x4096": {"fetch": 537966544, "write": 537919852, "valu": 25980242, "trans": 87602},
+    "layer_step_65536x4x7168": {"fetch": 30875978908, "write": 9469113107},
 }
 
 
@@ -174,18 +174,20 @@ def time_projection(bp, torch, A_np, G_np, steps, warmup, solver="newton"):
         step(k)
     eager_ms = eager(step)
     g_step, g_fwd, g_bwd = capture(step), capture(fwd), capture(bwd)
-    # replays must reproduce the eager results exactly (deterministic kernels)
+    # replays must reproduce the eager results exactly (deterministic kernels);
+    # the captured steps write the first min(steps, nsets) buffer sets
+    touched = sets[:min(steps, nsets)]
     ref = []
-    for A, P, G, dA in sets:
+    for A, P, G, dA in touched:
         Pe = bp.birkhoff_fwd(A, solver=solver)
         ref.append((Pe, bp.birkhoff_bwd(Pe, G)))
     for _ in range(2):
-        for A, P, G, dA in sets:
+        for A, P, G, dA in touched:
             P.zero_()
             dA.zero_()
         g_step.replay()
         torch.cuda.synchronize()
-        for (A, P, G, dA), (Pe, dAe) in zip(sets, ref):
+        for (A, P, G, dA), (Pe, dAe) in zip(touched, ref):
             if not (torch.equal(P, Pe) and torch.equal(dA, dAe)):
                 raise RuntimeError("graph replay differs from eager results")
         bp.birkhoff_fwd(sets[0][0], solver=solver)  # eager work between replays
