@@ -343,11 +343,16 @@ def bench_layer(args, bp, torch):
                         args.steps, args.warmup)
     ms = fwd_ms + bwd_ms
     D = 4 * C
-    fwd_bytes = T * (2 * D + 2 * C + 2 * C + 2 * D + 196)      # maps: x; mix: x, f, u, x_out
+    fwd_bytes = T * (2 * D + 196                               # maps: x; logits, maps out
+                     + 2 * D + 2 * C + 2 * C + 2 * D)          # mix: x, f; u, x_out
     bwd_bytes = T * (2 * D + 2 * D + 2 * C + 2 * C             # dots: x, dxo, f, du
                      + 2 * D + 2 * D + 2 * C + 2 * D + 2 * C  # dx: dxo, x, du; dx, df
                      + 2 * D)                                  # dw: x
     gbs = (fwd_bytes + bwd_bytes) / (ms / 1e3) / 1e9
+    # what any implementation must move: x, f read and u, x_out written once
+    # forward; x, grad_x_out, f, grad_u read and grad_x, grad_f written once
+    # backward (this one reads x three times and grad_x_out, grad_u twice)
+    min_bytes = T * ((2 * D + 2 * C + 2 * C + 2 * D) + (2 * D + 2 * D + 2 * C + 2 * C + 2 * D + 2 * C))
     m = measured(f"layer_step_{T}x4x{C}")
     return {
         "metric": "mHC layer step fwd+bwd tokens/s; achieved HBM GB/s vs peak",
@@ -361,7 +366,10 @@ def bench_layer(args, bp, torch):
                      "traffic": m["fetch"] + m["write"] if m else None},
         "kernels": {"fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
                     "fwd_GBs": fwd_bytes / (fwd_ms / 1e3) / 1e9,
-                    "bwd_GBs": bwd_bytes / (bwd_ms / 1e3) / 1e9},
+                    "bwd_GBs": bwd_bytes / (bwd_ms / 1e3) / 1e9,
+                    "algorithmic_bytes": fwd_bytes + bwd_bytes,
+                    "one_pass_bytes": min_bytes,
+                    "one_pass_frac": min_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS},
     }
 
 
