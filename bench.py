@@ -107,7 +107,7 @@ def cpu_baseline_projection(A, G, n_sample, label):
                       f"{label} batch), fwd+bwd, float64, {dt:.1f} s wall on {cores} processes"}
 
 
-def time_projection(bp, torch, A_np, G_np, steps, warmup, solver="newton"):
+def time_projection(bp, torch, A_np, G_np, steps, warmup, solver="newton", recompute=False):
     """Rotate over buffer sets and time `steps` fwd+bwd steps back to back,
     then `steps` forward launches alone and `steps` backward launches alone.
 
@@ -134,7 +134,10 @@ def time_projection(bp, torch, A_np, G_np, steps, warmup, solver="newton"):
 
     def bwd(k):
         A, P, G, dA = sets[k % nsets]
-        bp.birkhoff_bwd(P, G, out=dA)
+        if recompute:
+            bp.birkhoff_bwd_recompute(A, G, out=dA, solver=solver)
+        else:
+            bp.birkhoff_bwd(P, G, out=dA)
 
     def step(k):
         fwd(k)
@@ -180,7 +183,8 @@ def time_projection(bp, torch, A_np, G_np, steps, warmup, solver="newton"):
     ref = []
     for A, P, G, dA in touched:
         Pe = bp.birkhoff_fwd(A, solver=solver)
-        ref.append((Pe, bp.birkhoff_bwd(Pe, G)))
+        dAe = bp.birkhoff_bwd_recompute(A, G, solver=solver) if recompute else bp.birkhoff_bwd(Pe, G)
+        ref.append((Pe, dAe))
     for _ in range(2):
         for A, P, G, dA in touched:
             P.zero_()
@@ -241,16 +245,17 @@ def bench_projection(args, bp, torch, config):
         G = W.grad_batch(A.shape[0], 1)
         label = "N(0,1)"
     B = A.shape[0]
-    r = time_projection(bp, torch, A, G, args.steps, args.warmup)
+    r = time_projection(bp, torch, A, G, args.steps, args.warmup, recompute=args.recompute)
     ms = r["total_ms"] / args.steps
     fwd_avg = float(r["fwd_ms"])
     bwd_avg = float(r["bwd_ms"])
     value = B / (ms / 1e3)
+    bwd_bytes = BWD_BYTES  # recompute: logits and dL/dP in, dL/dA out -- also 192
     fwd_gbs = FWD_BYTES * B / (fwd_avg / 1e3) / 1e9
-    bwd_gbs = BWD_BYTES * B / (bwd_avg / 1e3) / 1e9
-    step_gbs = (FWD_BYTES + BWD_BYTES) * B / (ms / 1e3) / 1e9
+    bwd_gbs = bwd_bytes * B / (bwd_avg / 1e3) / 1e9
+    step_gbs = (FWD_BYTES + bwd_bytes) * B / (ms / 1e3) / 1e9
     m_fwd = measured(f"birkhoff_fwd_{B}_cfg{config}")
-    m_bwd = measured(f"birkhoff_bwd_{B}_cfg{config}")
+    m_bwd = None if args.recompute else measured(f"birkhoff_bwd_{B}_cfg{config}")
     # the forward solve is bound by vector-ALU issue (transcendental-heavy
     # Newton iterations), not by its 128 bytes per matrix
     if m_fwd is not None:
@@ -274,6 +279,7 @@ def bench_projection(args, bp, torch, config):
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"birkhoff fwd+bwd, {B} 4x4 fp32 matrices {label}",
                    "batch": B, "solver": "newton", "tol": 1e-6,
+                   "backward": "recompute" if args.recompute else "from P",
                    "buffer_sets": r["nsets"]},
         "roofline": roofline,
         "hbm": {"fwd_GBs": fwd_gbs, "bwd_GBs": bwd_gbs, "step_GBs": step_gbs,
@@ -384,6 +390,9 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain copy of this size first (counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--recompute", action="store_true",
+                    help="configs 1-3: backward by mhc_birkhoff_bwd_recompute (logits and "
+                         "dL/dP in, the projection solved again; P not kept)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: every batch element is independent, so the "

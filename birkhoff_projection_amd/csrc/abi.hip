@@ -115,6 +115,29 @@ mhc_status mhc_birkhoff_bwd(const float* P, const float* grad_P, float* grad_log
                     "birkhoff_bwd launch");
 }
 
+mhc_status mhc_birkhoff_bwd_recompute(const float* logits, const float* grad_P,
+                                      float* grad_logits, int64_t B,
+                                      const mhc_proj_opts* opts, void* stream)
+{
+    if (B < 0 || B > kMaxBatch) return fail(MHC_ERR_INVALID_ARGUMENT, "B=%lld out of range", (long long)B);
+    mhc::SolverOpts o;
+    const mhc_status s = check_opts(opts, &o);
+    if (s != MHC_OK) return s;
+    if (B == 0) return ok();
+    if (logits == nullptr || grad_P == nullptr || grad_logits == nullptr)
+        return fail(MHC_ERR_INVALID_ARGUMENT, "logits, grad_P and grad_logits must not be NULL");
+    if (!aligned16(logits) || !aligned16(grad_P) || !aligned16(grad_logits))
+        return fail(MHC_ERR_INVALID_ARGUMENT, "logits, grad_P and grad_logits must be 16-byte aligned");
+    const size_t bytes = (size_t)B * 64;
+    if (grad_logits != logits && overlap(logits, bytes, grad_logits, bytes))
+        return fail(MHC_ERR_INVALID_ARGUMENT, "grad_logits partially overlaps logits");
+    if (grad_logits != grad_P && overlap(grad_P, bytes, grad_logits, bytes))
+        return fail(MHC_ERR_INVALID_ARGUMENT, "grad_logits partially overlaps grad_P");
+    return launched(mhc::launch_birkhoff_bwd_recompute(logits, grad_P, grad_logits, B, o,
+                                                      (hipStream_t)stream),
+                    "birkhoff_bwd_recompute launch");
+}
+
 mhc_status mhc_stream_mix(const void* x, const float* H_or_logits, float* H_out, void* out,
                           int64_t T, int32_t n, int64_t C, const mhc_proj_opts* proj,
                           void* stream)

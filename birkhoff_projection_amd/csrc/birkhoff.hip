@@ -126,6 +126,29 @@ __global__ __launch_bounds__(kBlock) void birkhoff_bwd_kernel(const float4* __re
     }
 }
 
+// Recompute backward: lane per matrix, the forward solve redone in
+// registers and the implicit-differentiation gradient formed from that P
+// (matrix-per-lane form of the backward).  logits or G may be the same buffer
+// as dA: a lane reads its whole matrix from both before writing.
+template <int SOLVER>
+__global__ __launch_bounds__(kBlock) void birkhoff_bwd_recompute_kernel(const float* logits,
+                                                                        const float* G,
+                                                                        float* dA, int64_t B,
+                                                                        SolverOpts o)
+{
+    const int64_t b = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (b >= B) return;
+    float a[16], g[16], p[16], d[16];
+    load16(logits + 16 * b, a);
+    load16(G + 16 * b, g);
+    if (SOLVER == 0)
+        project_newton(a, p, o);
+    else
+        project_sinkhorn(a, p, o);
+    project_bwd(p, g, d);
+    store16(dA + 16 * b, d);
+}
+
 }  // namespace
 
 hipError_t launch_birkhoff_fwd(const float* logits, float* P, uint8_t* iters, int64_t B,
@@ -150,6 +173,19 @@ hipError_t launch_birkhoff_bwd(const float* P, const float* G, float* dA, int64_
     hipLaunchKernelGGL(birkhoff_bwd_kernel, grid, dim3(kBlock), 0, stream,
                        reinterpret_cast<const float4*>(P), reinterpret_cast<const float4*>(G),
                        reinterpret_cast<float4*>(dA), B);
+    return hipGetLastError();
+}
+
+hipError_t launch_birkhoff_bwd_recompute(const float* logits, const float* G, float* dA, int64_t B,
+                                         const SolverOpts& o, hipStream_t stream)
+{
+    const dim3 grid((unsigned)((B + kBlock - 1) / kBlock));
+    if (o.solver == 0)
+        hipLaunchKernelGGL(birkhoff_bwd_recompute_kernel<0>, grid, dim3(kBlock), 0, stream,
+                           logits, G, dA, B, o);
+    else
+        hipLaunchKernelGGL(birkhoff_bwd_recompute_kernel<1>, grid, dim3(kBlock), 0, stream,
+                           logits, G, dA, B, o);
     return hipGetLastError();
 }
 

@@ -13,6 +13,8 @@ hipError_t launch_birkhoff_fwd(const float* logits, float* P, uint8_t* iters, in
                                const SolverOpts& o, hipStream_t stream);
 hipError_t launch_birkhoff_bwd(const float* P, const float* G, float* dA, int64_t B,
                                hipStream_t stream);
+hipError_t launch_birkhoff_bwd_recompute(const float* logits, const float* G, float* dA, int64_t B,
+                                         const SolverOpts& o, hipStream_t stream);
 hipError_t launch_stream_mix_fwd(const void* x, const float* Hl, float* H_out, void* out,
                                  int64_t T, int64_t C, const SolverOpts* proj,
                                  hipStream_t stream);

@@ -85,27 +85,59 @@ def birkhoff_bwd(P: torch.Tensor, grad_P: torch.Tensor, out=None):
     return dA
 
 
+def birkhoff_bwd_recompute(logits: torch.Tensor, grad_P: torch.Tensor, *, solver="newton",
+                           max_iters=None, tol=None, warm_sweeps=None, out=None):
+    """dL/dlogits from the logits and dL/dP: the projection is solved again in
+    registers (same solver and options as the forward) and differentiated
+    there, so P need not be kept between forward and backward."""
+    _need(logits, "logits", torch.float32, (4, 4))
+    _need(grad_P, "grad_P", torch.float32, (4, 4))
+    if logits.shape != grad_P.shape or logits.device != grad_P.device:
+        raise ValueError("logits and grad_P must match in shape and device")
+    dA = torch.empty_like(logits) if out is None else out
+    if out is not None:
+        _need(out, "out", torch.float32, (4, 4))
+    o = make_opts(solver, max_iters, tol, warm_sweeps)
+    with torch.cuda.device(logits.device):
+        check(lib().mhc_birkhoff_bwd_recompute(_ptr(logits), _ptr(grad_P), _ptr(dA),
+                                               logits.numel() // 16, ctypes.byref(o),
+                                               _stream(logits.device)))
+    return dA
+
+
 class BirkhoffProjection(torch.autograd.Function):
-    """Autograd wrapper: saves only P for the backward (nothing else from the
-    forward solve is needed)."""
+    """Autograd wrapper.  By default it saves only P for the backward (nothing
+    else from the forward solve is needed); with ``recompute`` it saves the
+    logits instead and the backward solves the projection again."""
 
     @staticmethod
-    def forward(ctx, logits, solver="newton", max_iters=None, tol=None, warm_sweeps=None):
-        P = birkhoff_fwd(logits.contiguous(), solver=solver, max_iters=max_iters, tol=tol,
+    def forward(ctx, logits, solver="newton", max_iters=None, tol=None, warm_sweeps=None,
+                recompute=False):
+        logits = logits.contiguous()
+        P = birkhoff_fwd(logits, solver=solver, max_iters=max_iters, tol=tol,
                          warm_sweeps=warm_sweeps)
-        ctx.save_for_backward(P)
+        ctx.recompute = recompute
+        ctx.opts = (solver, max_iters, tol, warm_sweeps)
+        ctx.save_for_backward(logits if recompute else P)
         return P
 
     @staticmethod
     def backward(ctx, grad_P):
-        (P,) = ctx.saved_tensors
-        return birkhoff_bwd(P, grad_P.contiguous()), None, None, None, None
+        (saved,) = ctx.saved_tensors
+        if ctx.recompute:
+            solver, max_iters, tol, warm_sweeps = ctx.opts
+            dA = birkhoff_bwd_recompute(saved, grad_P.contiguous(), solver=solver,
+                                        max_iters=max_iters, tol=tol, warm_sweeps=warm_sweeps)
+        else:
+            dA = birkhoff_bwd(saved, grad_P.contiguous())
+        return dA, None, None, None, None, None
 
 
 def birkhoff_project(logits, **kw):
     """Differentiable projection (see BirkhoffProjection)."""
     return BirkhoffProjection.apply(logits, kw.get("solver", "newton"), kw.get("max_iters"),
-                                    kw.get("tol"), kw.get("warm_sweeps"))
+                                    kw.get("tol"), kw.get("warm_sweeps"),
+                                    bool(kw.get("recompute", False)))
 
 
 def stream_mix(x: torch.Tensor, H: torch.Tensor = None, *, logits: torch.Tensor = None,

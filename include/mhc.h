@@ -7,6 +7,9 @@
  *
  *   mhc_birkhoff_fwd    the projection of a batch of logit matrices
  *   mhc_birkhoff_bwd    its gradient by implicit differentiation
+ *   mhc_birkhoff_bwd_recompute
+ *                       the same gradient from the logits alone (the forward
+ *                       solve is redone in registers; P is not stored)
  *   mhc_stream_mix      out[t,i,:] = sum_j H[t,i,j] x[t,j,:], optionally with
  *                       the projection of H's logits fused in
  *   mhc_stream_mix_bwd  gradients of the stream mix
@@ -130,6 +133,31 @@ mhc_status mhc_birkhoff_fwd(const float* logits, float* P, int64_t B,
  */
 mhc_status mhc_birkhoff_bwd(const float* P, const float* grad_P, float* grad_logits,
                             int64_t B, void* stream);
+
+/* mhc_birkhoff_bwd_recompute -- dL/dA from the logits and dL/dP, without P.
+ *
+ * The recompute strategy of the mHC paper (neo-ai summary, section on
+ * recomputation: intermediate results are recomputed in the backward pass
+ * instead of stored) applied to the projection: each matrix is projected
+ * again with the same solver and options as mhc_birkhoff_fwd, and the
+ * implicit-differentiation gradient of mhc_birkhoff_bwd (gist.science
+ * summary, section 2.2) is formed from that P while it is still in
+ * registers.  Reads 128 bytes and writes 64 per matrix; the forward pass then
+ * needs to keep only the logits.  Results equal mhc_birkhoff_bwd applied to
+ * mhc_birkhoff_fwd's P up to fp32 rounding (the gradient is computed from P
+ * in the matrix-per-lane arithmetic rather than the row-per-lane one).
+ *
+ *   logits       [B,4,4] fp32, device, 16-byte aligned
+ *   grad_P       [B,4,4] fp32, device, 16-byte aligned
+ *   grad_logits  [B,4,4] fp32, device, 16-byte aligned; may alias logits or
+ *                grad_P exactly (each matrix is read whole before it is
+ *                written), must not overlap them partially
+ *   opts         solver options as for mhc_birkhoff_fwd (NULL = defaults)
+ *   B >= 0, stream as above.  Errors as for mhc_birkhoff_fwd.
+ */
+mhc_status mhc_birkhoff_bwd_recompute(const float* logits, const float* grad_P,
+                                      float* grad_logits, int64_t B,
+                                      const mhc_proj_opts* opts, void* stream);
 
 /* mhc_stream_mix -- apply per-token mixing matrices to the n residual streams:
  *   out[t,i,c] = sum_j H[t,i,j] x[t,j,c]

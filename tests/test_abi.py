@@ -55,6 +55,7 @@ def test_default_opts(L):
 def test_empty_batch_is_noop(L):
     assert L.mhc_birkhoff_fwd(None, None, 0, None, None, None) == 0
     assert L.mhc_birkhoff_bwd(None, None, None, 0, None) == 0
+    assert L.mhc_birkhoff_bwd_recompute(None, None, None, 0, None, None) == 0
     assert L.mhc_stream_mix(None, None, None, None, 0, 4, 8, None, None) == 0
     assert L.mhc_stream_mix_bwd(None, None, None, None, None, 0, 4, 8, None) == 0
 
@@ -88,6 +89,24 @@ def test_bwd_argument_errors(L):
     # grad_logits may not overlap P at all
     assert L.mhc_birkhoff_bwd(FAKE, FAKE + 8192, FAKE, 3, None) == INVALID
     assert "overlaps P" in _err(L)
+
+
+def test_bwd_recompute_argument_errors(L):
+    assert L.mhc_birkhoff_bwd_recompute(None, None, None, 0, None, None) == 0
+    assert L.mhc_birkhoff_bwd_recompute(FAKE, FAKE, FAKE, -1, None, None) == INVALID
+    assert L.mhc_birkhoff_bwd_recompute(FAKE, None, FAKE, 3, None, None) == INVALID
+    assert L.mhc_birkhoff_bwd_recompute(FAKE + 4, FAKE + 8192, FAKE + 16384, 3, None, None) == INVALID
+    assert "aligned" in _err(L)
+    # exact aliasing of either input is allowed, partial overlap is not
+    assert L.mhc_birkhoff_bwd_recompute(FAKE, FAKE + 8192, FAKE + 64, 3, None, None) == INVALID
+    assert "overlaps logits" in _err(L)
+    assert L.mhc_birkhoff_bwd_recompute(FAKE, FAKE + 8192, FAKE + 8192 + 64, 3, None, None) == INVALID
+    assert "overlaps grad_P" in _err(L)
+    o = ProjOpts()
+    L.mhc_proj_opts_default(ctypes.byref(o))
+    o.max_iters = 0
+    assert L.mhc_birkhoff_bwd_recompute(FAKE, FAKE + 8192, FAKE + 16384, 3, ctypes.byref(o), None) == INVALID
+    assert "max_iters" in _err(L)
 
 
 def test_mix_argument_errors(L):

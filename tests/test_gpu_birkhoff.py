@@ -231,3 +231,68 @@ def test_autograd_function(gpu_lib):
     ref = birkhoff_project(A.detach().cpu().numpy().astype(np.float64))
     dref = birkhoff_project_bwd(ref, G.cpu().numpy().astype(np.float64))
     assert_bwd(A.grad.cpu().numpy(), dref, G.cpu().numpy(), label="autograd")
+
+
+def _bwd_recompute(bp, A, G, **kw):
+    dA = bp.birkhoff_bwd_recompute(torch.from_numpy(np.ascontiguousarray(A, dtype=np.float32)).cuda(),
+                                   torch.from_numpy(np.ascontiguousarray(G, dtype=np.float32)).cuda(), **kw)
+    torch.cuda.synchronize()
+    return dA.cpu().numpy()
+
+
+@pytest.mark.parametrize("kind", ["normal1", "normal10", "diag20", "normal2"])
+@pytest.mark.parametrize("B", [1, 255, 1000])
+def test_bwd_recompute(gpu_lib, kind, B):
+    """Recompute backward (logits and dL/dP in, dL/dA out, P never stored)
+    against the oracle's gradient, and against the two-pass path."""
+    print(f"recompute bwd kind={kind} B={B}", flush=True)
+    A = W.logits_batch(kind, B, 300 + B)
+    G = W.grad_batch(B, 400 + B)
+    ref = birkhoff_project(A.astype(np.float64))
+    dref = birkhoff_project_bwd(ref, G.astype(np.float64))
+    dA = _bwd_recompute(gpu_lib, A, G)
+    assert_bwd(dA, dref, G, label=f"recompute {kind} B={B}")
+    P, _ = _fwd(gpu_lib, A)
+    two_pass = _bwd(gpu_lib, P, G)
+    assert_bwd(dA, two_pass.astype(np.float64), G, label=f"recompute vs two-pass {kind} B={B}")
+
+
+def test_bwd_recompute_alias_and_solver(gpu_lib):
+    """grad_logits may be the logits' or grad_P's own buffer; the Sinkhorn
+    solver's recompute matches its own two-pass gradient."""
+    B = 777
+    A = W.logits_batch("normal2", B, 51)
+    G = W.grad_batch(B, 52)
+    want = _bwd_recompute(gpu_lib, A, G)
+    At = torch.from_numpy(A).cuda()
+    Gt = torch.from_numpy(G).cuda()
+    gpu_lib.birkhoff_bwd_recompute(At, Gt, out=At)
+    torch.cuda.synchronize()
+    assert np.array_equal(At.cpu().numpy(), want)
+    At = torch.from_numpy(A).cuda()
+    gpu_lib.birkhoff_bwd_recompute(At, Gt, out=Gt)
+    torch.cuda.synchronize()
+    assert np.array_equal(Gt.cpu().numpy(), want)
+    A1 = W.logits_batch("normal1", B, 53)
+    dA = _bwd_recompute(gpu_lib, A1, G, solver="sinkhorn", tol=1e-6, max_iters=1000)
+    P, it = _fwd(gpu_lib, A1, solver="sinkhorn", tol=1e-6, max_iters=1000)
+    assert (it != 255).all()
+    assert_bwd(dA, _bwd(gpu_lib, P, G).astype(np.float64), G, label="sinkhorn recompute")
+
+
+def test_autograd_recompute(gpu_lib):
+    """birkhoff_project(recompute=True) keeps only the logits for backward and
+    gives the same gradient as the default path to the backward bar."""
+    A0 = torch.from_numpy(W.logits_batch("normal10", 500, 54)).cuda()
+    G = torch.from_numpy(W.grad_batch(500, 55)).cuda()
+    grads = []
+    for rec in (False, True):
+        A = A0.clone().requires_grad_(True)
+        P = gpu_lib.birkhoff_project(A, recompute=rec)
+        (P * G).sum().backward()
+        torch.cuda.synchronize()
+        grads.append(A.grad.cpu().numpy())
+    ref = birkhoff_project(A0.cpu().numpy().astype(np.float64))
+    dref = birkhoff_project_bwd(ref, G.cpu().numpy().astype(np.float64))
+    for g in grads:
+        assert_bwd(g, dref, G.cpu().numpy(), label="autograd recompute")
