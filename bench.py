@@ -107,7 +107,7 @@ def cpu_baseline_projection(A, G, n_sample, label):
                       f"{label} batch), fwd+bwd, float64, {dt:.1f} s wall on {cores} processes"}
 
 
-def time_projection(bp, torch, A_np, G_np, steps, warmup, solver="newton", recompute=False):
+def time_projection(bp, torch, A_np, G_np, steps, warmup, solver="newton", recompute=False, n=4):
     """Rotate over buffer sets and time `steps` fwd+bwd steps back to back,
     then `steps` forward launches alone and `steps` backward launches alone.
 
@@ -120,8 +120,10 @@ def time_projection(bp, torch, A_np, G_np, steps, warmup, solver="newton", recom
     the replay stream bracket each replay, so a kernel's average is its
     duration plus the inter-kernel gap, comparable with a kernel trace."""
     B = A_np.shape[0]
-    set_bytes = B * 64 * 4
+    set_bytes = B * n * n * 4 * 4
     nsets = max(2, int(np.ceil(600e6 / set_bytes)))
+    fwd_fn = bp.birkhoff_fwd if n == 4 else bp.birkhoff_fwd_n
+    bwd_fn = bp.birkhoff_bwd if n == 4 else bp.birkhoff_bwd_n
     A0 = torch.from_numpy(A_np).cuda()
     G0 = torch.from_numpy(G_np).cuda()
     sets = []
@@ -130,14 +132,14 @@ def time_projection(bp, torch, A_np, G_np, steps, warmup, solver="newton", recom
 
     def fwd(k):
         A, P, G, dA = sets[k % nsets]
-        bp.birkhoff_fwd(A, out=P, solver=solver)
+        fwd_fn(A, out=P, solver=solver)
 
     def bwd(k):
         A, P, G, dA = sets[k % nsets]
         if recompute:
             bp.birkhoff_bwd_recompute(A, G, out=dA, solver=solver)
         else:
-            bp.birkhoff_bwd(P, G, out=dA)
+            bwd_fn(P, G, out=dA)
 
     def step(k):
         fwd(k)
@@ -182,8 +184,8 @@ def time_projection(bp, torch, A_np, G_np, steps, warmup, solver="newton", recom
     touched = sets[:min(steps, nsets)]
     ref = []
     for A, P, G, dA in touched:
-        Pe = bp.birkhoff_fwd(A, solver=solver)
-        dAe = bp.birkhoff_bwd_recompute(A, G, solver=solver) if recompute else bp.birkhoff_bwd(Pe, G)
+        Pe = fwd_fn(A, solver=solver)
+        dAe = bp.birkhoff_bwd_recompute(A, G, solver=solver) if recompute else bwd_fn(Pe, G)
         ref.append((Pe, dAe))
     for _ in range(2):
         for A, P, G, dA in touched:
@@ -194,7 +196,7 @@ def time_projection(bp, torch, A_np, G_np, steps, warmup, solver="newton", recom
         for (A, P, G, dA), (Pe, dAe) in zip(touched, ref):
             if not (torch.equal(P, Pe) and torch.equal(dA, dAe)):
                 raise RuntimeError("graph replay differs from eager results")
-        bp.birkhoff_fwd(sets[0][0], solver=solver)  # eager work between replays
+        fwd_fn(sets[0][0], solver=solver)  # eager work between replays
     for _ in range(2):  # warm replays
         g_step.replay()
     total_ms = replay(g_step)
@@ -215,13 +217,13 @@ def copy_probe(torch, mib):
     del x, y
 
 
-def iteration_stats(bp, torch, A_np):
+def iteration_stats(bp, torch, A_np, n=4):
     """Newton iterations per matrix (the kernel's own count) and the mean over
     waves of the largest count among a wave's 64 consecutive matrices: a wave
     runs until its slowest lane is done, so their ratio is the share of
     issued lane-work that is useful."""
     A = torch.from_numpy(A_np).cuda()
-    _, it = bp.birkhoff_fwd(A, return_iters=True)
+    _, it = (bp.birkhoff_fwd if n == 4 else bp.birkhoff_fwd_n)(A, return_iters=True)
     it = it.cpu().numpy().astype(np.int64)
     ok = it != 255
     itc = np.where(ok, it, 30)
@@ -234,7 +236,16 @@ def iteration_stats(bp, torch, A_np):
 
 def bench_projection(args, bp, torch, config):
     import workloads as W
-    if config == 2:
+    n = args.n
+    if n != 4:
+        if config not in (1, 2):
+            raise SystemExit("--n applies to configs 1 and 2 (their shapes and distributions, n x n)")
+        B = 4096 if config == 1 else 131072
+        kind = "normal1" if config == 1 else "normal10"
+        A = W.logits_batch(kind, B, 0 if config == 1 else 2, n=n)
+        G = W.grad_batch(B, 1 if config == 1 else 3, n=n)
+        label = ("N(0,1)" if config == 1 else "N(0,10^2)") + f" {n}x{n}"
+    elif config == 2:
         A, G = W.config2()
         label = "N(0,10^2)"
     elif config == 3:
@@ -245,17 +256,21 @@ def bench_projection(args, bp, torch, config):
         G = W.grad_batch(A.shape[0], 1)
         label = "N(0,1)"
     B = A.shape[0]
-    r = time_projection(bp, torch, A, G, args.steps, args.warmup, recompute=args.recompute)
+    if args.recompute and n != 4:
+        raise SystemExit("--recompute is for 4x4 matrices")
+    r = time_projection(bp, torch, A, G, args.steps, args.warmup, recompute=args.recompute, n=n)
     ms = r["total_ms"] / args.steps
     fwd_avg = float(r["fwd_ms"])
     bwd_avg = float(r["bwd_ms"])
     value = B / (ms / 1e3)
-    bwd_bytes = BWD_BYTES  # recompute: logits and dL/dP in, dL/dA out -- also 192
-    fwd_gbs = FWD_BYTES * B / (fwd_avg / 1e3) / 1e9
+    fwd_bytes = FWD_BYTES * n * n // 16
+    bwd_bytes = BWD_BYTES * n * n // 16  # recompute: logits and dL/dP in, dL/dA out -- the same
+    fwd_gbs = fwd_bytes * B / (fwd_avg / 1e3) / 1e9
     bwd_gbs = bwd_bytes * B / (bwd_avg / 1e3) / 1e9
-    step_gbs = (FWD_BYTES + bwd_bytes) * B / (ms / 1e3) / 1e9
-    m_fwd = measured(f"birkhoff_fwd_{B}_cfg{config}")
-    m_bwd = None if args.recompute else measured(f"birkhoff_bwd_{B}_cfg{config}")
+    step_gbs = (fwd_bytes + bwd_bytes) * B / (ms / 1e3) / 1e9
+    tag = "" if n == 4 else f"_n{n}"
+    m_fwd = measured(f"birkhoff_fwd{tag}_{B}_cfg{config}")
+    m_bwd = None if args.recompute else measured(f"birkhoff_bwd{tag}_{B}_cfg{config}")
     # the forward solve is bound by vector-ALU issue (transcendental-heavy
     # Newton iterations), not by its 128 bytes per matrix
     if m_fwd is not None:
@@ -277,8 +292,8 @@ def bench_projection(args, bp, torch, config):
         "value": value, "unit": "projections/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": f"birkhoff fwd+bwd, {B} 4x4 fp32 matrices {label}",
-                   "batch": B, "solver": "newton", "tol": 1e-6,
+        "config": {"workload": f"birkhoff fwd+bwd, {B} {n}x{n} fp32 matrices {label}",
+                   "batch": B, "n": n, "solver": "newton", "tol": 1e-6,
                    "backward": "recompute" if args.recompute else "from P",
                    "buffer_sets": r["nsets"]},
         "roofline": roofline,
@@ -289,10 +304,11 @@ def bench_projection(args, bp, torch, config):
         "kernels": {"fwd_us": fwd_avg * 1e3, "bwd_us": bwd_avg * 1e3, "launch": "hip graph replay",
                     "eager_us_per_step": r["eager_ms_per_step"] * 1e3},
         "valu": valu,
-        "iters": iteration_stats(bp, torch, A),
+        "iters": iteration_stats(bp, torch, A, n),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_projection(A, G, args.cpu_sample, label)
+        sample = args.cpu_sample if n == 4 else max(args.cpu_sample * 16 // (n * n * 4), 16384)
+        out["cpu_baseline"] = cpu_baseline_projection(A, G, sample, label)
     return out
 
 
@@ -390,6 +406,8 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain copy of this size first (counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--n", type=int, default=4, choices=range(1, 9), metavar="N",
+                    help="configs 1-2: n x n matrices (1..8) through mhc_birkhoff_fwd_n/bwd_n")
     ap.add_argument("--recompute", action="store_true",
                     help="configs 1-3: backward by mhc_birkhoff_bwd_recompute (logits and "
                          "dL/dP in, the projection solved again; P not kept)")

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmhc.so")
-SOURCES = ["abi.hip", "birkhoff.hip", "mix.hip", "layer.hip"]
+SOURCES = ["abi.hip", "birkhoff.hip", "birkhoffn.hip", "mix.hip", "layer.hip"]
 ARCH = "gfx950"
 
 

@@ -138,6 +138,53 @@ mhc_status mhc_birkhoff_bwd_recompute(const float* logits, const float* grad_P,
                     "birkhoff_bwd_recompute launch");
 }
 
+static bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+mhc_status mhc_birkhoff_fwd_n(const float* logits, float* P, int64_t B, int32_t n,
+                              const mhc_proj_opts* opts, uint8_t* iters, void* stream)
+{
+    if (n < 1 || n > 8)
+        return fail(MHC_ERR_UNSUPPORTED, "n must be in 1..8 (got %d)", n);
+    if (n == 4) return mhc_birkhoff_fwd(logits, P, B, opts, iters, stream);
+    if (B < 0 || B > kMaxBatch) return fail(MHC_ERR_INVALID_ARGUMENT, "B=%lld out of range", (long long)B);
+    mhc::SolverOpts o;
+    const mhc_status s = check_opts(opts, &o);
+    if (s != MHC_OK) return s;
+    if (B == 0) return ok();
+    if (logits == nullptr || P == nullptr)
+        return fail(MHC_ERR_INVALID_ARGUMENT, "logits and P must not be NULL");
+    if (!aligned4(logits) || !aligned4(P))
+        return fail(MHC_ERR_INVALID_ARGUMENT, "logits and P must be 4-byte aligned");
+    const size_t bytes = (size_t)B * n * n * 4;
+    if (logits != P && overlap(logits, bytes, P, bytes))
+        return fail(MHC_ERR_INVALID_ARGUMENT, "P partially overlaps logits");
+    if (iters != nullptr && (overlap(iters, (size_t)B, logits, bytes) || overlap(iters, (size_t)B, P, bytes)))
+        return fail(MHC_ERR_INVALID_ARGUMENT, "iters overlaps logits or P");
+    return launched(mhc::launch_birkhoff_fwd_n(logits, P, iters, B, n, o, (hipStream_t)stream),
+                    "birkhoff_fwd_n launch");
+}
+
+mhc_status mhc_birkhoff_bwd_n(const float* P, const float* grad_P, float* grad_logits, int64_t B,
+                              int32_t n, void* stream)
+{
+    if (n < 1 || n > 8)
+        return fail(MHC_ERR_UNSUPPORTED, "n must be in 1..8 (got %d)", n);
+    if (n == 4) return mhc_birkhoff_bwd(P, grad_P, grad_logits, B, stream);
+    if (B < 0 || B > kMaxBatch) return fail(MHC_ERR_INVALID_ARGUMENT, "B=%lld out of range", (long long)B);
+    if (B == 0) return ok();
+    if (P == nullptr || grad_P == nullptr || grad_logits == nullptr)
+        return fail(MHC_ERR_INVALID_ARGUMENT, "P, grad_P and grad_logits must not be NULL");
+    if (!aligned4(P) || !aligned4(grad_P) || !aligned4(grad_logits))
+        return fail(MHC_ERR_INVALID_ARGUMENT, "P, grad_P and grad_logits must be 4-byte aligned");
+    const size_t bytes = (size_t)B * n * n * 4;
+    if (overlap(P, bytes, grad_logits, bytes))
+        return fail(MHC_ERR_INVALID_ARGUMENT, "grad_logits overlaps P");
+    if (grad_P != grad_logits && overlap(grad_P, bytes, grad_logits, bytes))
+        return fail(MHC_ERR_INVALID_ARGUMENT, "grad_logits partially overlaps grad_P");
+    return launched(mhc::launch_birkhoff_bwd_n(P, grad_P, grad_logits, B, n, (hipStream_t)stream),
+                    "birkhoff_bwd_n launch");
+}
+
 mhc_status mhc_stream_mix(const void* x, const float* H_or_logits, float* H_out, void* out,
                           int64_t T, int32_t n, int64_t C, const mhc_proj_opts* proj,
                           void* stream)

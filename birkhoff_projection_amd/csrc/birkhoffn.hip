@@ -1,0 +1,171 @@
+// n x n Birkhoff projection kernels for n = 1..8 other than 4 (the 4x4 case
+// has its own kernels in birkhoff.hip).  One lane per matrix: a lane reads
+// its n*n logits (4-byte loads: an n*n*4-byte matrix is not 16-byte aligned
+// in general), solves in registers (projn.h) and writes P; the backward
+// likewise reads P and G and writes dA.  A lane reads its whole matrix before
+// writing, so P may be the logits' buffer and dA the gradient's.
+#include "kernels.h"
+#include "projn.h"
+
+namespace mhc {
+
+namespace {
+
+constexpr int kBlockN = 256;
+
+template <int N, int SOLVER>
+__global__ __launch_bounds__(kBlockN) void birkhoff_fwd_n_kernel(const float* logits, float* P,
+                                                                 uint8_t* __restrict__ iters,
+                                                                 int64_t B, SolverOpts o)
+{
+    const int64_t b = (int64_t)blockIdx.x * kBlockN + threadIdx.x;
+    if (b >= B) return;
+    float a[N * N], p[N * N];
+#pragma unroll
+    for (int e = 0; e < N * N; ++e) a[e] = logits[N * N * b + e];
+    const uint32_t it = SOLVER == 0 ? project_newton_n<N>(a, p, o) : project_sinkhorn_n<N>(a, p, o);
+#pragma unroll
+    for (int e = 0; e < N * N; ++e) P[N * N * b + e] = p[e];
+    if (iters != nullptr) iters[b] = (uint8_t)it;
+}
+
+template <int N>
+__global__ __launch_bounds__(kBlockN) void birkhoff_bwd_n_kernel(const float* __restrict__ P,
+                                                                 const float* G, float* dA,
+                                                                 int64_t B)
+{
+    const int64_t b = (int64_t)blockIdx.x * kBlockN + threadIdx.x;
+    if (b >= B) return;
+    float p[N * N], g[N * N], d[N * N];
+#pragma unroll
+    for (int e = 0; e < N * N; ++e) {
+        p[e] = P[N * N * b + e];
+        g[e] = G[N * N * b + e];
+    }
+    project_bwd_n<N>(p, g, d);
+#pragma unroll
+    for (int e = 0; e < N * N; ++e) dA[N * N * b + e] = d[e];
+}
+
+// n = 2 in closed form.  A 2x2 doubly stochastic matrix is [[p, 1-p], [1-p, p]]
+// and diag(u) exp(A) diag(v) has that form exactly when
+// p / (1-p) = sqrt(K11 K22 / (K12 K21)), i.e. p = sigmoid(s / 2) with
+// s = a11 + a22 - a12 - a21 -- the unique scaling the Newton solve converges to
+// (used for the Newton solver; Sinkhorn keeps its own iterates).  1 - p is
+// formed as sigmoid(-s / 2), without cancellation.  The gradient through it is
+// dA = (G11 - G12 - G21 + G22) p (1-p) / 2 [[1, -1], [-1, 1]].
+MHC_DEV float sigmoid_half(float s)
+{
+    return mhc_rcp(1.f + mhc_exp2(-0.5f * kLog2e * s));
+}
+
+__global__ __launch_bounds__(kBlockN) void birkhoff_fwd_2_closed_kernel(const float* logits,
+                                                                        float* P,
+                                                                        uint8_t* __restrict__ iters,
+                                                                        int64_t B)
+{
+    const int64_t b = (int64_t)blockIdx.x * kBlockN + threadIdx.x;
+    if (b >= B) return;
+    const float4 a = reinterpret_cast<const float4*>(logits)[b];
+    const float s = (a.x + a.w) - (a.y + a.z);
+    const float p = sigmoid_half(s), q = sigmoid_half(-s);
+    reinterpret_cast<float4*>(P)[b] = make_float4(p, q, q, p);
+    if (iters != nullptr) iters[b] = 0;
+}
+
+__global__ __launch_bounds__(kBlockN) void birkhoff_bwd_2_closed_kernel(const float* __restrict__ P,
+                                                                        const float* G, float* dA,
+                                                                        int64_t B)
+{
+    const int64_t b = (int64_t)blockIdx.x * kBlockN + threadIdx.x;
+    if (b >= B) return;
+    const float4 p = reinterpret_cast<const float4*>(P)[b];
+    const float4 g = reinterpret_cast<const float4*>(G)[b];
+    // p (1-p) from the two entries of a row (they sum to 1)
+    const float h = 0.5f * p.x * p.y * ((g.x - g.y) - (g.z - g.w));
+    reinterpret_cast<float4*>(dA)[b] = make_float4(h, -h, -h, h);
+}
+
+// n = 1: the only doubly stochastic 1x1 matrix is [1]; its gradient is 0.
+__global__ __launch_bounds__(kBlockN) void birkhoff_one_kernel(float* out, uint8_t* iters,
+                                                               float value, int64_t B)
+{
+    const int64_t b = (int64_t)blockIdx.x * kBlockN + threadIdx.x;
+    if (b >= B) return;
+    out[b] = value;
+    if (iters != nullptr) iters[b] = 0;
+}
+
+template <int N>
+hipError_t fwd_n(const float* logits, float* P, uint8_t* iters, int64_t B, const SolverOpts& o,
+                 hipStream_t stream)
+{
+    const dim3 grid((unsigned)((B + kBlockN - 1) / kBlockN));
+    if (o.solver == 0)
+        hipLaunchKernelGGL((birkhoff_fwd_n_kernel<N, 0>), grid, dim3(kBlockN), 0, stream, logits,
+                           P, iters, B, o);
+    else
+        hipLaunchKernelGGL((birkhoff_fwd_n_kernel<N, 1>), grid, dim3(kBlockN), 0, stream, logits,
+                           P, iters, B, o);
+    return hipGetLastError();
+}
+
+template <int N>
+hipError_t bwd_n(const float* P, const float* G, float* dA, int64_t B, hipStream_t stream)
+{
+    const dim3 grid((unsigned)((B + kBlockN - 1) / kBlockN));
+    hipLaunchKernelGGL(birkhoff_bwd_n_kernel<N>, grid, dim3(kBlockN), 0, stream, P, G, dA, B);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_birkhoff_fwd_n(const float* logits, float* P, uint8_t* iters, int64_t B, int n,
+                                 const SolverOpts& o, hipStream_t stream)
+{
+    switch (n) {
+    case 1:
+        hipLaunchKernelGGL(birkhoff_one_kernel, dim3((unsigned)((B + kBlockN - 1) / kBlockN)),
+                           dim3(kBlockN), 0, stream, P, iters, 1.f, B);
+        return hipGetLastError();
+    case 2:
+        if (o.solver == 0 && ((uintptr_t)logits & 15u) == 0 && ((uintptr_t)P & 15u) == 0) {
+            hipLaunchKernelGGL(birkhoff_fwd_2_closed_kernel, dim3((unsigned)((B + kBlockN - 1) / kBlockN)),
+                               dim3(kBlockN), 0, stream, logits, P, iters, B);
+            return hipGetLastError();
+        }
+        return fwd_n<2>(logits, P, iters, B, o, stream);
+    case 3: return fwd_n<3>(logits, P, iters, B, o, stream);
+    case 5: return fwd_n<5>(logits, P, iters, B, o, stream);
+    case 6: return fwd_n<6>(logits, P, iters, B, o, stream);
+    case 7: return fwd_n<7>(logits, P, iters, B, o, stream);
+    case 8: return fwd_n<8>(logits, P, iters, B, o, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_birkhoff_bwd_n(const float* P, const float* G, float* dA, int64_t B, int n,
+                                 hipStream_t stream)
+{
+    switch (n) {
+    case 1:
+        hipLaunchKernelGGL(birkhoff_one_kernel, dim3((unsigned)((B + kBlockN - 1) / kBlockN)),
+                           dim3(kBlockN), 0, stream, dA, nullptr, 0.f, B);
+        return hipGetLastError();
+    case 2:
+        if (((uintptr_t)P & 15u) == 0 && ((uintptr_t)G & 15u) == 0 && ((uintptr_t)dA & 15u) == 0) {
+            hipLaunchKernelGGL(birkhoff_bwd_2_closed_kernel, dim3((unsigned)((B + kBlockN - 1) / kBlockN)),
+                               dim3(kBlockN), 0, stream, P, G, dA, B);
+            return hipGetLastError();
+        }
+        return bwd_n<2>(P, G, dA, B, stream);
+    case 3: return bwd_n<3>(P, G, dA, B, stream);
+    case 5: return bwd_n<5>(P, G, dA, B, stream);
+    case 6: return bwd_n<6>(P, G, dA, B, stream);
+    case 7: return bwd_n<7>(P, G, dA, B, stream);
+    case 8: return bwd_n<8>(P, G, dA, B, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace mhc

@@ -85,6 +85,46 @@ def birkhoff_bwd(P: torch.Tensor, grad_P: torch.Tensor, out=None):
     return dA
 
 
+def birkhoff_fwd_n(logits: torch.Tensor, *, solver="newton", max_iters=None, tol=None,
+                   warm_sweeps=None, out=None, return_iters=False):
+    """Project [..., n, n] fp32 logits (1 <= n <= 8) onto the doubly
+    stochastic matrices (n = 4 runs the 4x4 kernels)."""
+    if logits.dim() < 2 or logits.shape[-1] != logits.shape[-2]:
+        raise ValueError("logits must be [..., n, n]")
+    n = logits.shape[-1]
+    _need(logits, "logits", torch.float32, (n, n))
+    B = logits.numel() // (n * n)
+    P = torch.empty_like(logits) if out is None else out
+    if out is not None:
+        _need(out, "out", torch.float32, (n, n))
+        if out.shape != logits.shape or out.device != logits.device:
+            raise ValueError("out must match logits in shape and device")
+    iters = torch.empty(logits.shape[:-2], dtype=torch.uint8, device=logits.device) if return_iters else None
+    o = make_opts(solver, max_iters, tol, warm_sweeps)
+    with torch.cuda.device(logits.device):
+        check(lib().mhc_birkhoff_fwd_n(_ptr(logits), _ptr(P), B, n, ctypes.byref(o), _ptr(iters),
+                                       _stream(logits.device)))
+    return (P, iters) if return_iters else P
+
+
+def birkhoff_bwd_n(P: torch.Tensor, grad_P: torch.Tensor, out=None):
+    """dL/dlogits for [..., n, n] P = projection(logits) and dL/dP."""
+    if P.dim() < 2 or P.shape[-1] != P.shape[-2]:
+        raise ValueError("P must be [..., n, n]")
+    n = P.shape[-1]
+    _need(P, "P", torch.float32, (n, n))
+    _need(grad_P, "grad_P", torch.float32, (n, n))
+    if P.shape != grad_P.shape or P.device != grad_P.device:
+        raise ValueError("P and grad_P must match in shape and device")
+    dA = torch.empty_like(P) if out is None else out
+    if out is not None:
+        _need(out, "out", torch.float32, (n, n))
+    with torch.cuda.device(P.device):
+        check(lib().mhc_birkhoff_bwd_n(_ptr(P), _ptr(grad_P), _ptr(dA), P.numel() // (n * n), n,
+                                       _stream(P.device)))
+    return dA
+
+
 def birkhoff_bwd_recompute(logits: torch.Tensor, grad_P: torch.Tensor, *, solver="newton",
                            max_iters=None, tol=None, warm_sweeps=None, out=None):
     """dL/dlogits from the logits and dL/dP: the projection is solved again in

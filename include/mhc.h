@@ -7,6 +7,9 @@
  *
  *   mhc_birkhoff_fwd    the projection of a batch of logit matrices
  *   mhc_birkhoff_bwd    its gradient by implicit differentiation
+ *   mhc_birkhoff_fwd_n, mhc_birkhoff_bwd_n
+ *                       the same projection and gradient for n x n matrices,
+ *                       1 <= n <= 8
  *   mhc_birkhoff_bwd_recompute
  *                       the same gradient from the logits alone (the forward
  *                       solve is redone in registers; P is not stored)
@@ -158,6 +161,28 @@ mhc_status mhc_birkhoff_bwd(const float* P, const float* grad_P, float* grad_log
 mhc_status mhc_birkhoff_bwd_recompute(const float* logits, const float* grad_P,
                                       float* grad_logits, int64_t B,
                                       const mhc_proj_opts* opts, void* stream);
+
+/* mhc_birkhoff_fwd_n / mhc_birkhoff_bwd_n -- the projection and its gradient
+ * for a batch of n x n matrices, 1 <= n <= 8.
+ *
+ * The method of mhc_birkhoff_fwd/bwd for any n (gist.science summary,
+ * section 2.1: one potential per column, one of them fixed by the shift
+ * invariance, leaving n - 1 Newton variables; section 2.2 for the gradient);
+ * the pages build n = 4, which these calls pass to mhc_birkhoff_fwd/bwd
+ * (with those calls' 16-byte alignment rule).  n = 1 gives P = [1] and a zero
+ * gradient (neo-ai summary, properties of doubly stochastic matrices).
+ *
+ *   logits, P, grad_P, grad_logits
+ *           [B,n,n] fp32 row-major, device, 4-byte aligned (16 for n = 4);
+ *           aliasing as for the n = 4 calls (P may be logits, grad_logits
+ *           may be grad_P; no partial overlap)
+ *   n       1..8, else MHC_ERR_UNSUPPORTED
+ *   opts, iters, stream, errors as for mhc_birkhoff_fwd.
+ */
+mhc_status mhc_birkhoff_fwd_n(const float* logits, float* P, int64_t B, int32_t n,
+                              const mhc_proj_opts* opts, uint8_t* iters, void* stream);
+mhc_status mhc_birkhoff_bwd_n(const float* P, const float* grad_P, float* grad_logits,
+                              int64_t B, int32_t n, void* stream);
 
 /* mhc_stream_mix -- apply per-token mixing matrices to the n residual streams:
  *   out[t,i,c] = sum_j H[t,i,j] x[t,j,c]

@@ -109,6 +109,27 @@ def test_bwd_recompute_argument_errors(L):
     assert "max_iters" in _err(L)
 
 
+def test_n_argument_errors(L):
+    assert L.mhc_birkhoff_fwd_n(FAKE, FAKE, 5, 9, None, None, None) == UNSUPPORTED
+    assert L.mhc_birkhoff_fwd_n(FAKE, FAKE, 5, 0, None, None, None) == UNSUPPORTED
+    assert L.mhc_birkhoff_bwd_n(FAKE, FAKE, FAKE, 5, 9, None) == UNSUPPORTED
+    assert L.mhc_birkhoff_fwd_n(None, None, 0, 3, None, None, None) == 0
+    assert L.mhc_birkhoff_bwd_n(None, None, None, 0, 3, None) == 0
+    assert L.mhc_birkhoff_fwd_n(FAKE + 2, FAKE + 4096, 5, 3, None, None, None) == INVALID
+    assert "aligned" in _err(L)
+    # 4-byte alignment suffices for n != 4; n = 4 keeps its 16-byte rule
+    assert L.mhc_birkhoff_fwd_n(FAKE + 4, FAKE + 4, 5, 4, None, None, None) == INVALID
+    assert "16-byte" in _err(L)
+    assert L.mhc_birkhoff_fwd_n(FAKE, FAKE + 36, 5, 3, None, None, None) == INVALID
+    assert "overlap" in _err(L)
+    assert L.mhc_birkhoff_bwd_n(FAKE, FAKE + 8192, FAKE + 36, 5, 3, None) == INVALID
+    assert "overlaps P" in _err(L)
+    o = ProjOpts()
+    L.mhc_proj_opts_default(ctypes.byref(o))
+    o.solver = 5
+    assert L.mhc_birkhoff_fwd_n(FAKE, FAKE, 5, 3, ctypes.byref(o), None, None) == INVALID
+
+
 def test_mix_argument_errors(L):
     x, h, o = FAKE, FAKE + (1 << 24), FAKE + (1 << 25)
     assert L.mhc_stream_mix(x, h, None, o, 4, 3, 64, None, None) == UNSUPPORTED
