@@ -1,9 +1,14 @@
 // n x n Birkhoff projection kernels for n = 1..8 other than 4 (the 4x4 case
-// has its own kernels in birkhoff.hip).  One lane per matrix: a lane reads
-// its n*n logits (4-byte loads: an n*n*4-byte matrix is not 16-byte aligned
-// in general), solves in registers (projn.h) and writes P; the backward
-// likewise reads P and G and writes dA.  A lane reads its whole matrix before
-// writing, so P may be the logits' buffer and dA the gradient's.
+// has its own kernels in birkhoff.hip).  One lane per matrix, solved in
+// registers (projn.h).  A matrix is n*n floats, generally not 16-byte
+// aligned and, at n = 8, 256 bytes: a lane loading its own matrix would make
+// every load instruction touch 64 lines 256 bytes apart, and the lines are
+// evicted before they are used up.  So each wave moves its 64 consecutive
+// matrices through a padded LDS tile: the global loads and stores of the wave
+// are contiguous 256-byte runs, and each lane then reads its own record from
+// LDS without bank conflicts (pitch n*n rounded up to odd).  A wave reads all
+// of its inputs before it writes, so P may be the logits' buffer and dA the
+// gradient's.
 #include "kernels.h"
 #include "projn.h"
 
@@ -13,38 +18,96 @@ namespace {
 
 constexpr int kBlockN = 256;
 
+template <int R>
+constexpr int record_pitch() { return R | 1; }
+
+// Records first .. first+63 of R floats (those below B) into each lane's
+// out[R]: coalesced loads into the wave's LDS tile, then one record per lane.
+// Records past B read as zeros.  All loads are issued before any is used
+// (addresses past the batch are clamped to its last element, the value then
+// replaced by zero), so the wave has R loads in flight.
+template <int R>
+MHC_DEV void load_records(const float* __restrict__ g, int64_t first, int64_t B, float* tile,
+                          float* out, int lane)
+{
+    constexpr int kP = record_pitch<R>();
+    const int64_t have = B - first;
+    const int64_t last = R * B - 1;
+    float v[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const int64_t idx = R * first + lane + 64 * i;
+        v[i] = g[idx < last ? idx : last];
+    }
+    mhc_wave_lds_fence();  // earlier reads of the tile by other lanes come first
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const int e = lane + 64 * i;
+        const int rec = e / R, col = e % R;
+        tile[rec * kP + col] = rec < have ? v[i] : 0.f;
+    }
+    mhc_wave_lds_fence();  // the reads below see the other lanes' writes
+#pragma unroll
+    for (int k = 0; k < R; ++k) out[k] = tile[lane * kP + k];
+}
+
+template <int R>
+MHC_DEV void store_records(float* __restrict__ g, int64_t first, int64_t B, float* tile,
+                           const float* in, int lane)
+{
+    constexpr int kP = record_pitch<R>();
+    const int64_t have = B - first;
+    mhc_wave_lds_fence();
+#pragma unroll
+    for (int k = 0; k < R; ++k) tile[lane * kP + k] = in[k];
+    mhc_wave_lds_fence();
+    if (have >= 64) {  // a full wave: no per-element checks
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const int e = lane + 64 * i;
+            g[R * first + e] = tile[(e / R) * kP + e % R];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const int e = lane + 64 * i;
+            const int rec = e / R;
+            if (rec < have) g[R * first + e] = tile[rec * kP + e % R];
+        }
+    }
+}
+
 template <int N, int SOLVER>
 __global__ __launch_bounds__(kBlockN) void birkhoff_fwd_n_kernel(const float* logits, float* P,
                                                                  uint8_t* __restrict__ iters,
                                                                  int64_t B, SolverOpts o)
 {
-    const int64_t b = (int64_t)blockIdx.x * kBlockN + threadIdx.x;
-    if (b >= B) return;
-    float a[N * N], p[N * N];
-#pragma unroll
-    for (int e = 0; e < N * N; ++e) a[e] = logits[N * N * b + e];
+    constexpr int R = N * N;
+    __shared__ float tiles[kBlockN / 64][64 * record_pitch<R>()];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t first = (int64_t)blockIdx.x * kBlockN + 64 * w;
+    if (first >= B) return;  // the whole wave is past the batch
+    float a[R], p[R];
+    load_records<R>(logits, first, B, tiles[w], a, lane);
     const uint32_t it = SOLVER == 0 ? project_newton_n<N>(a, p, o) : project_sinkhorn_n<N>(a, p, o);
-#pragma unroll
-    for (int e = 0; e < N * N; ++e) P[N * N * b + e] = p[e];
-    if (iters != nullptr) iters[b] = (uint8_t)it;
+    store_records<R>(P, first, B, tiles[w], p, lane);
+    if (iters != nullptr && first + lane < B) iters[first + lane] = (uint8_t)it;
 }
 
 template <int N>
-__global__ __launch_bounds__(kBlockN) void birkhoff_bwd_n_kernel(const float* __restrict__ P,
-                                                                 const float* G, float* dA,
-                                                                 int64_t B)
+__global__ __launch_bounds__(kBlockN) void birkhoff_bwd_n_kernel(const float* P, const float* G,
+                                                                 float* dA, int64_t B)
 {
-    const int64_t b = (int64_t)blockIdx.x * kBlockN + threadIdx.x;
-    if (b >= B) return;
-    float p[N * N], g[N * N], d[N * N];
-#pragma unroll
-    for (int e = 0; e < N * N; ++e) {
-        p[e] = P[N * N * b + e];
-        g[e] = G[N * N * b + e];
-    }
+    constexpr int R = N * N;
+    __shared__ float tiles[kBlockN / 64][64 * record_pitch<R>()];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t first = (int64_t)blockIdx.x * kBlockN + 64 * w;
+    if (first >= B) return;
+    float p[R], g[R], d[R];
+    load_records<R>(P, first, B, tiles[w], p, lane);
+    load_records<R>(G, first, B, tiles[w], g, lane);
     project_bwd_n<N>(p, g, d);
-#pragma unroll
-    for (int e = 0; e < N * N; ++e) dA[N * N * b + e] = d[e];
+    store_records<R>(dA, first, B, tiles[w], d, lane);
 }
 
 // n = 2 in closed form.  A 2x2 doubly stochastic matrix is [[p, 1-p], [1-p, p]]

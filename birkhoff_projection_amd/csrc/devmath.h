@@ -33,6 +33,17 @@ MHC_DEV float mhc_opaque(float x)
     return x;
 }
 
+// Compiler barrier for LDS data that lanes of one wave exchange.  A wave's LDS
+// instructions execute in order, so the hardware needs no wait; but the
+// optimizer models each lane as a separate thread, and without this it may
+// reuse a value the lane read from LDS earlier (or move an LDS access across
+// the exchange) when it can prove that the lane's own writes did not touch
+// that address -- other lanes' writes are invisible to it.
+MHC_DEV void mhc_wave_lds_fence()
+{
+    asm volatile("" ::: "memory");
+}
+
 // Workgroup barrier that orders LDS traffic only: waits for this wave's LDS
 // operations, then s_barrier.  Unlike __syncthreads it does not drain the
 // wave's outstanding global loads and stores, so a streaming loop keeps its

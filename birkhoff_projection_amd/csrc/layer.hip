@@ -165,10 +165,13 @@ MHC_DEV void maps_issue(const MapLane& L, MapLoads& d, int64_t k0)
 MHC_DEV void maps_consume(const MapLane& L, const MapLoads& d, uint16_t (*sX)[kMapPitch],
                           floatx4 (&acc)[kMapTiles][2], float (&ssq)[kMapTiles], int64_t k0)
 {
+    mhc_wave_lds_fence();  // the previous stage's reads of the tile come first
 #pragma unroll
     for (int q = 0; q < kMapPieces; ++q)
         *reinterpret_cast<uint4*>(&sX[kMapRowsPerLoad * q + L.pr][8 * L.pc]) = d.xr[q];
-    // the tile is read only by this wave and LDS is in order within a wave
+    // the tile is this wave's own and LDS is in order within a wave; the
+    // fence keeps the compiler from reusing earlier reads of it
+    mhc_wave_lds_fence();
     const int64_t left = (L.C - k0) / 32;
     const int ns = left < kMapSteps ? (int)left : kMapSteps;
 #pragma unroll
@@ -770,10 +773,13 @@ MHC_DEV void dw_consume(const DwLoads& d, uint16_t (*sX)[kXPitch], floatx4 (&acc
                         bool live, int lane)
 {
     const int row = lane & 15, kq = lane >> 4;
+    mhc_wave_lds_fence();  // the previous chunk's reads of the region come first
 #pragma unroll
     for (int q = 0; q < kDwPieces; ++q)
         *reinterpret_cast<uint4*>(&sX[4 * q + (lane >> 4)][8 * (lane & 15)]) = d.xr[q];
-    // the region is this wave's own and LDS is in order within a wave
+    // the region is this wave's own and LDS is in order within a wave; the
+    // fence keeps the compiler from reusing earlier reads of it
+    mhc_wave_lds_fence();
     if (!live) return;
     bf16x8 ahi[2], alo[2];
 #pragma unroll
