@@ -50,34 +50,51 @@ BWD_BYTES = 192   # per matrix: P and dL/dP in, dL/dA out
 # scaled by what the counter reads for a plain copy of known size, and VALU
 # instructions (SQ_INSTS_VALU, of which SQ_INSTS_VALU_TRANS_F32 are
 # transcendental).  They hold only for the kernel sources they were taken on:
-# every file under csrc/ is hashed, and a mismatch reports them as null.
-MEASURED_SHA = "9386592a405d01d5"
+# each entry carries the hash of the csrc files its kernels are built from
+# (KERNEL_SOURCES), and a mismatch reports it as null.
+KERNEL_SOURCES = {
+    "proj": ("devmath.h", "proj4.h", "kernels.h", "birkhoff.hip"),
+    "projn": ("devmath.h", "proj4.h", "projn.h", "kernels.h", "birkhoffn.hip"),
+    "mix": ("devmath.h", "proj4.h", "kernels.h", "mix.hip"),
+    "layer": ("devmath.h", "proj4.h", "kernels.h", "layer.hip"),
+}
 MEASURED = {
-    "birkhoff_fwd_131072_cfg2": {"fetch": 8499427, "write": 8389412, "valu": 4716769, "trans": 310834},
-    "birkhoff_bwd_131072_cfg2": {"fetch": 16848680, "write": 8388608, "valu": 976896, "trans": 26624},
-    "birkhoff_fwd_1048576_cfg3": {"fetch": 67216021, "write": 67115951, "valu": 35271807, "trans": 2344295},
-    "birkhoff_bwd_1048576_cfg3": {"fetch": 134274854, "write": 67108864, "valu": 7485440, "trans": 198656},
-    "stream_mix_fwd_16384x4x4096": {"fetch": 537966544, "write": 537919852, "valu": 25980242, "trans": 87602},
-    "layer_step_65536x4x7168": {"fetch": 30875978908, "write": 9469113107},
+    "birkhoff_fwd_131072_cfg2": {"fetch": 8497391, "write": 8389412, "valu": 4716769, "trans": 310834, "sha": "fdf5b098d492b8d4"},
+    "birkhoff_bwd_131072_cfg2": {"fetch": 16848717, "write": 8388608, "valu": 976896, "trans": 26624, "sha": "fdf5b098d492b8d4"},
+    "birkhoff_fwd_1048576_cfg3": {"fetch": 67214910, "write": 67115951, "valu": 35271807, "trans": 2344295, "sha": "fdf5b098d492b8d4"},
+    "birkhoff_bwd_1048576_cfg3": {"fetch": 134274531, "write": 67108864, "valu": 7485440, "trans": 198656, "sha": "fdf5b098d492b8d4"},
+    "birkhoff_fwd_n8_131072_cfg2": {"fetch": 33925090, "write": 33555341, "valu": 24023489, "trans": 787839, "sha": "b1ae8cfad88183db"},
+    "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67448132, "write": 33554432, "valu": 6424576, "trans": 14336, "sha": "b1ae8cfad88183db"},
+    "stream_mix_fwd_16384x4x4096": {"fetch": 537967348, "write": 537919875, "valu": 25980242, "trans": 87602, "sha": "37aaeca905a33ee9"},
+    "layer_step_65536x4x7168": {"fetch": 30891120454, "write": 9469114163, "sha": "0dda8f9b9fe7d123"},
 }
 
 
-def _sources_sha():
+def source_group(key):
+    if key.startswith(("birkhoff_fwd_n", "birkhoff_bwd_n")):
+        return "projn"
+    if key.startswith("birkhoff_"):
+        return "proj"
+    return "mix" if key.startswith("stream_mix") else "layer"
+
+
+def sources_sha(group):
     import hashlib
     h = hashlib.sha256()
     d = os.path.join(ROOT, "birkhoff_projection_amd", "csrc")
-    for f in sorted(os.listdir(d)):
+    for f in KERNEL_SOURCES[group]:
         with open(os.path.join(d, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
 
 
 def measured(key):
-    """Counter-derived per-launch figures for `key`, or None if the kernel
+    """Counter-derived per-launch figures for `key`, or None if its kernel
     sources changed since they were taken."""
-    if MEASURED_SHA is None or _sources_sha() != MEASURED_SHA:
+    m = MEASURED.get(key)
+    if m is None or m.get("sha") != sources_sha(source_group(key)):
         return None
-    return MEASURED.get(key)
+    return m
 
 
 def _cpu_worker(args):
