@@ -51,16 +51,22 @@ constexpr float kNoiseFloor = 4e-6f;
 // Curvature test of the line search: accept a trial whose directional
 // derivative is at most this fraction of the initial one's magnitude.
 constexpr float kCurvature = 0.9f;
-// Step growth: an accepted full first trial whose directional derivative
-// still has at least this fraction of its initial magnitude shows that the
-// line minimum lies well beyond the Newton step (the objective is locally
-// exponential, not quadratic, along d), so the next iteration's first trial
-// is twice as long, up to kMaxGrow times the Newton step.
+// Step growth.  Where some entries of P are tending to zero the objective is
+// exponential, not quadratic, along the Newton direction d: its directional
+// derivative decays like e^-t in units of the Newton step, so each full step
+// gains only a factor e and the potentials drift a constant distance per
+// iteration.  An accepted full first trial whose directional derivative
+// still has at least kFar of its initial magnitude doubles the next
+// iteration's first trial (up to kMaxGrow Newton steps); one that stopped
+// short of the line minimum (derivative still negative) keeps the current
+// multiple.  Either needs the trial to have cut the residual by at least
+// kGrowProgress: when the drift ends, the directional derivative keeps
+// looking far while the residual stalls, and longer trials there only
+// overshoot.  An overshoot, a stall or a backtracked iteration returns to the
+// plain Newton step.
 constexpr float kFar = 0.25f;
 constexpr float kMaxGrow = 64.f;
-// Growth stops once the residual is below kGrowMinRes, where the iteration is
-// in its quadratic phase and an overshoot would only cost trials.
-constexpr float kGrowMinRes = 1e-4f;
+constexpr float kGrowProgress = 0.5f;
 // Floor on a column mass before its logarithm is taken.
 constexpr float kMinMass = 7.8886091e-31f;  // 2^-100
 
@@ -76,13 +82,28 @@ struct SolverOpts {
 struct Eval {
     float P[16];
     float c[4];
-    float res;  // max_j |c_j - 1|
+    float b[4];  // 1 - c_j
+    float res;   // max_j |c_j - 1|
 };
+
+// Column sums of E.P, their defects b_j = 1 - c_j and the residual
+// max_j |b_j|.  Contraction is off so that the sums add the stored entries
+// (which the Hessian weights use too) instead of re-multiplying them.
+MHC_DEV void column_sums(Eval& E)
+{
+#pragma clang fp contract(off)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        E.c[j] = (E.P[j] + E.P[4 + j]) + (E.P[8 + j] + E.P[12 + j]);
+        E.b[j] = 1.f - E.c[j];
+    }
+    E.res = mhc_max(mhc_max(mhc_abs(E.b[0]), mhc_abs(E.b[1])),
+                    mhc_max(mhc_abs(E.b[2]), mhc_abs(E.b[3])));
+}
 
 // Row softmax of a + 1 g^T (g3 = 0) with the row max-shift before exp2.
 MHC_DEV void evaluate_shifted(const float* a, float g0, float g1, float g2, Eval& E)
 {
-    E.c[0] = E.c[1] = E.c[2] = E.c[3] = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const float z0 = a[4 * i + 0] + g0;
@@ -99,13 +120,8 @@ MHC_DEV void evaluate_shifted(const float* a, float g0, float g1, float g2, Eval
         E.P[4 * i + 1] = e1 * r;
         E.P[4 * i + 2] = e2 * r;
         E.P[4 * i + 3] = e3 * r;
-        E.c[0] += E.P[4 * i + 0];
-        E.c[1] += E.P[4 * i + 1];
-        E.c[2] += E.P[4 * i + 2];
-        E.c[3] += E.P[4 * i + 3];
     }
-    E.res = mhc_max(mhc_max(mhc_abs(E.c[0] - 1.f), mhc_abs(E.c[1] - 1.f)),
-                    mhc_max(mhc_abs(E.c[2] - 1.f), mhc_abs(E.c[3] - 1.f)));
+    column_sums(E);
 }
 
 // The same row softmax from k = 2^a (a's rows have maximum 0, so k <= 1 with
@@ -127,7 +143,6 @@ constexpr float kMinLogit = -126.f;
 MHC_DEV bool evaluate_factored(const float* k, float g0, float g1, float g2, Eval& E)
 {
     const float u0 = mhc_exp2(g0), u1 = mhc_exp2(g1), u2 = mhc_exp2(g2);
-    E.c[0] = E.c[1] = E.c[2] = E.c[3] = 0.f;
     bool ok = true;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -142,13 +157,8 @@ MHC_DEV bool evaluate_factored(const float* k, float g0, float g1, float g2, Eva
         E.P[4 * i + 1] = e1 * r;
         E.P[4 * i + 2] = e2 * r;
         E.P[4 * i + 3] = e3 * r;
-        E.c[0] += E.P[4 * i + 0];
-        E.c[1] += E.P[4 * i + 1];
-        E.c[2] += E.P[4 * i + 2];
-        E.c[3] += E.P[4 * i + 3];
     }
-    E.res = mhc_max(mhc_max(mhc_abs(E.c[0] - 1.f), mhc_abs(E.c[1] - 1.f)),
-                    mhc_max(mhc_abs(E.c[2] - 1.f), mhc_abs(E.c[3] - 1.f)));
+    column_sums(E);
     return ok;
 }
 
@@ -248,9 +258,9 @@ MHC_DEV uint32_t iters_code(int n) { return n > 254 ? 254u : (uint32_t)n; }
 //            minimum by much), which needs only the column sums the
 //            evaluation already has -- no logarithms.  Near the fp32 noise
 //            floor (residual <= kNoiseFloor) a trial is accepted only if it
-//            lowers the residual, and one that does not ends the solve.  A
-//            rejected trial halves t.  Every trial reaching the tolerance is
-//            accepted.
+//            lowers the residual, and a rejected trial no longer than the
+//            Newton step ends the solve.  A rejected trial halves t.  Every
+//            trial reaching the tolerance is accepted.
 // The Newton direction solves the Laplacian system of the Hessian with a
 // relative ridge (Kron reduction); its first trial step is capped at kMaxStep.
 struct NewtonLane {
@@ -275,12 +285,12 @@ MHC_DEV void newton_direction(const Eval& E, float& d0, float& d1, float& d2, fl
     const Weights w = laplacian_weights(E.P);
     const float lam = ridge(w);
     float n0, n1, n2;
-    laplacian_solve(w.w01, w.w02, w.w03, w.w12, w.w13, w.w23, lam, 1.f - E.c[0], 1.f - E.c[1],
-                    1.f - E.c[2], n0, n1, n2);
+    laplacian_solve(w.w01, w.w02, w.w03, w.w12, w.w13, w.w23, lam, E.b[0], E.b[1], E.b[2], n0,
+                    n1, n2);
     d0 = n0 * kLog2e;
     d1 = n1 * kLog2e;
     d2 = n2 * kLog2e;
-    slope = (E.c[0] - 1.f) * d0 + (E.c[1] - 1.f) * d1 + (E.c[2] - 1.f) * d2;
+    slope = -(E.b[0] * d0 + E.b[1] * d1 + E.b[2] * d2);
     const float dmax = mhc_max(mhc_max(mhc_abs(d0), mhc_abs(d1)), mhc_abs(d2));
     tcap = kMaxStep * mhc_rcp(dmax);
 }
@@ -356,7 +366,7 @@ MHC_DEV void newton_step(NewtonLane& s, const SolverOpts& o)
     float nd0, nd1, nd2, nslope, ncap;
     newton_direction(E, nd0, nd1, nd2, nslope, ncap);
 
-    const float dphi = (E.c[0] - 1.f) * s.d0 + (E.c[1] - 1.f) * s.d1 + (E.c[2] - 1.f) * s.d2;
+    const float dphi = -(E.b[0] * s.d0 + E.b[1] * s.d1 + E.b[2] * s.d2);
     // (bitwise & and | on bools: no short-circuit branches)
     const bool near_floor = s.res <= kNoiseFloor;
     const bool lower = E.res < s.res;
@@ -365,15 +375,17 @@ MHC_DEV void newton_step(NewtonLane& s, const SolverOpts& o)
     const bool pass = conv_t | (near_floor & lower) | (!near_floor & curved);
     const bool accept = ok & pass;
     const bool reject = ok & !pass;
-    // a full first trial that stayed far from the line minimum doubles the
-    // next first trial; any other accepted trial resets it to the Newton step
-    const bool far = (s.trials == 0) & (s.t >= s.grow) & (dphi <= kFar * s.slope) &
-                     (E.res > kGrowMinRes);
-    const float grow = far ? mhc_min(2.f * s.grow, kMaxGrow) : 1.f;
+    // next first trial: after a full first trial that at least halved the
+    // residual, doubled if it stayed far from the line minimum and kept if it
+    // stopped short of it; the Newton step otherwise
+    const bool first = (s.trials == 0) & (s.t >= s.grow) & (E.res < kGrowProgress * s.res);
+    const bool far = first & (dphi <= kFar * s.slope);
+    const bool short_of_min = first & (dphi < 0.f);
+    const float grow = far ? mhc_min(2.f * s.grow, kMaxGrow) : (short_of_min ? s.grow : 1.f);
     const bool conv = accept & conv_t;
     const bool maxed = accept & !conv & (s.newton >= o.max_iters);
     const int trials = s.trials + 1;
-    const bool stuck = reject & (near_floor | (trials > 30));
+    const bool stuck = reject & ((near_floor & (s.t <= 1.f)) | (trials > 30));
 
     s.g0 = accept ? t0 : s.g0;
     s.g1 = accept ? t1 : s.g1;

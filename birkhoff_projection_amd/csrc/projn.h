@@ -8,7 +8,7 @@
 //     Hessian = graph Laplacian with weights W_jk = sum_i P_ij P_ik, solved
 //     by Kron reduction (eliminating vertices in turn; every term is
 //     non-negative); globalisation, noise floor and step growth as in
-//     proj4.h;
+//     proj4.h, except that growth does not wait for the residual to halve;
 //   * backward (section 2.2): dA = P o (G - alpha 1^T - 1 beta^T) with the
 //     same Laplacian for beta, in the cancellation-free centred forms.
 // Everything is fully unrolled; a lane holds O(n^2) registers (about 250
@@ -280,13 +280,16 @@ MHC_DEV void newton_step_n(NewtonLaneN<N>& s, const SolverOpts& o)
     const bool pass = conv_t | (near_floor & lower) | (!near_floor & curved);
     const bool accept = ok & pass;
     const bool reject = ok & !pass;
-    const bool far = (s.trials == 0) & (s.t >= s.grow) & (dphi <= kFar * s.slope) &
-                     (E.res > kGrowMinRes);
-    const float grow = far ? mhc_min(2.f * s.grow, kMaxGrow) : 1.f;
+    // (no residual-progress condition here: with more columns the residual
+    // stalls in the drift too, and at n = 8 the condition cost convergence)
+    const bool first = (s.trials == 0) & (s.t >= s.grow);
+    const bool far = first & (dphi <= kFar * s.slope);
+    const bool short_of_min = first & (dphi < 0.f);
+    const float grow = far ? mhc_min(2.f * s.grow, kMaxGrow) : (short_of_min ? s.grow : 1.f);
     const bool conv = accept & conv_t;
     const bool maxed = accept & !conv & (s.newton >= o.max_iters);
     const int trials = s.trials + 1;
-    const bool stuck = reject & (near_floor | (trials > 30));
+    const bool stuck = reject & ((near_floor & (s.t <= 1.f)) | (trials > 30));
 
 #pragma unroll
     for (int j = 0; j < N - 1; ++j) {
