@@ -59,14 +59,14 @@ KERNEL_SOURCES = {
     "layer": ("devmath.h", "proj4.h", "kernels.h", "layer.hip"),
 }
 MEASURED = {
-    "birkhoff_fwd_131072_cfg2": {"fetch": 8497391, "write": 8389412, "valu": 4716769, "trans": 310834, "sha": "fdf5b098d492b8d4"},
-    "birkhoff_bwd_131072_cfg2": {"fetch": 16848717, "write": 8388608, "valu": 976896, "trans": 26624, "sha": "fdf5b098d492b8d4"},
-    "birkhoff_fwd_1048576_cfg3": {"fetch": 67214910, "write": 67115951, "valu": 35271807, "trans": 2344295, "sha": "fdf5b098d492b8d4"},
-    "birkhoff_bwd_1048576_cfg3": {"fetch": 134274531, "write": 67108864, "valu": 7485440, "trans": 198656, "sha": "fdf5b098d492b8d4"},
-    "birkhoff_fwd_n8_131072_cfg2": {"fetch": 33925090, "write": 33555341, "valu": 24023489, "trans": 787839, "sha": "b1ae8cfad88183db"},
-    "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67448132, "write": 33554432, "valu": 6424576, "trans": 14336, "sha": "b1ae8cfad88183db"},
-    "stream_mix_fwd_16384x4x4096": {"fetch": 537967348, "write": 537919875, "valu": 25980242, "trans": 87602, "sha": "37aaeca905a33ee9"},
-    "layer_step_65536x4x7168": {"fetch": 30891120454, "write": 9469114163, "sha": "0dda8f9b9fe7d123"},
+    "birkhoff_fwd_131072_cfg2": {"fetch": 8491272, "write": 8389412, "valu": 4356095, "trans": 294026, "sha": "0d7e1a300d80bc1d"},
+    "birkhoff_bwd_131072_cfg2": {"fetch": 16848755, "write": 8388608, "valu": 976896, "trans": 26624, "sha": "0d7e1a300d80bc1d"},
+    "birkhoff_fwd_1048576_cfg3": {"fetch": 67208205, "write": 67115949, "valu": 33049435, "trans": 2248538, "sha": "0d7e1a300d80bc1d"},
+    "birkhoff_bwd_1048576_cfg3": {"fetch": 134274486, "write": 67108864, "valu": 7485440, "trans": 198656, "sha": "0d7e1a300d80bc1d"},
+    "birkhoff_fwd_n8_131072_cfg2": {"fetch": 33929951, "write": 33555356, "valu": 22489476, "trans": 745416, "sha": "cbcaffe7ec444273"},
+    "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67448028, "write": 33554432, "valu": 6424576, "trans": 14336, "sha": "cbcaffe7ec444273"},
+    "stream_mix_fwd_16384x4x4096": {"fetch": 537966050, "write": 537919715, "valu": 25953598, "trans": 87580, "sha": "7f9b9fd407f18b60"},
+    "layer_step_65536x4x7168": {"fetch": 30861767994, "write": 9469111776, "sha": "951db502969214f6"},
 }
 
 
