@@ -318,8 +318,8 @@ __global__ __launch_bounds__(kBlock) void layer_mix_kernel(
         for (int64_t c = tid; c < C8; c += kBlock) {
             float xs[4][8], ff[8];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) unpack8(x[(t * 4 + j) * C8 + c], xs[j]);
-            unpack8(f[t * C8 + c], ff);
+            for (int j = 0; j < 4; ++j) unpack8(mhc_load_stream(&x[(t * 4 + j) * C8 + c]), xs[j]);
+            unpack8(mhc_load_stream(&f[t * C8 + c]), ff);
             float uu[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -328,7 +328,7 @@ __global__ __launch_bounds__(kBlock) void layer_mix_kernel(
                 s = __builtin_fmaf(M[2], xs[2][e], s);
                 uu[e] = __builtin_fmaf(M[3], xs[3][e], s);
             }
-            u[t * C8 + c] = pack8(uu);
+            mhc_store_stream(&u[t * C8 + c], pack8(uu));
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float o8[8];
@@ -340,7 +340,7 @@ __global__ __launch_bounds__(kBlock) void layer_mix_kernel(
                     s = __builtin_fmaf(M[8 + 4 * i + 2], xs[2][e], s);
                     o8[e] = __builtin_fmaf(M[8 + 4 * i + 3], xs[3][e], s);
                 }
-                xo[(t * 4 + i) * C8 + c] = pack8(o8);
+                mhc_store_stream(&xo[(t * 4 + i) * C8 + c], pack8(o8));
             }
         }
     }

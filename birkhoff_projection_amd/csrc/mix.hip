@@ -126,10 +126,10 @@ __global__ __launch_bounds__(kBlock) void stream_mix_fwd_kernel(
         for (int64_t c = tid; c < C8; c += kBlock) {
             uint4 xin[4], oo[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) xin[j] = x[row + j * C8 + c];
+            for (int j = 0; j < 4; ++j) xin[j] = mhc_load_stream(&x[row + j * C8 + c]);
             mix_chunk(M, xin, oo);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) out[row + i * C8 + c] = oo[i];
+            for (int i = 0; i < 4; ++i) mhc_store_stream(&out[row + i * C8 + c], oo[i]);
         }
     }
 }
@@ -187,12 +187,12 @@ __global__ __launch_bounds__(kBlock) void stream_mix_bwd_kernel(
             uint4 xin[4], gin[4], oo[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                xin[j] = x[row + j * C8 + c];
-                gin[j] = gout[row + j * C8 + c];
+                xin[j] = mhc_load_stream(&x[row + j * C8 + c]);
+                gin[j] = mhc_load_stream(&gout[row + j * C8 + c]);
             }
             mix_chunk(Mt, gin, oo);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) gx[row + j * C8 + c] = oo[j];
+            for (int j = 0; j < 4; ++j) mhc_store_stream(&gx[row + j * C8 + c], oo[j]);
             float xf[4][8], gf[4][8];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
