@@ -22,7 +22,7 @@ MHC_DEV void load16(const float* src, float* v)
     const float4* p = reinterpret_cast<const float4*>(src);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const float4 q = p[k];
+        const float4 q = mhc_load_stream(p + k);
         v[4 * k + 0] = q.x;
         v[4 * k + 1] = q.y;
         v[4 * k + 2] = q.z;
@@ -34,7 +34,8 @@ MHC_DEV void store16(float* dst, const float* v)
 {
     float4* p = reinterpret_cast<float4*>(dst);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) p[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+    for (int k = 0; k < 4; ++k)
+        mhc_store_stream(p + k, make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]));
 }
 
 // logits and P may be the same buffer: each lane reads its whole matrix
@@ -72,8 +73,8 @@ struct BwdRows {
 MHC_DEV void bwd_issue(const float4* P, const float4* G, int64_t r, int64_t rows, BwdRows& d)
 {
     const int64_t rc = r < rows ? r : rows - 1;
-    d.p = P[rc];
-    d.g = G[rc];
+    d.p = mhc_load_stream(P + rc);
+    d.g = mhc_load_stream(G + rc);
 }
 
 MHC_DEV void bwd_consume(const BwdRows& d, float4* dA, int64_t r)
@@ -82,7 +83,7 @@ MHC_DEV void bwd_consume(const BwdRows& d, float4* dA, int64_t r)
     const float g[4] = {d.g.x, d.g.y, d.g.z, d.g.w};
     float o[4];
     project_bwd_row(p, g, o);
-    dA[r] = make_float4(o[0], o[1], o[2], o[3]);
+    mhc_store_stream(dA + r, make_float4(o[0], o[1], o[2], o[3]));
 }
 
 MHC_DEV void bwd_consume_tail(const BwdRows& d, float4* dA, int64_t r, int64_t rows)
@@ -92,7 +93,7 @@ MHC_DEV void bwd_consume_tail(const BwdRows& d, float4* dA, int64_t r, int64_t r
     const float g[4] = {ok ? d.g.x : 0.f, ok ? d.g.y : 0.f, ok ? d.g.z : 0.f, ok ? d.g.w : 0.f};
     float o[4];
     project_bwd_row(p, g, o);
-    if (ok) dA[r] = make_float4(o[0], o[1], o[2], o[3]);
+    if (ok) mhc_store_stream(dA + r, make_float4(o[0], o[1], o[2], o[3]));
 }
 
 __global__ __launch_bounds__(kBlock) void birkhoff_bwd_kernel(const float4* __restrict__ P,
