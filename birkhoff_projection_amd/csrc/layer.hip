@@ -631,7 +631,7 @@ MHC_DEV void dx_consume(const DxLane& L, const DxLoads& d, float (*sD)[kDxPitch]
             sm = __builtin_fmaf(L.ho[2], gs[2][e], sm);
             g8[e] = __builtin_fmaf(L.ho[3], gs[3][e], sm);
         }
-        L.gf[L.tr * L.C8 + c8] = pack8(g8);
+        mhc_store_stream(&L.gf[L.tr * L.C8 + c8], pack8(g8));
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -650,7 +650,7 @@ MHC_DEV void dx_consume(const DxLane& L, const DxLoads& d, float (*sD)[kDxPitch]
             sm = __builtin_fmaf(L.hp[j], uu[e], sm);
             o8[e] = __builtin_fmaf(__builtin_fmaf(-xs[e], L.sr, dn[e]), L.inv, sm);
         }
-        L.gx[(L.tr * 4 + j) * L.C8 + c8] = pack8(o8);
+        mhc_store_stream(&L.gx[(L.tr * 4 + j) * L.C8 + c8], pack8(o8));
     }
 }
 
