@@ -53,20 +53,20 @@ BWD_BYTES = 192   # per matrix: P and dL/dP in, dL/dA out
 # each entry carries the hash of the csrc files its kernels are built from
 # (KERNEL_SOURCES), and a mismatch reports it as null.
 KERNEL_SOURCES = {
-    "proj": ("devmath.h", "proj4.h", "kernels.h", "birkhoff.hip"),
-    "projn": ("devmath.h", "proj4.h", "projn.h", "kernels.h", "birkhoffn.hip"),
+    "proj": ("devmath.h", "proj4.h", "stage.h", "kernels.h", "birkhoff.hip"),
+    "projn": ("devmath.h", "proj4.h", "projn.h", "stage.h", "kernels.h", "birkhoffn.hip"),
     "mix": ("devmath.h", "proj4.h", "kernels.h", "mix.hip"),
     "layer": ("devmath.h", "proj4.h", "kernels.h", "layer.hip"),
 }
 MEASURED = {
-    "birkhoff_fwd_131072_cfg2": {"fetch": 8491272, "write": 8389412, "valu": 4356095, "trans": 294026, "sha": "0d7e1a300d80bc1d"},
-    "birkhoff_bwd_131072_cfg2": {"fetch": 16848755, "write": 8388608, "valu": 976896, "trans": 26624, "sha": "0d7e1a300d80bc1d"},
-    "birkhoff_fwd_1048576_cfg3": {"fetch": 67208205, "write": 67115949, "valu": 33049435, "trans": 2248538, "sha": "0d7e1a300d80bc1d"},
-    "birkhoff_bwd_1048576_cfg3": {"fetch": 134274486, "write": 67108864, "valu": 7485440, "trans": 198656, "sha": "0d7e1a300d80bc1d"},
-    "birkhoff_fwd_n8_131072_cfg2": {"fetch": 33929951, "write": 33555356, "valu": 22489476, "trans": 745416, "sha": "cbcaffe7ec444273"},
-    "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67448028, "write": 33554432, "valu": 6424576, "trans": 14336, "sha": "cbcaffe7ec444273"},
-    "stream_mix_fwd_16384x4x4096": {"fetch": 537966050, "write": 537919715, "valu": 25953598, "trans": 87580, "sha": "7f9b9fd407f18b60"},
-    "layer_step_65536x4x7168": {"fetch": 30861767994, "write": 9469111776, "sha": "951db502969214f6"},
+    "birkhoff_fwd_131072_cfg2": {"fetch": 8491288, "write": 8485563, "valu": 4356095, "trans": 294026, "sha": "fbe00d98e1b23076"},
+    "birkhoff_bwd_131072_cfg2": {"fetch": 16848737, "write": 8388631, "valu": 976896, "trans": 26624, "sha": "fbe00d98e1b23076"},
+    "birkhoff_fwd_1048576_cfg3": {"fetch": 68453841, "write": 92317049, "valu": 33049435, "trans": 2248538, "sha": "fbe00d98e1b23076"},
+    "birkhoff_bwd_1048576_cfg3": {"fetch": 134274574, "write": 67108864, "valu": 7485440, "trans": 198656, "sha": "fbe00d98e1b23076"},
+    "birkhoff_fwd_n8_131072_cfg2": {"fetch": 33929917, "write": 33555355, "valu": 22489476, "trans": 745416, "sha": "943c493b299b2e67"},
+    "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67448173, "write": 33554432, "valu": 6424576, "trans": 14336, "sha": "943c493b299b2e67"},
+    "stream_mix_fwd_16384x4x4096": {"fetch": 537973752, "write": 537926272, "valu": 25679166, "trans": 87580, "sha": "5671d1e437a30d56"},
+    "layer_step_65536x4x7168": {"fetch": 30734402423, "write": 9469202125, "sha": "0c79f53321dfd3a6"},
 }
 
 

@@ -1,15 +1,18 @@
 // Batched 4x4 Birkhoff projection kernels for gfx950: forward (Newton or
 // Sinkhorn-Knopp) and backward (implicit differentiation).
 //
-// Layout: one lane per matrix, 64 matrices per wave64, 256 per workgroup.
-// A lane reads its matrix as four 16-byte loads (64 contiguous bytes), keeps
-// the whole solve in VGPRs (proj4.h) and writes four 16-byte stores.  There is
-// no cross-lane communication, so a tail wave simply masks off the lanes past
-// B.  The forward is bound by VALU work (exp2/log2/rcp and the Newton solve);
-// the backward is straight-line and bound by HBM traffic (192 bytes/matrix),
-// so it uses one row per lane instead (see birkhoff_bwd_kernel).
+// Forward layout: one lane per matrix, 64 matrices per wave64, 256 per
+// workgroup.  A wave moves its 64 consecutive matrices (4 KB) through a
+// per-wave LDS tile (stage.h), so its global loads and stores are contiguous
+// 1 KB pieces, and each lane keeps its whole solve in VGPRs (proj4.h).  There
+// is no other cross-lane communication; lanes past B solve a zero matrix and
+// store nothing.  The forward is bound by VALU work (exp2/log2/rcp and the
+// Newton solve); the backward is straight-line and bound by HBM traffic
+// (192 bytes/matrix), so it uses one row per lane instead (see
+// birkhoff_bwd_kernel).
 #include "kernels.h"
 #include "proj4.h"
+#include "stage.h"
 
 namespace mhc {
 
@@ -17,41 +20,22 @@ namespace {
 
 constexpr int kBlock = 256;
 
-MHC_DEV void load16(const float* src, float* v)
-{
-    const float4* p = reinterpret_cast<const float4*>(src);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const float4 q = mhc_load_stream(p + k);
-        v[4 * k + 0] = q.x;
-        v[4 * k + 1] = q.y;
-        v[4 * k + 2] = q.z;
-        v[4 * k + 3] = q.w;
-    }
-}
-
-MHC_DEV void store16(float* dst, const float* v)
-{
-    float4* p = reinterpret_cast<float4*>(dst);
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-        mhc_store_stream(p + k, make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]));
-}
-
-// logits and P may be the same buffer: each lane reads its whole matrix
-// before it writes it, and no lane touches another lane's matrix.
+// logits and P may be the same buffer: a wave reads all of its matrices
+// before it writes any, and no wave touches another wave's matrices.
 template <int SOLVER>
 __global__ __launch_bounds__(kBlock) void birkhoff_fwd_kernel(const float* logits, float* P,
                                                               uint8_t* __restrict__ iters,
                                                               int64_t B, SolverOpts o)
 {
-    const int64_t b = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    if (b >= B) return;
+    __shared__ float tiles[kBlock / 64][stage_tile_floats<16>()];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t first = (int64_t)blockIdx.x * kBlock + 64 * w;
+    if (first >= B) return;  // the whole wave is past the batch
     float a[16], p[16];
-    load16(logits + 16 * b, a);
+    load_records_v4<16>(logits, first, B, tiles[w], a, lane);
     const uint32_t it = SOLVER == 0 ? project_newton(a, p, o) : project_sinkhorn(a, p, o);
-    store16(P + 16 * b, p);
-    if (iters != nullptr) iters[b] = (uint8_t)it;
+    store_records_v4<16>(P, first, B, tiles[w], p, lane);
+    if (iters != nullptr && first + lane < B) iters[first + lane] = (uint8_t)it;
 }
 
 // Backward: one row per lane (quad = one matrix), so loads and stores are
@@ -129,25 +113,28 @@ __global__ __launch_bounds__(kBlock) void birkhoff_bwd_kernel(const float4* __re
 
 // Recompute backward: lane per matrix, the forward solve redone in
 // registers and the implicit-differentiation gradient formed from that P
-// (matrix-per-lane form of the backward).  logits or G may be the same buffer
-// as dA: a lane reads its whole matrix from both before writing.
+// (matrix-per-lane form of the backward), records staged as in the forward.
+// logits or G may be the same buffer as dA: a wave reads all of its matrices
+// from both before writing.
 template <int SOLVER>
 __global__ __launch_bounds__(kBlock) void birkhoff_bwd_recompute_kernel(const float* logits,
                                                                         const float* G,
                                                                         float* dA, int64_t B,
                                                                         SolverOpts o)
 {
-    const int64_t b = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    if (b >= B) return;
+    __shared__ float tiles[kBlock / 64][stage_tile_floats<16>()];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t first = (int64_t)blockIdx.x * kBlock + 64 * w;
+    if (first >= B) return;
     float a[16], g[16], p[16], d[16];
-    load16(logits + 16 * b, a);
-    load16(G + 16 * b, g);
+    load_records_v4<16>(logits, first, B, tiles[w], a, lane);
+    load_records_v4<16>(G, first, B, tiles[w], g, lane);
     if (SOLVER == 0)
         project_newton(a, p, o);
     else
         project_sinkhorn(a, p, o);
     project_bwd(p, g, d);
-    store16(dA + 16 * b, d);
+    store_records_v4<16>(dA, first, B, tiles[w], d, lane);
 }
 
 }  // namespace

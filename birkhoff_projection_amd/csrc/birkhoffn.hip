@@ -1,16 +1,13 @@
 // n x n Birkhoff projection kernels for n = 1..8 other than 4 (the 4x4 case
 // has its own kernels in birkhoff.hip).  One lane per matrix, solved in
 // registers (projn.h).  A matrix is n*n floats, generally not 16-byte
-// aligned and, at n = 8, 256 bytes: a lane loading its own matrix would make
-// every load instruction touch 64 lines 256 bytes apart, and the lines are
-// evicted before they are used up.  So each wave moves its 64 consecutive
-// matrices through a padded LDS tile: the global loads and stores of the wave
-// are contiguous 256-byte runs, and each lane then reads its own record from
-// LDS without bank conflicts (pitch n*n rounded up to odd).  A wave reads all
-// of its inputs before it writes, so P may be the logits' buffer and dA the
-// gradient's.
+// aligned and, at n = 8, 256 bytes, so each wave moves its 64 consecutive
+// matrices through a padded LDS tile (stage.h): the wave's global loads and
+// stores are contiguous 256-byte runs.  A wave reads all of its inputs before
+// it writes, so P may be the logits' buffer and dA the gradient's.
 #include "kernels.h"
 #include "projn.h"
+#include "stage.h"
 
 namespace mhc {
 
@@ -18,72 +15,13 @@ namespace {
 
 constexpr int kBlockN = 256;
 
-template <int R>
-constexpr int record_pitch() { return R | 1; }
-
-// Records first .. first+63 of R floats (those below B) into each lane's
-// out[R]: coalesced loads into the wave's LDS tile, then one record per lane.
-// Records past B read as zeros.  All loads are issued before any is used
-// (addresses past the batch are clamped to its last element, the value then
-// replaced by zero), so the wave has R loads in flight.
-template <int R>
-MHC_DEV void load_records(const float* __restrict__ g, int64_t first, int64_t B, float* tile,
-                          float* out, int lane)
-{
-    constexpr int kP = record_pitch<R>();
-    const int64_t have = B - first;
-    const int64_t last = R * B - 1;
-    float v[R];
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-        const int64_t idx = R * first + lane + 64 * i;
-        v[i] = g[idx < last ? idx : last];
-    }
-    mhc_wave_lds_fence();  // earlier reads of the tile by other lanes come first
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-        const int e = lane + 64 * i;
-        const int rec = e / R, col = e % R;
-        tile[rec * kP + col] = rec < have ? v[i] : 0.f;
-    }
-    mhc_wave_lds_fence();  // the reads below see the other lanes' writes
-#pragma unroll
-    for (int k = 0; k < R; ++k) out[k] = tile[lane * kP + k];
-}
-
-template <int R>
-MHC_DEV void store_records(float* __restrict__ g, int64_t first, int64_t B, float* tile,
-                           const float* in, int lane)
-{
-    constexpr int kP = record_pitch<R>();
-    const int64_t have = B - first;
-    mhc_wave_lds_fence();
-#pragma unroll
-    for (int k = 0; k < R; ++k) tile[lane * kP + k] = in[k];
-    mhc_wave_lds_fence();
-    if (have >= 64) {  // a full wave: no per-element checks
-#pragma unroll
-        for (int i = 0; i < R; ++i) {
-            const int e = lane + 64 * i;
-            g[R * first + e] = tile[(e / R) * kP + e % R];
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < R; ++i) {
-            const int e = lane + 64 * i;
-            const int rec = e / R;
-            if (rec < have) g[R * first + e] = tile[rec * kP + e % R];
-        }
-    }
-}
-
 template <int N, int SOLVER>
 __global__ __launch_bounds__(kBlockN) void birkhoff_fwd_n_kernel(const float* logits, float* P,
                                                                  uint8_t* __restrict__ iters,
                                                                  int64_t B, SolverOpts o)
 {
     constexpr int R = N * N;
-    __shared__ float tiles[kBlockN / 64][64 * record_pitch<R>()];
+    __shared__ float tiles[kBlockN / 64][stage_tile_floats<R>()];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int64_t first = (int64_t)blockIdx.x * kBlockN + 64 * w;
     if (first >= B) return;  // the whole wave is past the batch
@@ -99,7 +37,7 @@ __global__ __launch_bounds__(kBlockN) void birkhoff_bwd_n_kernel(const float* P,
                                                                  float* dA, int64_t B)
 {
     constexpr int R = N * N;
-    __shared__ float tiles[kBlockN / 64][64 * record_pitch<R>()];
+    __shared__ float tiles[kBlockN / 64][stage_tile_floats<R>()];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int64_t first = (int64_t)blockIdx.x * kBlockN + 64 * w;
     if (first >= B) return;
