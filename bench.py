@@ -59,14 +59,14 @@ KERNEL_SOURCES = {
     "layer": ("devmath.h", "proj4.h", "kernels.h", "layer.hip"),
 }
 MEASURED = {
-    "birkhoff_fwd_131072_cfg2": {"fetch": 8491288, "write": 8485563, "valu": 4356095, "trans": 294026, "sha": "fbe00d98e1b23076"},
-    "birkhoff_bwd_131072_cfg2": {"fetch": 16848737, "write": 8388631, "valu": 976896, "trans": 26624, "sha": "fbe00d98e1b23076"},
-    "birkhoff_fwd_1048576_cfg3": {"fetch": 68453841, "write": 92317049, "valu": 33049435, "trans": 2248538, "sha": "fbe00d98e1b23076"},
-    "birkhoff_bwd_1048576_cfg3": {"fetch": 134274574, "write": 67108864, "valu": 7485440, "trans": 198656, "sha": "fbe00d98e1b23076"},
-    "birkhoff_fwd_n8_131072_cfg2": {"fetch": 33929917, "write": 33555355, "valu": 22489476, "trans": 745416, "sha": "943c493b299b2e67"},
-    "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67448173, "write": 33554432, "valu": 6424576, "trans": 14336, "sha": "943c493b299b2e67"},
-    "stream_mix_fwd_16384x4x4096": {"fetch": 537973752, "write": 537926272, "valu": 25679166, "trans": 87580, "sha": "5671d1e437a30d56"},
-    "layer_step_65536x4x7168": {"fetch": 30734402423, "write": 9469202125, "sha": "0c79f53321dfd3a6"},
+    "birkhoff_fwd_131072_cfg2": {"fetch": 8497411, "write": 8389412, "valu": 4534296, "trans": 294026, "sha": "1cb976dbac0cfad9"},
+    "birkhoff_bwd_131072_cfg2": {"fetch": 16848700, "write": 8388608, "valu": 976896, "trans": 26624, "sha": "1cb976dbac0cfad9"},
+    "birkhoff_fwd_1048576_cfg3": {"fetch": 67217078, "write": 67115949, "valu": 34475040, "trans": 2248538, "sha": "1cb976dbac0cfad9"},
+    "birkhoff_bwd_1048576_cfg3": {"fetch": 134274249, "write": 67108864, "valu": 7485440, "trans": 198656, "sha": "1cb976dbac0cfad9"},
+    "birkhoff_fwd_n8_131072_cfg2": {"fetch": 33929894, "write": 33555308, "valu": 22489476, "trans": 745416, "sha": "419583f86fcba2d6"},
+    "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67447807, "write": 33554514, "valu": 6424576, "trans": 14336, "sha": "419583f86fcba2d6"},
+    "stream_mix_fwd_16384x4x4096": {"fetch": 537970942, "write": 537926746, "valu": 25679166, "trans": 87580, "sha": "5671d1e437a30d56"},
+    "layer_step_65536x4x7168": {"fetch": 30737965722, "write": 9469208410, "sha": "0c79f53321dfd3a6"},
 }
 
 
