@@ -66,6 +66,7 @@ MEASURED = {
     "birkhoff_fwd_n8_131072_cfg2": {"fetch": 33929894, "write": 33555308, "valu": 22489476, "trans": 745416, "sha": "419583f86fcba2d6"},
     "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67447807, "write": 33554514, "valu": 6424576, "trans": 14336, "sha": "419583f86fcba2d6"},
     "stream_mix_fwd_16384x4x4096": {"fetch": 537970942, "write": 537926746, "valu": 25679166, "trans": 87580, "sha": "5671d1e437a30d56"},
+    "stream_mix_bwd_16384x4x4096": {"fetch": 1074730354, "write": 537943255, "valu": 50135040, "trans": 0, "sha": "5671d1e437a30d56"},
     "layer_step_65536x4x7168": {"fetch": 30737965722, "write": 9469208410, "sha": "0c79f53321dfd3a6"},
 }
 
@@ -367,6 +368,31 @@ def bench_mix(args, bp, torch):
     }
 
 
+def bench_mix_bwd(args, bp, torch):
+    """Stream-mix backward alone (mhc_stream_mix_bwd), T=16384, C=4096: the
+    standalone call; the layer step uses its own backward passes."""
+    import workloads as W
+    T, C = W.CONFIG4_SHAPE["T"], W.CONFIG4_SHAPE["C"]
+    x, dout, logits = W.mix_bwd_inputs(T, C, seed=44)
+    H = bp.birkhoff_fwd(logits)
+    gx, gH = torch.empty_like(x), torch.empty_like(H)
+    ms = _time_loop(torch, lambda k: bp.stream_mix_bwd(x, H, dout, out=(gx, gH)), args.steps,
+                    args.warmup)
+    per_tok = 3 * (4 * C * 2) + 64 + 64  # x, grad_out in, grad_x out; H in, grad_H out
+    gbs = per_tok * T / (ms / 1e3) / 1e9
+    m = measured(f"stream_mix_bwd_{T}x4x{C}")
+    return {
+        "metric": "stream mix backward tokens/s; achieved HBM GB/s vs peak",
+        "value": T / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"stream mix backward, T={T}, n=4, C={C} bf16"},
+        "roofline": {"bound": "hbm", "kernel": "stream_mix_bwd", "achieved": gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": m["fetch"] + m["write"] if m else None},
+    }
+
+
 def bench_layer(args, bp, torch):
     """Full layer step fwd+bwd, T=65536, n=4, C=7168."""
     import workloads as W
@@ -425,6 +451,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--n", type=int, default=4, choices=range(1, 9), metavar="N",
                     help="configs 1-2: n x n matrices (1..8) through mhc_birkhoff_fwd_n/bwd_n")
+    ap.add_argument("--mix-bwd", action="store_true",
+                    help="config 4: time the standalone stream-mix backward instead")
     ap.add_argument("--recompute", action="store_true",
                     help="configs 1-3: backward by mhc_birkhoff_bwd_recompute (logits and "
                          "dL/dP in, the projection solved again; P not kept)")
@@ -443,7 +471,7 @@ def main():
     if args.copy_probe_mib:
         copy_probe(torch, args.copy_probe_mib)
     if args.config == 4:
-        out = bench_mix(args, bp, torch)
+        out = bench_mix_bwd(args, bp, torch) if args.mix_bwd else bench_mix(args, bp, torch)
     elif args.config == 5:
         out = bench_layer(args, bp, torch)
     else:

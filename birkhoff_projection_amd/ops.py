@@ -209,14 +209,21 @@ def stream_mix(x: torch.Tensor, H: torch.Tensor = None, *, logits: torch.Tensor 
     return (y, H_out) if return_H else y
 
 
-def stream_mix_bwd(x: torch.Tensor, H: torch.Tensor, grad_out: torch.Tensor):
-    """(grad_x bf16 [T,4,C], grad_H fp32 [T,4,4]) of the stream mix."""
+def stream_mix_bwd(x: torch.Tensor, H: torch.Tensor, grad_out: torch.Tensor, out=None):
+    """(grad_x bf16 [T,4,C], grad_H fp32 [T,4,4]) of the stream mix; ``out``
+    may be a preallocated (grad_x, grad_H) pair."""
     _need(x, "x", torch.bfloat16)
     _need(grad_out, "grad_out", torch.bfloat16)
     T, n, C = x.shape
     _need(H, "H", torch.float32, (n, n))
-    gx = torch.empty_like(x)
-    gH = torch.empty_like(H)
+    if out is None:
+        gx, gH = torch.empty_like(x), torch.empty_like(H)
+    else:
+        gx, gH = out
+        _need(gx, "grad_x", torch.bfloat16)
+        _need(gH, "grad_H", torch.float32, (n, n))
+        if gx.shape != x.shape or gH.shape != H.shape:
+            raise ValueError("out must be (grad_x like x, grad_H like H)")
     with torch.cuda.device(x.device):
         check(lib().mhc_stream_mix_bwd(_ptr(x), _ptr(H), _ptr(grad_out), _ptr(gx), _ptr(gH), T,
                                        n, C, _stream(x.device)))
