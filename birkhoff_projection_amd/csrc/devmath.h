@@ -33,6 +33,15 @@ MHC_DEV float mhc_opaque(float x)
     return x;
 }
 
+// Like mhc_opaque, but the value is materialised on every path: a volatile
+// statement cannot be sunk into one arm of a branch, so a select between
+// pinned values stays a v_cndmask instead of becoming an if/else.
+MHC_DEV float mhc_pin(float x)
+{
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 // Compiler barrier for LDS data that lanes of one wave exchange.  A wave's LDS
 // instructions execute in order, so the hardware needs no wait; but the
 // optimizer models each lane as a separate thread, and without this it may

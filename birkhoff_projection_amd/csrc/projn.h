@@ -285,7 +285,9 @@ MHC_DEV void newton_step_n(NewtonLaneN<N>& s, const SolverOpts& o)
     const bool first = (s.trials == 0) & (s.t >= s.grow);
     const bool far = first & (dphi <= kFar * s.slope);
     const bool short_of_min = first & (dphi < 0.f);
-    const float grow = far ? mhc_min(2.f * s.grow, kMaxGrow) : (short_of_min ? s.grow : 1.f);
+    const float grow_far = mhc_pin(mhc_min(2.f * s.grow, kMaxGrow));
+    const float grow_else = mhc_pin(short_of_min ? s.grow : 1.f);
+    const float grow = far ? grow_far : grow_else;
     const bool conv = accept & conv_t;
     const bool maxed = accept & !conv & (s.newton >= o.max_iters);
     const int trials = s.trials + 1;
