@@ -52,8 +52,8 @@ mhc_status check_opts(const mhc_proj_opts* in, mhc::SolverOpts* out)
         return fail(MHC_ERR_INVALID_ARGUMENT, "opts.max_iters must be in 1..10000");
     if (!(o.tol >= 0.f) || o.tol > 1.f)
         return fail(MHC_ERR_INVALID_ARGUMENT, "opts.tol must be in [0, 1]");
-    if (o.warm_sweeps < 0 || o.warm_sweeps > 64)
-        return fail(MHC_ERR_INVALID_ARGUMENT, "opts.warm_sweeps must be in 0..64");
+    if (o.warm_sweeps < -1 || o.warm_sweeps > 64)
+        return fail(MHC_ERR_INVALID_ARGUMENT, "opts.warm_sweeps must be -1 (default) or in 0..64");
     *out = mhc::SolverOpts{o.solver, o.max_iters, o.tol, o.warm_sweeps};
     return MHC_OK;
 }
@@ -74,7 +74,7 @@ mhc_status mhc_proj_opts_default(mhc_proj_opts* opts)
     opts->solver = MHC_SOLVER_NEWTON;
     opts->max_iters = 30;
     opts->tol = 1e-6f;
-    opts->warm_sweeps = 1;
+    opts->warm_sweeps = -1;
     return MHC_OK;
 }
 

@@ -229,7 +229,8 @@ MHC_DEV void newton_init_n(NewtonLaneN<N>& s, const float* a_nat, const SolverOp
     s.res = E.res;
     s.done = s.res <= o.tol;
     s.code = 0;
-    for (int sw = 0; sw < o.warm_sweeps; ++sw) {
+    const int warm = o.warm_sweeps < 0 ? 1 : o.warm_sweeps;  // -1: one sweep from g = 0
+    for (int sw = 0; sw < warm; ++sw) {
         const float ln = mhc_log2(mhc_max(E.c[N - 1], kMinMass));
         float ng[N - 1];
 #pragma unroll

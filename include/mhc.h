@@ -85,8 +85,13 @@ typedef struct {
                             normalised last, so they sum to 1 up to rounding);
                             default 1e-6.  Sinkhorn with tol == 0 runs exactly
                             max_iters sweeps (fixed-count mode). */
-    int32_t warm_sweeps; /* log-domain Sinkhorn sweeps before the first Newton
-                            step; default 1; 0 .. 64 */
+    int32_t warm_sweeps; /* log-domain Sinkhorn sweeps between the starting
+                            point and the first Newton step; 0 .. 64, or -1
+                            (the default) for the solver's own choice: none
+                            for n = 4, whose start (from the assignment
+                            problem) leaves nothing for a sweep to gain, and
+                            one for the general-n solver, which starts from
+                            g = 0 */
 } mhc_proj_opts;
 
 /* Iteration codes written to the optional `iters` output. */

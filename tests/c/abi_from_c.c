@@ -34,7 +34,7 @@ int main(void)
     CHECK(mhc_last_error() != NULL);
 
     CHECK(mhc_proj_opts_default(&o) == MHC_OK);
-    CHECK(o.solver == MHC_SOLVER_NEWTON && o.max_iters == 30 && o.warm_sweeps == 1);
+    CHECK(o.solver == MHC_SOLVER_NEWTON && o.max_iters == 30 && o.warm_sweeps == -1);
     CHECK(o.tol > 0.9e-6f && o.tol < 1.1e-6f);
     CHECK(mhc_proj_opts_default(NULL) == MHC_ERR_INVALID_ARGUMENT);
 

@@ -47,7 +47,7 @@ def test_abi_version_and_strings(L):
 def test_default_opts(L):
     o = ProjOpts()
     assert L.mhc_proj_opts_default(ctypes.byref(o)) == 0
-    assert (o.solver, o.max_iters, o.warm_sweeps) == (0, 30, 1)
+    assert (o.solver, o.max_iters, o.warm_sweeps) == (0, 30, -1)
     assert abs(o.tol - 1e-6) < 1e-12
     assert L.mhc_proj_opts_default(None) == INVALID
 
@@ -74,7 +74,8 @@ def test_fwd_argument_errors(L):
     assert L.mhc_birkhoff_fwd(FAKE, FAKE + 64, 5, None, None, None) == INVALID
     assert "overlap" in _err(L)
     for field, value in (("solver", 3), ("max_iters", 0), ("max_iters", 10001),
-                         ("tol", -1.0), ("tol", float("nan")), ("warm_sweeps", 65)):
+                         ("tol", -1.0), ("tol", float("nan")), ("warm_sweeps", 65),
+                         ("warm_sweeps", -2)):
         o = ProjOpts()
         L.mhc_proj_opts_default(ctypes.byref(o))
         setattr(o, field, value)
