@@ -59,15 +59,15 @@ KERNEL_SOURCES = {
     "layer": ("devmath.h", "proj4.h", "kernels.h", "layer.hip"),
 }
 MEASURED = {
-    "birkhoff_fwd_131072_cfg2": {"fetch": 8497480, "write": 8389412, "valu": 4546350, "trans": 294026, "sha": "a83a84703524f760"},
-    "birkhoff_bwd_131072_cfg2": {"fetch": 16848706, "write": 8388608, "valu": 976896, "trans": 26624, "sha": "a83a84703524f760"},
-    "birkhoff_fwd_1048576_cfg3": {"fetch": 67216812, "write": 67115949, "valu": 34596110, "trans": 2248538, "sha": "a83a84703524f760"},
-    "birkhoff_bwd_1048576_cfg3": {"fetch": 134274555, "write": 67108864, "valu": 7485440, "trans": 198656, "sha": "a83a84703524f760"},
-    "birkhoff_fwd_n8_131072_cfg2": {"fetch": 33928039, "write": 33555309, "valu": 22585748, "trans": 745229, "sha": "32880e5ad924d6b9"},
-    "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67447826, "write": 33555276, "valu": 6424576, "trans": 14336, "sha": "32880e5ad924d6b9"},
-    "stream_mix_fwd_16384x4x4096": {"fetch": 537972068, "write": 537925510, "valu": 25687092, "trans": 87580, "sha": "3727c82adac701fd"},
-    "stream_mix_bwd_16384x4x4096": {"fetch": 1074731734, "write": 537962473, "valu": 50135040, "trans": 0, "sha": "3727c82adac701fd"},
-    "layer_step_65536x4x7168": {"fetch": 30727631706, "write": 9469199469, "sha": "2b7a647b9b279504"},
+    "birkhoff_fwd_131072_cfg2": {"fetch": 8535295, "write": 8389412, "valu": 2777594, "trans": 150185, "sha": "68f0e2fece420514"},
+    "birkhoff_bwd_131072_cfg2": {"fetch": 16848627, "write": 8388608, "valu": 976896, "trans": 26624, "sha": "68f0e2fece420514"},
+    "birkhoff_fwd_1048576_cfg3": {"fetch": 67251208, "write": 67116138, "valu": 21246384, "trans": 1144634, "sha": "68f0e2fece420514"},
+    "birkhoff_bwd_1048576_cfg3": {"fetch": 134274402, "write": 67108864, "valu": 7485440, "trans": 198656, "sha": "68f0e2fece420514"},
+    "birkhoff_fwd_n8_131072_cfg2": {"fetch": 33927927, "write": 33555316, "valu": 22585748, "trans": 745229, "sha": "78084b7ec7982182"},
+    "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67447656, "write": 33554722, "valu": 6424576, "trans": 14336, "sha": "78084b7ec7982182"},
+    "stream_mix_fwd_16384x4x4096": {"fetch": 537991873, "write": 537927191, "valu": 25710592, "trans": 68608, "sha": "5e0a953206ecbe03"},
+    "stream_mix_bwd_16384x4x4096": {"fetch": 1074729265, "write": 537959255, "valu": 50135040, "trans": 0, "sha": "5e0a953206ecbe03"},
+    "layer_step_65536x4x7168": {"fetch": 30734967755, "write": 9469207667, "sha": "5215c1a5373b532c"},
 }
 
 
