@@ -9,6 +9,8 @@
 //     by Kron reduction (eliminating vertices in turn; every term is
 //     non-negative); globalisation, noise floor and step growth as in
 //     proj4.h, except that growth does not wait for the residual to halve;
+//     for 3 <= n <= 6 the start comes from the assignment problem as in
+//     proj4.h (n = 7, 8 start from g = 0), followed by one Sinkhorn sweep;
 //   * backward (section 2.2): dA = P o (G - alpha 1^T - 1 beta^T) with the
 //     same Laplacian for beta, in the cancellation-free centred forms.
 // Everything is fully unrolled; a lane holds O(n^2) registers (about 250
@@ -200,6 +202,118 @@ MHC_DEV void newton_direction_n(const EvalN<N>& E, float* d, float& slope, float
     tcap = kMaxStep * mhc_rcp(dmax);
 }
 
+// Largest n whose start comes from the assignment problem (the 4x4 start of
+// proj4.h, assignment_start, for any n): the best permutation by dynamic
+// programming over column subsets, two layers of which are live at a time
+// (at most 20 + 15 states at n = 6, each a value and its permutation packed
+// 3 bits per row); larger n would need more registers than a lane has left.
+constexpr int kAssignStartMaxN = 6;
+
+constexpr int popcount_c(int m) { return m == 0 ? 0 : (m & 1) + popcount_c(m >> 1); }
+
+// Starting potentials g_0..g_{n-2} (base 2, g_{n-1} = 0) from the assignment
+// problem on the base-2 logits a: the optimal permutation, the middle of each
+// column potential's range over the optimal LP duals (shortest paths to and
+// from column n-1 in the permutation's exchange graph, n-2 Bellman-Ford
+// rounds after the direct edges), then two max-balancing sweeps; g = 0 if the
+// result is not finite.  See assignment_start in proj4.h for the reasoning.
+template <int N>
+MHC_DEV void assignment_start_n(const float* a, float* g)
+{
+    static_assert(N >= 3 && N <= kAssignStartMaxN, "assignment start: 3 <= n <= 6");
+    // best[mask]: largest sum of a[r][sigma(r)] over rows r < popcount(mask)
+    // assigned to the columns in mask; code[mask]: those columns, 3 bits a row
+    float best[1 << N];
+    uint32_t code[1 << N];
+    best[0] = 0.f;
+    code[0] = 0u;
+#pragma unroll
+    for (int row = 0; row < N; ++row) {
+#pragma unroll
+        for (int mask = 1; mask < (1 << N); ++mask) {
+            if (popcount_c(mask) != row + 1) continue;
+            float v = -__builtin_inff();
+            uint32_t c = 0u;
+            bool first = true;
+#pragma unroll
+            for (int j = 0; j < N; ++j) {
+                if (!(mask & (1 << j))) continue;
+                const int prev = mask ^ (1 << j);
+                const float cand = best[prev] + a[N * row + j];
+                const uint32_t cc = code[prev] | ((uint32_t)j << (3 * row));
+                const bool take = first | (cand > v);
+                v = take ? cand : v;
+                c = take ? cc : c;
+                first = false;
+            }
+            best[mask] = v;
+            code[mask] = c;
+        }
+    }
+    const uint32_t perm = code[(1 << N) - 1];
+    // w[c][j]: length of the edge c -> j (the row owning column c moves to j)
+    float w[N][N];
+#pragma unroll
+    for (int c = 0; c < N; ++c) {
+        float row[N];
+#pragma unroll
+        for (int j = 0; j < N; ++j) row[j] = a[N * (N - 1) + j];
+#pragma unroll
+        for (int r = N - 2; r >= 0; --r) {
+            const bool owns = ((perm >> (3 * r)) & 7u) == (uint32_t)c;
+#pragma unroll
+            for (int j = 0; j < N; ++j) row[j] = owns ? a[N * r + j] : row[j];
+        }
+#pragma unroll
+        for (int j = 0; j < N; ++j) w[c][j] = row[c] - row[j];
+    }
+    float to[N - 1], from[N - 1];
+#pragma unroll
+    for (int j = 0; j < N - 1; ++j) {
+        to[j] = w[N - 1][j];
+        from[j] = w[j][N - 1];
+    }
+#pragma unroll
+    for (int round = 0; round < N - 2; ++round) {
+#pragma unroll
+        for (int j = 0; j < N - 1; ++j) {
+#pragma unroll
+            for (int k = 0; k < N - 1; ++k) {
+                if (k == j) continue;
+                to[j] = mhc_min(to[j], to[k] + w[k][j]);
+                from[j] = mhc_min(from[j], w[j][k] + from[k]);
+            }
+        }
+    }
+    float h[N];
+#pragma unroll
+    for (int j = 0; j < N - 1; ++j) h[j] = 0.5f * (to[j] - from[j]);
+    h[N - 1] = 0.f;
+#pragma unroll
+    for (int sweep = 0; sweep < kBalanceSweeps; ++sweep) {
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            float in = __builtin_inff(), out = __builtin_inff();
+#pragma unroll
+            for (int k = 0; k < N; ++k) {
+                if (k == j) continue;
+                in = mhc_min(in, w[k][j] + h[k]);
+                out = mhc_min(out, w[j][k] - h[k]);
+            }
+            h[j] = 0.5f * (in - out);
+        }
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < N - 1; ++j) {
+        h[j] -= h[N - 1];
+        sum += mhc_abs(h[j]);
+    }
+    const bool finite = sum < __builtin_inff();  // NaN, +-inf, overflow: g = 0
+#pragma unroll
+    for (int j = 0; j < N - 1; ++j) g[j] = finite ? h[j] : 0.f;
+}
+
 template <int N>
 MHC_DEV void newton_init_n(NewtonLaneN<N>& s, const float* a_nat, const SolverOpts& o)
 {
@@ -219,8 +333,12 @@ MHC_DEV void newton_init_n(NewtonLaneN<N>& s, const float* a_nat, const SolverOp
     s.slow = !s.kfast;
 #pragma unroll
     for (int e = 0; e < N * N; ++e) s.k[e] = mhc_exp2(s.a[e]);
+    if constexpr (N >= 3 && N <= kAssignStartMaxN) {
+        assignment_start_n<N>(s.a, s.g);
+    } else {
 #pragma unroll
-    for (int j = 0; j < N - 1; ++j) s.g[j] = 0.f;
+        for (int j = 0; j < N - 1; ++j) s.g[j] = 0.f;
+    }
     s.newton = 0;
     s.trials = 0;
     s.grow = 1.f;
@@ -229,7 +347,10 @@ MHC_DEV void newton_init_n(NewtonLaneN<N>& s, const float* a_nat, const SolverOp
     s.res = E.res;
     s.done = s.res <= o.tol;
     s.code = 0;
-    const int warm = o.warm_sweeps < 0 ? 1 : o.warm_sweeps;  // -1: one sweep from g = 0
+    // -1: one sweep, after either start.  After the assignment start it
+    // still pays for small logits (6x6 N(0,1): slowest lane of a wave 3.9
+    // Newton trials without it, 3.0 with it), unlike for n = 4.
+    const int warm = o.warm_sweeps < 0 ? 1 : o.warm_sweeps;
     for (int sw = 0; sw < warm; ++sw) {
         const float ln = mhc_log2(mhc_max(E.c[N - 1], kMinMass));
         float ng[N - 1];

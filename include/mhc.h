@@ -90,8 +90,7 @@ typedef struct {
                             (the default) for the solver's own choice: none
                             for n = 4, whose start (from the assignment
                             problem) leaves nothing for a sweep to gain, and
-                            one for the general-n solver, which starts from
-                            g = 0 */
+                            one for the general-n solver */
 } mhc_proj_opts;
 
 /* Iteration codes written to the optional `iters` output. */
