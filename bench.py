@@ -63,8 +63,8 @@ MEASURED = {
     "birkhoff_bwd_131072_cfg2": {"fetch": 16848627, "write": 8388608, "valu": 976896, "trans": 26624, "sha": "68f0e2fece420514"},
     "birkhoff_fwd_1048576_cfg3": {"fetch": 67251208, "write": 67116138, "valu": 21246384, "trans": 1144634, "sha": "68f0e2fece420514"},
     "birkhoff_bwd_1048576_cfg3": {"fetch": 134274402, "write": 67108864, "valu": 7485440, "trans": 198656, "sha": "68f0e2fece420514"},
-    "birkhoff_fwd_n8_131072_cfg2": {"fetch": 33927927, "write": 33555316, "valu": 22585748, "trans": 745229, "sha": "78084b7ec7982182"},
-    "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67447656, "write": 33554722, "valu": 6424576, "trans": 14336, "sha": "78084b7ec7982182"},
+    "birkhoff_fwd_n8_131072_cfg2": {"fetch": 33931703, "write": 33555311, "valu": 22585748, "trans": 745229, "sha": "a34ab5dc167fbe97"},
+    "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67447699, "write": 33555497, "valu": 6424576, "trans": 14336, "sha": "a34ab5dc167fbe97"},
     "stream_mix_fwd_16384x4x4096": {"fetch": 537991873, "write": 537927191, "valu": 25710592, "trans": 68608, "sha": "5e0a953206ecbe03"},
     "stream_mix_bwd_16384x4x4096": {"fetch": 1074729265, "write": 537959255, "valu": 50135040, "trans": 0, "sha": "5e0a953206ecbe03"},
     "layer_step_65536x4x7168": {"fetch": 30734967755, "write": 9469207667, "sha": "5215c1a5373b532c"},
