@@ -217,11 +217,38 @@ def time_projection(bp, torch, A_np, G_np, steps, warmup, solver="newton", recom
         fwd_fn(sets[0][0], solver=solver)  # eager work between replays
     for _ in range(2):  # warm replays
         g_step.replay()
-    total_ms = replay(g_step)
+    total_ms = replay(g_step)  # the timed region: exactly `steps` steps
     fwd_ms = replay(g_fwd) / steps
     bwd_ms = replay(g_bwd) / steps
+    # spread: five more replays of the step graph (not part of the headline)
+    spread = sorted(replay(g_step) / steps for _ in range(5))
+    # hot cache: every step on the same buffer set (reported apart, never the
+    # headline: the set fits in the 256 MB last-level cache)
+    g_hot = capture(lambda k: step(0))
+    g_hot.replay()
+    hot_ms = replay(g_hot) / steps
     return dict(total_ms=total_ms, fwd_ms=fwd_ms, bwd_ms=bwd_ms, nsets=nsets,
-                eager_ms_per_step=eager_ms / steps)
+                eager_ms_per_step=eager_ms / steps, step_ms_median=spread[2],
+                step_ms_min=spread[0], hot_ms_per_step=hot_ms)
+
+
+def copy_bandwidth(torch, mib=256, reps=20):
+    """Read+write GB/s of a plain device copy of `mib` MiB, the practical
+    streaming ceiling the kernels' algorithmic GB/s is compared with."""
+    n = mib * (1 << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    y.copy_(x)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(reps):
+        y.copy_(x)
+    stop.record()
+    torch.cuda.synchronize()
+    gbs = 2 * n * 4 * reps / (start.elapsed_time(stop) / 1e3) / 1e9
+    del x, y
+    return gbs
 
 
 def copy_probe(torch, mib):
@@ -249,7 +276,9 @@ def iteration_stats(bp, torch, A_np, n=4):
     wave_max = itc[:n].reshape(-1, 64).max(axis=1)
     return {"mean": float(itc.mean()), "wave_max_mean": float(wave_max.mean()),
             "useful_frac": float(itc[:n].mean() / wave_max.mean()) if wave_max.mean() > 0 else 1.0,
-            "not_converged": int((~ok).sum())}
+            "not_converged": int((~ok).sum()),
+            "hist_matrix": np.bincount(it[ok], minlength=1).tolist(),
+            "hist_wave_max": np.bincount(wave_max, minlength=1).tolist()}
 
 
 def bench_projection(args, bp, torch, config):
@@ -286,6 +315,7 @@ def bench_projection(args, bp, torch, config):
     fwd_gbs = fwd_bytes * B / (fwd_avg / 1e3) / 1e9
     bwd_gbs = bwd_bytes * B / (bwd_avg / 1e3) / 1e9
     step_gbs = (fwd_bytes + bwd_bytes) * B / (ms / 1e3) / 1e9
+    copy_gbs = copy_bandwidth(torch)
     tag = "" if n == 4 else f"_n{n}"
     m_fwd = measured(f"birkhoff_fwd{tag}_{B}_cfg{config}")
     m_bwd = None if args.recompute else measured(f"birkhoff_bwd{tag}_{B}_cfg{config}")
@@ -317,10 +347,14 @@ def bench_projection(args, bp, torch, config):
         "roofline": roofline,
         "hbm": {"fwd_GBs": fwd_gbs, "bwd_GBs": bwd_gbs, "step_GBs": step_gbs,
                 "step_frac": step_gbs / HBM_PEAK_GBS, "bwd_frac": bwd_gbs / HBM_PEAK_GBS,
+                "copy_GBs": copy_gbs, "step_frac_of_copy": step_gbs / copy_gbs,
                 "fwd_traffic": m_fwd["fetch"] + m_fwd["write"] if m_fwd else None,
                 "bwd_traffic": m_bwd["fetch"] + m_bwd["write"] if m_bwd else None},
         "kernels": {"fwd_us": fwd_avg * 1e3, "bwd_us": bwd_avg * 1e3, "launch": "hip graph replay",
-                    "eager_us_per_step": r["eager_ms_per_step"] * 1e3},
+                    "eager_us_per_step": r["eager_ms_per_step"] * 1e3,
+                    "step_us_median_of_5": r["step_ms_median"] * 1e3,
+                    "step_us_min_of_5": r["step_ms_min"] * 1e3,
+                    "hot_us_per_step": r["hot_ms_per_step"] * 1e3},
         "valu": valu,
         "iters": iteration_stats(bp, torch, A, n),
     }
