@@ -209,6 +209,13 @@ MHC_DEV void newton_direction_n(const EvalN<N>& E, float* d, float& slope, float
 // 3 bits per row); larger n would need more registers than a lane has left.
 constexpr int kAssignStartMaxN = 6;
 
+// Step-growth threshold of the general-n solver (see kFar in proj4.h).  It
+// stays at 0.25 for every n: from g = 0 (n = 7, 8) drifts are long and a
+// lower threshold catches them a step earlier, and after the assignment
+// start the 4x4 value 0.35 measured no better (5x5 forward 13.94 against
+// 13.96 us) or worse (6x6: 20.23 against 19.88 us).
+constexpr float kFarN = 0.25f;
+
 constexpr int popcount_c(int m) { return m == 0 ? 0 : (m & 1) + popcount_c(m >> 1); }
 
 // Starting potentials g_0..g_{n-2} (base 2, g_{n-1} = 0) from the assignment
@@ -405,7 +412,7 @@ MHC_DEV void newton_step_n(NewtonLaneN<N>& s, const SolverOpts& o)
     // (no residual-progress condition here: with more columns the residual
     // stalls in the drift too, and at n = 8 the condition cost convergence)
     const bool first = (s.trials == 0) & (s.t >= s.grow);
-    const bool far = first & (dphi <= kFar * s.slope);
+    const bool far = first & (dphi <= kFarN * s.slope);
     const bool short_of_min = first & (dphi < 0.f);
     const float grow_far = mhc_pin(mhc_min(2.f * s.grow, kMaxGrow));
     const float grow_else = mhc_pin(short_of_min ? s.grow : 1.f);
