@@ -59,15 +59,15 @@ KERNEL_SOURCES = {
     "layer": ("devmath.h", "proj4.h", "kernels.h", "layer.hip"),
 }
 MEASURED = {
-    "birkhoff_fwd_131072_cfg2": {"fetch": 8535295, "write": 8389412, "valu": 2777594, "trans": 150185, "sha": "68f0e2fece420514"},
-    "birkhoff_bwd_131072_cfg2": {"fetch": 16848627, "write": 8388608, "valu": 976896, "trans": 26624, "sha": "68f0e2fece420514"},
-    "birkhoff_fwd_1048576_cfg3": {"fetch": 67251208, "write": 67116138, "valu": 21246384, "trans": 1144634, "sha": "68f0e2fece420514"},
-    "birkhoff_bwd_1048576_cfg3": {"fetch": 134274402, "write": 67108864, "valu": 7485440, "trans": 198656, "sha": "68f0e2fece420514"},
-    "birkhoff_fwd_n8_131072_cfg2": {"fetch": 33931703, "write": 33555311, "valu": 22585748, "trans": 745229, "sha": "a34ab5dc167fbe97"},
-    "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67447699, "write": 33555497, "valu": 6424576, "trans": 14336, "sha": "a34ab5dc167fbe97"},
-    "stream_mix_fwd_16384x4x4096": {"fetch": 537991873, "write": 537927191, "valu": 25710592, "trans": 68608, "sha": "5e0a953206ecbe03"},
-    "stream_mix_bwd_16384x4x4096": {"fetch": 1074729265, "write": 537959255, "valu": 50135040, "trans": 0, "sha": "5e0a953206ecbe03"},
-    "layer_step_65536x4x7168": {"fetch": 30734967755, "write": 9469207667, "sha": "5215c1a5373b532c"},
+    "birkhoff_fwd_131072_cfg2": {"fetch": 8535161, "write": 8389041, "valu": 2704820, "trans": 145928, "sha": "c1f901d592a62d64"},
+    "birkhoff_bwd_131072_cfg2": {"fetch": 16848637, "write": 8388608, "valu": 976896, "trans": 26624, "sha": "c1f901d592a62d64"},
+    "birkhoff_fwd_1048576_cfg3": {"fetch": 67251143, "write": 67113398, "valu": 20974751, "trans": 1128750, "sha": "c1f901d592a62d64"},
+    "birkhoff_bwd_1048576_cfg3": {"fetch": 134274346, "write": 67108864, "valu": 7485440, "trans": 198656, "sha": "c1f901d592a62d64"},
+    "birkhoff_fwd_n8_131072_cfg2": {"fetch": 33931517, "write": 33554885, "valu": 22585728, "trans": 745229, "sha": "e35a87cd63a64e60"},
+    "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67447574, "write": 33555250, "valu": 6424576, "trans": 14336, "sha": "e35a87cd63a64e60"},
+    "stream_mix_fwd_16384x4x4096": {"fetch": 537991389, "write": 537925731, "valu": 25710592, "trans": 68608, "sha": "c9ed36a327de060d"},
+    "stream_mix_bwd_16384x4x4096": {"fetch": 1074732717, "write": 537938790, "valu": 50135040, "trans": 0, "sha": "c9ed36a327de060d"},
+    "layer_step_65536x4x7168": {"fetch": 30709885947, "write": 9469220960, "sha": "e44e2104e41f30c0"},
 }
 
 
