@@ -102,6 +102,10 @@ def test_config2_full(gpu_lib):
     assert np.abs(P64.sum(-2) - 1).max() <= SUM_TOL
     flagged = np.nonzero(it == 255)[0]
     assert flagged.size <= 0.001 * A.shape[0], f"{flagged.size} unconverged"
+    # from the assignment-problem start no matrix needs more than 5 Newton
+    # iterations in a CPU replay of the kernel code (13 from g = 0 and a
+    # Sinkhorn sweep); the bound leaves room for rounding differences
+    assert it[it != 255].max() <= 7, f"{it[it != 255].max()} Newton iterations"
     # gradients of a projection have zero row and column sums
     assert np.abs(dA.astype(np.float64).sum(-1)).max() <= 1e-4
     idx = _sample(A.shape[0], 12288, 7, must=flagged)
