@@ -59,10 +59,10 @@ KERNEL_SOURCES = {
     "layer": ("devmath.h", "proj4.h", "kernels.h", "layer.hip"),
 }
 MEASURED = {
-    "birkhoff_fwd_131072_cfg2": {"fetch": 8535161, "write": 8389041, "valu": 2704820, "trans": 145928, "sha": "c1f901d592a62d64"},
-    "birkhoff_bwd_131072_cfg2": {"fetch": 16848637, "write": 8388608, "valu": 976896, "trans": 26624, "sha": "c1f901d592a62d64"},
-    "birkhoff_fwd_1048576_cfg3": {"fetch": 67251143, "write": 67113398, "valu": 20974751, "trans": 1128750, "sha": "c1f901d592a62d64"},
-    "birkhoff_bwd_1048576_cfg3": {"fetch": 134274346, "write": 67108864, "valu": 7485440, "trans": 198656, "sha": "c1f901d592a62d64"},
+    "birkhoff_fwd_131072_cfg2": {"fetch": 8540263, "write": 8389041, "valu": 2704820, "trans": 145928, "sha": "7b729b69dbaa4dff"},
+    "birkhoff_bwd_131072_cfg2": {"fetch": 16804870, "write": 8388701, "valu": 1122304, "trans": 24576, "sha": "7b729b69dbaa4dff"},
+    "birkhoff_fwd_1048576_cfg3": {"fetch": 67256146, "write": 67112613, "valu": 20974751, "trans": 1128750, "sha": "7b729b69dbaa4dff"},
+    "birkhoff_bwd_1048576_cfg3": {"fetch": 134230324, "write": 67109064, "valu": 8978432, "trans": 196608, "sha": "7b729b69dbaa4dff"},
     "birkhoff_fwd_n8_131072_cfg2": {"fetch": 33931517, "write": 33554885, "valu": 22585728, "trans": 745229, "sha": "e35a87cd63a64e60"},
     "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67447574, "write": 33555250, "valu": 6424576, "trans": 14336, "sha": "e35a87cd63a64e60"},
     "stream_mix_fwd_16384x4x4096": {"fetch": 537991389, "write": 537925731, "valu": 25710592, "trans": 68608, "sha": "c9ed36a327de060d"},
