@@ -120,9 +120,21 @@ def cpu_baseline_projection(A, G, n_sample, label):
     with ctx.Pool(cores) as pool:
         done = sum(pool.map(_cpu_worker, work))
     dt = time.perf_counter() - t0
+    # one process alone, on the first 16384 matrices
+    n1 = min(16384, A.shape[0])
+    t1 = time.perf_counter()
+    _cpu_worker((A[:n1], G[:n1]))
+    dt1 = time.perf_counter() - t1
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # threadpoolctl missing: report unknown
+        blas = None
     return {"value": done / dt, "unit": "projections/s", "cores": cores, "kind": "oracle",
             "sample": f"{done} matrices ({done / A.shape[0]:g} passes over the {A.shape[0]} "
-                      f"{label} batch), fwd+bwd, float64, {dt:.1f} s wall on {cores} processes"}
+                      f"{label} batch), fwd+bwd, float64, {dt:.1f} s wall on {cores} processes",
+            "single_core": {"value": n1 / dt1, "sample": f"first {n1} matrices, one process"},
+            "blas_threads": blas}
 
 
 def time_projection(bp, torch, A_np, G_np, steps, warmup, solver="newton", recompute=False, n=4):
