@@ -59,15 +59,16 @@ KERNEL_SOURCES = {
     "layer": ("devmath.h", "proj4.h", "kernels.h", "layer.hip"),
 }
 MEASURED = {
-    "birkhoff_fwd_131072_cfg2": {"fetch": 8540263, "write": 8389041, "valu": 2704820, "trans": 145928, "sha": "7b729b69dbaa4dff"},
-    "birkhoff_bwd_131072_cfg2": {"fetch": 16804870, "write": 8388701, "valu": 1122304, "trans": 24576, "sha": "7b729b69dbaa4dff"},
-    "birkhoff_fwd_1048576_cfg3": {"fetch": 67256146, "write": 67112613, "valu": 20974751, "trans": 1128750, "sha": "7b729b69dbaa4dff"},
-    "birkhoff_bwd_1048576_cfg3": {"fetch": 134230324, "write": 67109064, "valu": 8978432, "trans": 196608, "sha": "7b729b69dbaa4dff"},
-    "birkhoff_fwd_n8_131072_cfg2": {"fetch": 33931517, "write": 33554885, "valu": 22585728, "trans": 745229, "sha": "e35a87cd63a64e60"},
-    "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67447574, "write": 33555250, "valu": 6424576, "trans": 14336, "sha": "e35a87cd63a64e60"},
-    "stream_mix_fwd_16384x4x4096": {"fetch": 537991389, "write": 537925731, "valu": 25710592, "trans": 68608, "sha": "c9ed36a327de060d"},
-    "stream_mix_bwd_16384x4x4096": {"fetch": 1074732717, "write": 537938790, "valu": 50135040, "trans": 0, "sha": "c9ed36a327de060d"},
-    "layer_step_65536x4x7168": {"fetch": 30709885947, "write": 9469220960, "sha": "e44e2104e41f30c0"},
+    "birkhoff_fwd_131072_cfg2": {"fetch": 8543362, "write": 8389041, "valu": 2704820, "trans": 145928, "sha": "aab674bf95fec978"},
+    "birkhoff_bwd_131072_cfg2": {"fetch": 16805875, "write": 8388673, "valu": 1122304, "trans": 24576, "sha": "aab674bf95fec978"},
+    "birkhoff_fwd_1048576_cfg3": {"fetch": 67259328, "write": 67112793, "valu": 20974751, "trans": 1128750, "sha": "aab674bf95fec978"},
+    "birkhoff_bwd_1048576_cfg3": {"fetch": 134231550, "write": 67109210, "valu": 8978432, "trans": 196608, "sha": "aab674bf95fec978"},
+    "birkhoff_fwd_n8_131072_cfg2": {"fetch": 33931449, "write": 33554893, "valu": 22585728, "trans": 745229, "sha": "c64e2b5e6d28525f"},
+    "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67447363, "write": 33555117, "valu": 6424576, "trans": 14336, "sha": "c64e2b5e6d28525f"},
+    "birkhoff_fwd_bwd_131072_cfg2": {"fetch": 16952460, "write": 16777251, "valu": 3243424, "trans": 152072, "sha": "aab674bf95fec978"},
+    "stream_mix_fwd_16384x4x4096": {"fetch": 537990608, "write": 537927767, "valu": 25710592, "trans": 68608, "sha": "7a25a3c96bcee9e9"},
+    "stream_mix_bwd_16384x4x4096": {"fetch": 1074731216, "write": 537963770, "valu": 50135040, "trans": 0, "sha": "7a25a3c96bcee9e9"},
+    "layer_step_65536x4x7168": {"fetch": 30725726804, "write": 9469211162, "sha": "1e39f47d32ca8a27"},
 }
 
 
@@ -137,7 +138,8 @@ def cpu_baseline_projection(A, G, n_sample, label):
             "blas_threads": blas}
 
 
-def time_projection(bp, torch, A_np, G_np, steps, warmup, solver="newton", recompute=False, n=4):
+def time_projection(bp, torch, A_np, G_np, steps, warmup, solver="newton", recompute=False, n=4,
+                    fused=False):
     """Rotate over buffer sets and time `steps` fwd+bwd steps back to back,
     then `steps` forward launches alone and `steps` backward launches alone.
 
@@ -162,10 +164,15 @@ def time_projection(bp, torch, A_np, G_np, steps, warmup, solver="newton", recom
 
     def fwd(k):
         A, P, G, dA = sets[k % nsets]
-        fwd_fn(A, out=P, solver=solver)
+        if fused:  # P and dA in one launch
+            bp.birkhoff_fwd_bwd(A, G, out_P=P, out_grad=dA, solver=solver)
+        else:
+            fwd_fn(A, out=P, solver=solver)
 
     def bwd(k):
         A, P, G, dA = sets[k % nsets]
+        if fused:
+            return
         if recompute:
             bp.birkhoff_bwd_recompute(A, G, out=dA, solver=solver)
         else:
@@ -208,14 +215,18 @@ def time_projection(bp, torch, A_np, G_np, steps, warmup, solver="newton", recom
     for k in range(warmup):
         step(k)
     eager_ms = eager(step)
-    g_step, g_fwd, g_bwd = capture(step), capture(fwd), capture(bwd)
+    g_step, g_fwd = capture(step), capture(fwd)
+    g_bwd = None if fused else capture(bwd)  # fused: nothing left to time apart
     # replays must reproduce the eager results exactly (deterministic kernels);
     # the captured steps write the first min(steps, nsets) buffer sets
     touched = sets[:min(steps, nsets)]
     ref = []
     for A, P, G, dA in touched:
-        Pe = fwd_fn(A, solver=solver)
-        dAe = bp.birkhoff_bwd_recompute(A, G, solver=solver) if recompute else bwd_fn(Pe, G)
+        if fused:
+            Pe, dAe = bp.birkhoff_fwd_bwd(A, G, solver=solver)
+        else:
+            Pe = fwd_fn(A, solver=solver)
+            dAe = bp.birkhoff_bwd_recompute(A, G, solver=solver) if recompute else bwd_fn(Pe, G)
         ref.append((Pe, dAe))
     for _ in range(2):
         for A, P, G, dA in touched:
@@ -231,7 +242,7 @@ def time_projection(bp, torch, A_np, G_np, steps, warmup, solver="newton", recom
         g_step.replay()
     total_ms = replay(g_step)  # the timed region: exactly `steps` steps
     fwd_ms = replay(g_fwd) / steps
-    bwd_ms = replay(g_bwd) / steps
+    bwd_ms = 0.0 if fused else replay(g_bwd) / steps
     # spread: five more replays of the step graph (not part of the headline)
     spread = sorted(replay(g_step) / steps for _ in range(5))
     # hot cache: every step on the same buffer set (reported apart, never the
@@ -315,35 +326,42 @@ def bench_projection(args, bp, torch, config):
         G = W.grad_batch(A.shape[0], 1)
         label = "N(0,1)"
     B = A.shape[0]
-    if args.recompute and n != 4:
-        raise SystemExit("--recompute is for 4x4 matrices")
-    r = time_projection(bp, torch, A, G, args.steps, args.warmup, recompute=args.recompute, n=n)
+    if (args.recompute or args.fused) and n != 4:
+        raise SystemExit("--recompute and --fused are for 4x4 matrices")
+    if args.recompute and args.fused:
+        raise SystemExit("--recompute and --fused exclude each other")
+    r = time_projection(bp, torch, A, G, args.steps, args.warmup, recompute=args.recompute, n=n,
+                        fused=args.fused)
     ms = r["total_ms"] / args.steps
     fwd_avg = float(r["fwd_ms"])
     bwd_avg = float(r["bwd_ms"])
     value = B / (ms / 1e3)
     fwd_bytes = FWD_BYTES * n * n // 16
     bwd_bytes = BWD_BYTES * n * n // 16  # recompute: logits and dL/dP in, dL/dA out -- the same
+    if args.fused:  # one kernel: logits and dL/dP in, P and dL/dA out
+        fwd_bytes, bwd_bytes = 2 * FWD_BYTES, 0
     fwd_gbs = fwd_bytes * B / (fwd_avg / 1e3) / 1e9
-    bwd_gbs = bwd_bytes * B / (bwd_avg / 1e3) / 1e9
+    bwd_gbs = bwd_bytes * B / (bwd_avg / 1e3) / 1e9 if bwd_avg > 0 else None
     step_gbs = (fwd_bytes + bwd_bytes) * B / (ms / 1e3) / 1e9
     copy_gbs = copy_bandwidth(torch)
     tag = "" if n == 4 else f"_n{n}"
-    m_fwd = measured(f"birkhoff_fwd{tag}_{B}_cfg{config}")
-    m_bwd = None if args.recompute else measured(f"birkhoff_bwd{tag}_{B}_cfg{config}")
+    fwd_key = f"birkhoff_fwd_bwd_{B}_cfg{config}" if args.fused else f"birkhoff_fwd{tag}_{B}_cfg{config}"
+    kname = "birkhoff_fwd_bwd (fused Newton + backward)" if args.fused else "birkhoff_fwd (Newton)"
+    m_fwd = measured(fwd_key)
+    m_bwd = None if (args.recompute or args.fused) else measured(f"birkhoff_bwd{tag}_{B}_cfg{config}")
     # the forward solve is bound by vector-ALU issue (transcendental-heavy
     # Newton iterations), not by its 128 bytes per matrix
     if m_fwd is not None:
         slots = m_fwd["valu"] + (TRANS_SLOTS - 1) * m_fwd["trans"]
         achieved = slots / (fwd_avg / 1e3)
-        roofline = {"bound": "alu", "kernel": "birkhoff_fwd (Newton)", "achieved": achieved,
+        roofline = {"bound": "alu", "kernel": kname, "achieved": achieved,
                     "peak": VALU_PEAK_SLOTS, "unit": "wave64 VALU issue slots/s",
                     "frac": achieved / VALU_PEAK_SLOTS,
                     "traffic": m_fwd["fetch"] + m_fwd["write"]}
         valu = {"instructions_per_launch": m_fwd["valu"], "transcendental": m_fwd["trans"],
                 "issue_slots_per_launch": slots, "slots_per_matrix": slots / B}
     else:
-        roofline = {"bound": "alu", "kernel": "birkhoff_fwd (Newton)", "achieved": None,
+        roofline = {"bound": "alu", "kernel": kname, "achieved": None,
                     "peak": VALU_PEAK_SLOTS, "unit": "wave64 VALU issue slots/s", "frac": None,
                     "traffic": None, "note": "kernel changed since its counters were taken"}
         valu = None
@@ -354,11 +372,13 @@ def bench_projection(args, bp, torch, config):
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"birkhoff fwd+bwd, {B} {n}x{n} fp32 matrices {label}",
                    "batch": B, "n": n, "solver": "newton", "tol": 1e-6,
-                   "backward": "recompute" if args.recompute else "from P",
+                   "backward": ("recompute" if args.recompute else
+                                "fused with the forward (dL/dP given)" if args.fused else "from P"),
                    "buffer_sets": r["nsets"]},
         "roofline": roofline,
         "hbm": {"fwd_GBs": fwd_gbs, "bwd_GBs": bwd_gbs, "step_GBs": step_gbs,
-                "step_frac": step_gbs / HBM_PEAK_GBS, "bwd_frac": bwd_gbs / HBM_PEAK_GBS,
+                "step_frac": step_gbs / HBM_PEAK_GBS,
+                "bwd_frac": bwd_gbs / HBM_PEAK_GBS if bwd_gbs is not None else None,
                 "copy_GBs": copy_gbs, "step_frac_of_copy": step_gbs / copy_gbs,
                 "fwd_traffic": m_fwd["fetch"] + m_fwd["write"] if m_fwd else None,
                 "bwd_traffic": m_bwd["fetch"] + m_bwd["write"] if m_bwd else None},
@@ -499,6 +519,10 @@ def main():
                     help="configs 1-2: n x n matrices (1..8) through mhc_birkhoff_fwd_n/bwd_n")
     ap.add_argument("--mix-bwd", action="store_true",
                     help="config 4: time the standalone stream-mix backward instead")
+    ap.add_argument("--fused", action="store_true",
+                    help="configs 1-3, 4x4: time mhc_birkhoff_fwd_bwd, P and the gradient in one "
+                         "launch for a dL/dP known at forward time (not a training step; never "
+                         "the headline)")
     ap.add_argument("--recompute", action="store_true",
                     help="configs 1-3: backward by mhc_birkhoff_bwd_recompute (logits and "
                          "dL/dP in, the projection solved again; P not kept)")

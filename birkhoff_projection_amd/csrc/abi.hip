@@ -138,6 +138,38 @@ mhc_status mhc_birkhoff_bwd_recompute(const float* logits, const float* grad_P,
                     "birkhoff_bwd_recompute launch");
 }
 
+mhc_status mhc_birkhoff_fwd_bwd(const float* logits, const float* grad_P, float* P,
+                                float* grad_logits, int64_t B, const mhc_proj_opts* opts,
+                                uint8_t* iters, void* stream)
+{
+    if (B < 0 || B > kMaxBatch) return fail(MHC_ERR_INVALID_ARGUMENT, "B=%lld out of range", (long long)B);
+    mhc::SolverOpts o;
+    const mhc_status s = check_opts(opts, &o);
+    if (s != MHC_OK) return s;
+    if (B == 0) return ok();
+    if (logits == nullptr || grad_P == nullptr || P == nullptr || grad_logits == nullptr)
+        return fail(MHC_ERR_INVALID_ARGUMENT, "logits, grad_P, P and grad_logits must not be NULL");
+    if (!aligned16(logits) || !aligned16(grad_P) || !aligned16(P) || !aligned16(grad_logits))
+        return fail(MHC_ERR_INVALID_ARGUMENT,
+                    "logits, grad_P, P and grad_logits must be 16-byte aligned");
+    const size_t bytes = (size_t)B * 64;
+    if (P != logits && overlap(logits, bytes, P, bytes))
+        return fail(MHC_ERR_INVALID_ARGUMENT, "P partially overlaps logits");
+    if (grad_logits != grad_P && overlap(grad_P, bytes, grad_logits, bytes))
+        return fail(MHC_ERR_INVALID_ARGUMENT, "grad_logits partially overlaps grad_P");
+    if (overlap(P, bytes, grad_P, bytes) || overlap(P, bytes, grad_logits, bytes))
+        return fail(MHC_ERR_INVALID_ARGUMENT, "P overlaps grad_P or grad_logits");
+    if (overlap(grad_logits, bytes, logits, bytes))
+        return fail(MHC_ERR_INVALID_ARGUMENT, "grad_logits overlaps logits");
+    if (iters != nullptr &&
+        (overlap(iters, (size_t)B, logits, bytes) || overlap(iters, (size_t)B, grad_P, bytes) ||
+         overlap(iters, (size_t)B, P, bytes) || overlap(iters, (size_t)B, grad_logits, bytes)))
+        return fail(MHC_ERR_INVALID_ARGUMENT, "iters overlaps logits, grad_P, P or grad_logits");
+    return launched(mhc::launch_birkhoff_fwd_bwd(logits, grad_P, P, grad_logits, iters, B, o,
+                                                (hipStream_t)stream),
+                    "birkhoff_fwd_bwd launch");
+}
+
 static bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
 mhc_status mhc_birkhoff_fwd_n(const float* logits, float* P, int64_t B, int32_t n,

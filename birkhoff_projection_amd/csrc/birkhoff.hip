@@ -67,16 +67,25 @@ __global__ __launch_bounds__(kBlock) void birkhoff_bwd_kernel(const float4* __re
     if (ok) mhc_store_stream(dA + r, make_float4(o[0], o[1], o[2], o[3]));
 }
 
-// Recompute backward: lane per matrix, the forward solve redone in
-// registers and the implicit-differentiation gradient formed from that P
-// (matrix-per-lane form of the backward), records staged as in the forward.
-// logits or G may be the same buffer as dA: a wave reads all of its matrices
-// from both before writing.
-template <int SOLVER>
-__global__ __launch_bounds__(kBlock) void birkhoff_bwd_recompute_kernel(const float* logits,
-                                                                        const float* G,
-                                                                        float* dA, int64_t B,
-                                                                        SolverOpts o)
+// Solve and differentiate in one pass: lane per matrix, the projection
+// solved in registers and the implicit-differentiation gradient formed from
+// that P while it is still there (matrix-per-lane form of the backward),
+// records staged as in the forward.  Two entry points use it:
+//  * the recompute backward (WRITE_P false): P is not stored at all, the
+//    forward solve is simply redone;
+//  * the fused forward + backward (WRITE_P true), for when dL/dP is known
+//    when the projection is computed: P (and the iteration codes) are
+//    stored as well, 256 bytes per matrix in one launch instead of 320 in
+//    two.
+// A wave reads all of its matrices from logits and G before writing any, so
+// P may be the logits buffer and dA the G buffer (the ABI rejects the other
+// overlaps).
+template <int SOLVER, bool WRITE_P>
+__global__ __launch_bounds__(kBlock) void birkhoff_solve_bwd_kernel(const float* logits,
+                                                                    const float* G, float* P,
+                                                                    float* dA,
+                                                                    uint8_t* __restrict__ iters,
+                                                                    int64_t B, SolverOpts o)
 {
     __shared__ float tiles[kBlock / 64][stage_tile_floats<16>()];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -85,12 +94,11 @@ __global__ __launch_bounds__(kBlock) void birkhoff_bwd_recompute_kernel(const fl
     float a[16], g[16], p[16], d[16];
     load_records_v4<16>(logits, first, B, tiles[w], a, lane);
     load_records_v4<16>(G, first, B, tiles[w], g, lane);
-    if (SOLVER == 0)
-        project_newton(a, p, o);
-    else
-        project_sinkhorn(a, p, o);
+    const uint32_t it = SOLVER == 0 ? project_newton(a, p, o) : project_sinkhorn(a, p, o);
     project_bwd(p, g, d);
+    if (WRITE_P) store_records_v4<16>(P, first, B, tiles[w], p, lane);
     store_records_v4<16>(dA, first, B, tiles[w], d, lane);
+    if (WRITE_P && iters != nullptr && first + lane < B) iters[first + lane] = (uint8_t)it;
 }
 
 }  // namespace
@@ -124,11 +132,25 @@ hipError_t launch_birkhoff_bwd_recompute(const float* logits, const float* G, fl
 {
     const dim3 grid((unsigned)((B + kBlock - 1) / kBlock));
     if (o.solver == 0)
-        hipLaunchKernelGGL(birkhoff_bwd_recompute_kernel<0>, grid, dim3(kBlock), 0, stream,
-                           logits, G, dA, B, o);
+        hipLaunchKernelGGL((birkhoff_solve_bwd_kernel<0, false>), grid, dim3(kBlock), 0, stream,
+                           logits, G, nullptr, dA, nullptr, B, o);
     else
-        hipLaunchKernelGGL(birkhoff_bwd_recompute_kernel<1>, grid, dim3(kBlock), 0, stream,
-                           logits, G, dA, B, o);
+        hipLaunchKernelGGL((birkhoff_solve_bwd_kernel<1, false>), grid, dim3(kBlock), 0, stream,
+                           logits, G, nullptr, dA, nullptr, B, o);
+    return hipGetLastError();
+}
+
+hipError_t launch_birkhoff_fwd_bwd(const float* logits, const float* G, float* P, float* dA,
+                                   uint8_t* iters, int64_t B, const SolverOpts& o,
+                                   hipStream_t stream)
+{
+    const dim3 grid((unsigned)((B + kBlock - 1) / kBlock));
+    if (o.solver == 0)
+        hipLaunchKernelGGL((birkhoff_solve_bwd_kernel<0, true>), grid, dim3(kBlock), 0, stream,
+                           logits, G, P, dA, iters, B, o);
+    else
+        hipLaunchKernelGGL((birkhoff_solve_bwd_kernel<1, true>), grid, dim3(kBlock), 0, stream,
+                           logits, G, P, dA, iters, B, o);
     return hipGetLastError();
 }
 

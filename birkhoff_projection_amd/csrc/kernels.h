@@ -15,6 +15,9 @@ hipError_t launch_birkhoff_bwd(const float* P, const float* G, float* dA, int64_
                                hipStream_t stream);
 hipError_t launch_birkhoff_bwd_recompute(const float* logits, const float* G, float* dA, int64_t B,
                                          const SolverOpts& o, hipStream_t stream);
+hipError_t launch_birkhoff_fwd_bwd(const float* logits, const float* G, float* P, float* dA,
+                                   uint8_t* iters, int64_t B, const SolverOpts& o,
+                                   hipStream_t stream);
 // n x n projection for n in {1, 2, 3, 5, 6, 7, 8} (4 has its own kernels).
 hipError_t launch_birkhoff_fwd_n(const float* logits, float* P, uint8_t* iters, int64_t B, int n,
                                  const SolverOpts& o, hipStream_t stream);

@@ -145,6 +145,32 @@ def birkhoff_bwd_recompute(logits: torch.Tensor, grad_P: torch.Tensor, *, solver
     return dA
 
 
+def birkhoff_fwd_bwd(logits: torch.Tensor, grad_P: torch.Tensor, *, solver="newton",
+                     max_iters=None, tol=None, warm_sweeps=None, out_P=None, out_grad=None,
+                     return_iters=False):
+    """P and dL/dlogits in one pass, for when dL/dP is known when the
+    projection is computed (otherwise use birkhoff_fwd, then birkhoff_bwd).
+    out_P may be ``logits`` itself and out_grad ``grad_P`` itself."""
+    _need(logits, "logits", torch.float32, (4, 4))
+    _need(grad_P, "grad_P", torch.float32, (4, 4))
+    if logits.shape != grad_P.shape or logits.device != grad_P.device:
+        raise ValueError("logits and grad_P must match in shape and device")
+    P = torch.empty_like(logits) if out_P is None else out_P
+    dA = torch.empty_like(logits) if out_grad is None else out_grad
+    for t, name in ((P, "out_P"), (dA, "out_grad")):
+        _need(t, name, torch.float32, (4, 4))
+        if t.shape != logits.shape:
+            raise ValueError(f"{name} must have the shape of logits")
+    B = logits.numel() // 16
+    it = torch.empty(logits.shape[:-2], dtype=torch.uint8, device=logits.device) if return_iters else None
+    o = make_opts(solver, max_iters, tol, warm_sweeps)
+    with torch.cuda.device(logits.device):
+        check(lib().mhc_birkhoff_fwd_bwd(_ptr(logits), _ptr(grad_P), _ptr(P), _ptr(dA), B,
+                                         ctypes.byref(o), _ptr(it),
+                                         _stream(logits.device)))
+    return (P, dA, it) if return_iters else (P, dA)
+
+
 class BirkhoffProjection(torch.autograd.Function):
     """Autograd wrapper.  By default it saves only P for the backward (nothing
     else from the forward solve is needed); with ``recompute`` it saves the

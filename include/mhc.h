@@ -13,6 +13,9 @@
  *   mhc_birkhoff_bwd_recompute
  *                       the same gradient from the logits alone (the forward
  *                       solve is redone in registers; P is not stored)
+ *   mhc_birkhoff_fwd_bwd
+ *                       projection and gradient in one pass, for when dL/dP
+ *                       is already known when the projection is computed
  *   mhc_stream_mix      out[t,i,:] = sum_j H[t,i,j] x[t,j,:], optionally with
  *                       the projection of H's logits fused in
  *   mhc_stream_mix_bwd  gradients of the stream mix
@@ -62,7 +65,9 @@
 extern "C" {
 #endif
 
-#define MHC_ABI_VERSION 1
+/* Version history: 1 first release; 2 adds mhc_birkhoff_fwd_bwd and makes
+ * -1 (the solver's own choice) the default of mhc_proj_opts.warm_sweeps. */
+#define MHC_ABI_VERSION 2
 
 typedef enum {
     MHC_OK = 0,
@@ -165,6 +170,31 @@ mhc_status mhc_birkhoff_bwd(const float* P, const float* grad_P, float* grad_log
 mhc_status mhc_birkhoff_bwd_recompute(const float* logits, const float* grad_P,
                                       float* grad_logits, int64_t B,
                                       const mhc_proj_opts* opts, void* stream);
+
+/* mhc_birkhoff_fwd_bwd -- P and dL/dA in one pass, when dL/dP is at hand.
+ *
+ * The last Newton Hessian is the matrix the implicit-differentiation
+ * backward needs (gist.science summary, section 2.2), so when the gradient
+ * dL/dP is already known at the time of the projection (a loss linear in P,
+ * a fixed upstream gradient, a benchmark) both results come from one solve
+ * kept in registers: P as mhc_birkhoff_fwd computes it and the gradient as
+ * mhc_birkhoff_bwd_recompute computes it.  Reads 128 bytes and writes 128 per
+ * matrix in one launch, against 128 + 192 in two for mhc_birkhoff_fwd then
+ * mhc_birkhoff_bwd.  In training, where dL/dP depends on P, use those two.
+ *
+ *   logits       [B,4,4] fp32, device, 16-byte aligned
+ *   grad_P       [B,4,4] fp32, device, 16-byte aligned
+ *   P            [B,4,4] fp32, device, 16-byte aligned, written; may alias
+ *                logits exactly, must not overlap grad_P or grad_logits
+ *   grad_logits  [B,4,4] fp32, device, 16-byte aligned, written; may alias
+ *                grad_P exactly, must not overlap logits or P
+ *   opts, iters  as for mhc_birkhoff_fwd (iters must not overlap any of the
+ *                four arrays)
+ *   B >= 0, stream as above.  Errors as for mhc_birkhoff_fwd.
+ */
+mhc_status mhc_birkhoff_fwd_bwd(const float* logits, const float* grad_P, float* P,
+                                float* grad_logits, int64_t B, const mhc_proj_opts* opts,
+                                uint8_t* iters, void* stream);
 
 /* mhc_birkhoff_fwd_n / mhc_birkhoff_bwd_n -- the projection and its gradient
  * for a batch of n x n matrices, 1 <= n <= 8.

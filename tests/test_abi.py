@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_strings(L):
-    assert L.mhc_abi_version() == 1
+    assert L.mhc_abi_version() == 2
     assert L.mhc_status_string(0) == b"ok"
     assert L.mhc_status_string(1) == b"invalid argument"
     assert L.mhc_status_string(2) == b"unsupported"
@@ -90,6 +90,37 @@ def test_bwd_argument_errors(L):
     # grad_logits may not overlap P at all
     assert L.mhc_birkhoff_bwd(FAKE, FAKE + 8192, FAKE, 3, None) == INVALID
     assert "overlaps P" in _err(L)
+
+
+def test_fwd_bwd_argument_errors(L):
+    """mhc_birkhoff_fwd_bwd: B = 0 is a no-op; NULL, misalignment and every
+    overlap other than P == logits and grad_logits == grad_P are rejected
+    before anything is enqueued (FAKE pointers are never dereferenced)."""
+    f = L.mhc_birkhoff_fwd_bwd
+    A, G, P, D = FAKE, FAKE + 8192, FAKE + 16384, FAKE + 24576
+    assert f(None, None, None, None, 0, None, None, None) == 0
+    assert f(A, G, P, D, -1, None, None, None) == INVALID
+    assert f(A, G, None, D, 3, None, None, None) == INVALID
+    assert "NULL" in _err(L)
+    assert f(A, G, P + 4, D, 3, None, None, None) == INVALID
+    assert "aligned" in _err(L)
+    assert f(A, G, A + 64, D, 3, None, None, None) == INVALID
+    assert "P partially overlaps logits" in _err(L)
+    assert f(A, G, P, G + 64, 3, None, None, None) == INVALID
+    assert "grad_logits partially overlaps grad_P" in _err(L)
+    assert f(A, G, G, D, 3, None, None, None) == INVALID
+    assert "P overlaps grad_P or grad_logits" in _err(L)
+    assert f(A, G, P, P, 3, None, None, None) == INVALID
+    assert "P overlaps grad_P or grad_logits" in _err(L)
+    assert f(A, G, P, A, 3, None, None, None) == INVALID
+    assert "grad_logits overlaps logits" in _err(L)
+    assert f(A, G, P, D, 3, None, ctypes.c_void_p(A + 16), None) == INVALID
+    assert "iters overlaps" in _err(L)
+    o = ProjOpts()
+    L.mhc_proj_opts_default(ctypes.byref(o))
+    o.warm_sweeps = -2
+    assert f(A, G, P, D, 3, ctypes.byref(o), None, None) == INVALID
+    assert "warm_sweeps" in _err(L)
 
 
 def test_bwd_recompute_argument_errors(L):

@@ -284,6 +284,42 @@ def test_bwd_recompute_alias_and_solver(gpu_lib):
     assert_bwd(dA, _bwd(gpu_lib, P, G).astype(np.float64), G, label="sinkhorn recompute")
 
 
+@pytest.mark.parametrize("kind", ["normal1", "normal10", "diag20"])
+@pytest.mark.parametrize("B", [1, 255, 1000])
+def test_fwd_bwd_fused(gpu_lib, kind, B):
+    """mhc_birkhoff_fwd_bwd: P is the forward's P (same solve; 2e-7 allows
+    for a different contraction of the inlined code) with the same iteration
+    codes, dA is the recompute backward's bit for bit (same kernel body), and
+    both match the oracle."""
+    print(f"fused fwd+bwd kind={kind} B={B}", flush=True)
+    A = W.logits_batch(kind, B, 300 + B)
+    G = W.grad_batch(B, 400 + B)
+    At, Gt = torch.from_numpy(A).cuda(), torch.from_numpy(G).cuda()
+    P, dA, it = gpu_lib.birkhoff_fwd_bwd(At, Gt, return_iters=True)
+    P_f, it_f = gpu_lib.birkhoff_fwd(At, return_iters=True)
+    dA_r = gpu_lib.birkhoff_bwd_recompute(At, Gt)
+    torch.cuda.synchronize()
+    assert (P - P_f).abs().max().item() <= 2e-7
+    assert (it == it_f).float().mean().item() >= 0.999
+    assert torch.equal(dA, dA_r)
+    ref = birkhoff_project(A.astype(np.float64))
+    assert_fwd(P.cpu().numpy(), ref, label=f"fused {kind} B={B}")
+    assert_bwd(dA.cpu().numpy(), birkhoff_project_bwd(ref, G.astype(np.float64)), G,
+               label=f"fused {kind} B={B}")
+
+
+def test_fwd_bwd_fused_alias(gpu_lib):
+    """P may be written over the logits and dA over grad_P."""
+    B = 777
+    A = W.logits_batch("normal10", B, 61)
+    G = W.grad_batch(B, 62)
+    At, Gt = torch.from_numpy(A).cuda(), torch.from_numpy(G).cuda()
+    P, dA = gpu_lib.birkhoff_fwd_bwd(At, Gt)
+    gpu_lib.birkhoff_fwd_bwd(At, Gt, out_P=At, out_grad=Gt)
+    torch.cuda.synchronize()
+    assert torch.equal(At, P) and torch.equal(Gt, dA)
+
+
 def test_autograd_recompute(gpu_lib):
     """birkhoff_project(recompute=True) keeps only the logits for backward and
     gives the same gradient as the default path to the backward bar."""

@@ -45,6 +45,11 @@ def test_projection_4x4_writes_only_its_batch(gpu_lib, B):
         full, head = _out(B, (4, 4))
         call(head)
         _check(full, B, label)
+    fullP, headP = _out(B, (4, 4))
+    fullD, headD = _out(B, (4, 4))
+    gpu_lib.birkhoff_fwd_bwd(A, G, out_P=headP, out_grad=headD)
+    _check(fullP, B, "fused fwd+bwd P")
+    _check(fullD, B, "fused fwd+bwd dA")
 
 
 @pytest.mark.parametrize("n", [2, 3, 5, 8])
