@@ -65,7 +65,7 @@ MEASURED = {
     "birkhoff_bwd_1048576_cfg3": {"fetch": 134231550, "write": 67109210, "valu": 8978432, "trans": 196608, "sha": "aab674bf95fec978"},
     "birkhoff_fwd_n8_131072_cfg2": {"fetch": 33931449, "write": 33554893, "valu": 22585728, "trans": 745229, "sha": "c64e2b5e6d28525f"},
     "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67447363, "write": 33555117, "valu": 6424576, "trans": 14336, "sha": "c64e2b5e6d28525f"},
-    "birkhoff_fwd_bwd_131072_cfg2": {"fetch": 16952460, "write": 16777251, "valu": 3243424, "trans": 152072, "sha": "aab674bf95fec978"},
+    "birkhoff_fwd_bwd_131072_cfg2": {"fetch": 16952581, "write": 16777269, "valu": 3243424, "trans": 152072, "sha": "aab674bf95fec978"},
     "stream_mix_fwd_16384x4x4096": {"fetch": 537990608, "write": 537927767, "valu": 25710592, "trans": 68608, "sha": "7a25a3c96bcee9e9"},
     "stream_mix_bwd_16384x4x4096": {"fetch": 1074731216, "write": 537963770, "valu": 50135040, "trans": 0, "sha": "7a25a3c96bcee9e9"},
     "layer_step_65536x4x7168": {"fetch": 30725726804, "write": 9469211162, "sha": "1e39f47d32ca8a27"},
