@@ -63,8 +63,8 @@ MEASURED = {
     "birkhoff_bwd_131072_cfg2": {"fetch": 16805875, "write": 8388673, "valu": 1122304, "trans": 24576, "sha": "aab674bf95fec978"},
     "birkhoff_fwd_1048576_cfg3": {"fetch": 67259328, "write": 67112793, "valu": 20974751, "trans": 1128750, "sha": "aab674bf95fec978"},
     "birkhoff_bwd_1048576_cfg3": {"fetch": 134231550, "write": 67109210, "valu": 8978432, "trans": 196608, "sha": "aab674bf95fec978"},
-    "birkhoff_fwd_n8_131072_cfg2": {"fetch": 33931449, "write": 33554893, "valu": 22585728, "trans": 745229, "sha": "c64e2b5e6d28525f"},
-    "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67447363, "write": 33555117, "valu": 6424576, "trans": 14336, "sha": "c64e2b5e6d28525f"},
+    "birkhoff_fwd_n8_131072_cfg2": {"fetch": 40971775, "write": 59769832, "valu": 22793498, "trans": 745229, "sha": "7fd179215a1335d3"},
+    "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67434629, "write": 33554973, "valu": 6424576, "trans": 14336, "sha": "7fd179215a1335d3"},
     "birkhoff_fwd_bwd_131072_cfg2": {"fetch": 16952581, "write": 16777269, "valu": 3243424, "trans": 152072, "sha": "aab674bf95fec978"},
     "stream_mix_fwd_16384x4x4096": {"fetch": 537990608, "write": 537927767, "valu": 25710592, "trans": 68608, "sha": "7a25a3c96bcee9e9"},
     "stream_mix_bwd_16384x4x4096": {"fetch": 1074731216, "write": 537963770, "valu": 50135040, "trans": 0, "sha": "7a25a3c96bcee9e9"},

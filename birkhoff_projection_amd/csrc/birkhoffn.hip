@@ -15,8 +15,14 @@ namespace {
 
 constexpr int kBlockN = 256;
 
+// At least two waves per SIMD: left to itself the compiler gives the 7x7 and
+// 8x8 Newton solves 276 and 306 registers (all 256 VGPRs plus AGPRs), one
+// wave per SIMD, so 131072 matrices run in two generations of lone waves.
+// Held to 256 the 7x7 solve needs no spill and the 8x8 one spills 204 bytes
+// to scratch, and still: 7x7 51.7 -> 41.1 us, 8x8 74.6 -> 62.7 us at 131072
+// matrices (same-process A/B, bit-identical output).  Smaller n already fit.
 template <int N, int SOLVER>
-__global__ __launch_bounds__(kBlockN) void birkhoff_fwd_n_kernel(const float* logits, float* P,
+__global__ __launch_bounds__(kBlockN) __attribute__((amdgpu_waves_per_eu(2))) void birkhoff_fwd_n_kernel(const float* logits, float* P,
                                                                  uint8_t* __restrict__ iters,
                                                                  int64_t B, SolverOpts o)
 {
