@@ -54,3 +54,37 @@ def test_mix_graph_replays(gpu_lib):
         assert torch.equal(y, ye), f"replay {rep}: out"
         gpu_lib.stream_mix(x[:10], logits=logits[:10])
         torch.cuda.synchronize()
+
+
+def test_fused_recompute_and_n8_graph_replays(gpu_lib):
+    """The fused forward + backward, the recompute backward and the 8x8
+    forward (whose kernel spills to scratch memory) in one captured graph."""
+    B = 3000
+    A = torch.from_numpy(W.logits_batch("normal10", B, 64)).cuda()
+    G = torch.from_numpy(W.grad_batch(B, 65)).cuda()
+    A8 = torch.from_numpy(W.logits_batch("normal10", B, 66, n=8)).cuda()
+    G8 = torch.from_numpy(W.grad_batch(B, 67, n=8)).cuda()
+    Pf, dAf = torch.empty_like(A), torch.empty_like(A)
+    dAr = torch.empty_like(A)
+    P8, dA8 = torch.empty_like(A8), torch.empty_like(A8)
+    Pfe, dAfe = gpu_lib.birkhoff_fwd_bwd(A, G)
+    dAre = gpu_lib.birkhoff_bwd_recompute(A, G)
+    P8e = gpu_lib.birkhoff_fwd_n(A8)
+    dA8e = gpu_lib.birkhoff_bwd_n(P8e, G8)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gpu_lib.birkhoff_fwd_bwd(A, G, out_P=Pf, out_grad=dAf)
+        gpu_lib.birkhoff_bwd_recompute(A, G, out=dAr)
+        gpu_lib.birkhoff_fwd_n(A8, out=P8)
+        gpu_lib.birkhoff_bwd_n(P8, G8, out=dA8)
+    for rep in range(3):
+        for t in (Pf, dAf, dAr, P8, dA8):
+            t.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Pf, Pfe) and torch.equal(dAf, dAfe), f"replay {rep}: fused"
+        assert torch.equal(dAr, dAre), f"replay {rep}: recompute"
+        assert torch.equal(P8, P8e) and torch.equal(dA8, dA8e), f"replay {rep}: 8x8"
+        gpu_lib.birkhoff_fwd_n(A8[:100])  # eager work between replays
+        torch.cuda.synchronize()
