@@ -42,6 +42,8 @@ int main(void)
     CHECK(mhc_birkhoff_fwd(NULL, NULL, 0, NULL, NULL, NULL) == MHC_OK);
     CHECK(mhc_birkhoff_bwd(NULL, NULL, NULL, 0, NULL) == MHC_OK);
     CHECK(mhc_birkhoff_fwd_n(NULL, NULL, 0, 3, NULL, NULL, NULL) == MHC_OK);
+    CHECK(mhc_birkhoff_bwd_recompute(NULL, NULL, NULL, 0, NULL, NULL) == MHC_OK);
+    CHECK(mhc_birkhoff_fwd_bwd(NULL, NULL, NULL, NULL, 0, NULL, NULL, NULL) == MHC_OK);
 
     /* argument errors */
     CHECK(mhc_birkhoff_fwd(FAKE(0), FAKE(0), -1, NULL, NULL, NULL) == MHC_ERR_INVALID_ARGUMENT);
@@ -51,6 +53,13 @@ int main(void)
     o.max_iters = -1;
     CHECK(mhc_birkhoff_fwd(FAKE(0), FAKE(0), 5, &o, NULL, NULL) == MHC_ERR_INVALID_ARGUMENT);
     CHECK(mhc_birkhoff_bwd(FAKE(0), NULL, FAKE(0), 3, NULL) == MHC_ERR_INVALID_ARGUMENT);
+    CHECK(mhc_birkhoff_bwd_recompute(FAKE(0), FAKE(8192), FAKE(64), 3, NULL, NULL) ==
+          MHC_ERR_INVALID_ARGUMENT);
+    /* fused: P may alias logits, but not grad_P */
+    CHECK(mhc_birkhoff_fwd_bwd(FAKE(0), FAKE(8192), FAKE(8192), FAKE(16384), 3, NULL, NULL,
+                               NULL) == MHC_ERR_INVALID_ARGUMENT);
+    CHECK(mhc_birkhoff_fwd_bwd(FAKE(0), FAKE(8192), FAKE(16384), FAKE(64), 3, NULL, NULL,
+                               NULL) == MHC_ERR_INVALID_ARGUMENT);
     CHECK(mhc_birkhoff_fwd_n(FAKE(0), FAKE(0), 5, 9, NULL, NULL, NULL) == MHC_ERR_UNSUPPORTED);
     CHECK(mhc_birkhoff_bwd_n(FAKE(0), FAKE(0), FAKE(0), 5, 0, NULL) == MHC_ERR_UNSUPPORTED);
     CHECK(mhc_stream_mix(FAKE(0), FAKE(8192), NULL, FAKE(16384), 4, 5, 64, NULL, NULL) ==
