@@ -59,16 +59,16 @@ KERNEL_SOURCES = {
     "layer": ("devmath.h", "proj4.h", "kernels.h", "layer.hip"),
 }
 MEASURED = {
-    "birkhoff_fwd_131072_cfg2": {"fetch": 8543362, "write": 8389041, "valu": 2704820, "trans": 145928, "sha": "aab674bf95fec978"},
-    "birkhoff_bwd_131072_cfg2": {"fetch": 16805875, "write": 8388673, "valu": 1122304, "trans": 24576, "sha": "aab674bf95fec978"},
-    "birkhoff_fwd_1048576_cfg3": {"fetch": 67259328, "write": 67112793, "valu": 20974751, "trans": 1128750, "sha": "aab674bf95fec978"},
-    "birkhoff_bwd_1048576_cfg3": {"fetch": 134231550, "write": 67109210, "valu": 8978432, "trans": 196608, "sha": "aab674bf95fec978"},
-    "birkhoff_fwd_n8_131072_cfg2": {"fetch": 40971775, "write": 59769832, "valu": 22793498, "trans": 745229, "sha": "7fd179215a1335d3"},
-    "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67434629, "write": 33554973, "valu": 6424576, "trans": 14336, "sha": "7fd179215a1335d3"},
-    "birkhoff_fwd_bwd_131072_cfg2": {"fetch": 16952581, "write": 16777269, "valu": 3243424, "trans": 152072, "sha": "aab674bf95fec978"},
-    "stream_mix_fwd_16384x4x4096": {"fetch": 537990608, "write": 537927767, "valu": 25710592, "trans": 68608, "sha": "7a25a3c96bcee9e9"},
-    "stream_mix_bwd_16384x4x4096": {"fetch": 1074731216, "write": 537963770, "valu": 50135040, "trans": 0, "sha": "7a25a3c96bcee9e9"},
-    "layer_step_65536x4x7168": {"fetch": 30725726804, "write": 9469211162, "sha": "1e39f47d32ca8a27"},
+    "birkhoff_fwd_131072_cfg2": {"fetch": 8542311, "write": 8389041, "valu": 2704820, "trans": 145928, "sha": "5de4aab0ad4df34e"},
+    "birkhoff_bwd_131072_cfg2": {"fetch": 16805880, "write": 8388911, "valu": 1122304, "trans": 24576, "sha": "5de4aab0ad4df34e"},
+    "birkhoff_fwd_1048576_cfg3": {"fetch": 67258854, "write": 67112764, "valu": 20974744, "trans": 1128750, "sha": "5de4aab0ad4df34e"},
+    "birkhoff_bwd_1048576_cfg3": {"fetch": 134231869, "write": 67109574, "valu": 8978432, "trans": 196608, "sha": "5de4aab0ad4df34e"},
+    "birkhoff_fwd_n8_131072_cfg2": {"fetch": 40903702, "write": 59770066, "valu": 22793498, "trans": 745229, "sha": "48cdc0bc8b0af7a7"},
+    "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67434335, "write": 33554904, "valu": 6424576, "trans": 14336, "sha": "48cdc0bc8b0af7a7"},
+    "birkhoff_fwd_bwd_131072_cfg2": {"fetch": 16947314, "write": 16777237, "valu": 3243424, "trans": 152072, "sha": "5de4aab0ad4df34e"},
+    "stream_mix_fwd_16384x4x4096": {"fetch": 537990666, "write": 537927767, "valu": 25710592, "trans": 68608, "sha": "3923325df41443f4"},
+    "stream_mix_bwd_16384x4x4096": {"fetch": 1074731338, "write": 537957722, "valu": 50135040, "trans": 0, "sha": "3923325df41443f4"},
+    "layer_step_65536x4x7168": {"fetch": 30728315744, "write": 9469199341, "sha": "5e702fe7a80ba9e2"},
 }
 
 

@@ -515,7 +515,14 @@ MHC_DEV void newton_step(NewtonLane& s, const SolverOpts& o)
     const bool lower = E.res < s.res;
     const bool curved = dphi <= kCurvature * mhc_abs(s.slope);
     const bool conv_t = E.res <= o.tol;
-    const bool pass = conv_t | (near_floor & lower) | (!near_floor & curved);
+    // On the max-shifted path (lanes whose logits span more than ~87 natural
+    // units, where the potentials reach the hundreds) two fp32 stalls are
+    // cut short; the factored loop, all ordinary inputs, skips both tests.
+    // A trial that takes the residual from above the noise floor into it is
+    // judged by the residual (the directional derivative is quantised there
+    // and can read as an overshoot).
+    const bool to_floor = !FACTORED && (E.res <= kNoiseFloor);
+    const bool pass = conv_t | ((near_floor | to_floor) & lower) | (!near_floor & curved);
     const bool accept = ok & pass;
     const bool reject = ok & !pass;
     // next first trial: after a full first trial that at least halved the
@@ -530,7 +537,14 @@ MHC_DEV void newton_step(NewtonLane& s, const SolverOpts& o)
     const bool conv = accept & conv_t;
     const bool maxed = accept & !conv & (s.newton >= o.max_iters);
     const int trials = s.trials + 1;
-    const bool stuck = reject & ((near_floor & (s.t <= 1.f)) | (trials > 30));
+    // A trial point equal to the accepted one (t d below the fp32 resolution
+    // of every potential) changes nothing, and the next iteration from that
+    // point would repeat it: the solve is at its fp32 limit.  Without these
+    // two tests such lanes spent up to 340 evaluations on N(0,100^2) logits
+    // (5 at most otherwise; the forward there ran 3.7x longer).  Applied to
+    // every trial they cost 3 % of the ordinary forward, hence this path only.
+    const bool still = !FACTORED && ((t0 == s.g0) & (t1 == s.g1) & (t2 == s.g2) & !conv_t);
+    const bool stuck = (reject & ((near_floor & (s.t <= 1.f)) | (trials > 30))) | (ok & still);
 
     s.g0 = accept ? t0 : s.g0;
     s.g1 = accept ? t1 : s.g1;

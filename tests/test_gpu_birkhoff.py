@@ -374,12 +374,14 @@ def test_degenerate_assignments(gpu_lib):
         assert (P[np.isinf(A32)] == 0).all(), label
 
 
-def test_huge_logits(gpu_lib):
-    """N(0,1000^2) logits (spreads of thousands of natural units; the oracle
-    cannot follow there): outputs finite, rows stochastic, at least 97 % of
-    matrices converged with column sums within SUM_TOL, every column sum
-    within 1e-4 (no column left empty)."""
-    A = (1000.0 * np.random.Generator(np.random.PCG64(42)).standard_normal((4096, 4, 4))).astype(np.float32)
+@pytest.mark.parametrize("sigma", [100.0, 1000.0])
+def test_huge_logits(gpu_lib, sigma):
+    """N(0,sigma^2) logits with spreads of hundreds to thousands of natural
+    units, where the oracle's Jacobian turns singular: outputs finite, rows
+    stochastic, at least 97 % of matrices converged with column sums within
+    SUM_TOL, every column sum within 1e-4 (no column left empty).  At 100 the
+    potentials sit in the hundreds, where fp32 steps can stall."""
+    A = (sigma * np.random.Generator(np.random.PCG64(42)).standard_normal((4096, 4, 4))).astype(np.float32)
     P, it = _fwd(gpu_lib, A)
     assert np.isfinite(P).all() and (P >= 0).all()
     P64 = P.astype(np.float64)
