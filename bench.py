@@ -59,16 +59,16 @@ KERNEL_SOURCES = {
     "layer": ("devmath.h", "proj4.h", "kernels.h", "layer.hip"),
 }
 MEASURED = {
-    "birkhoff_fwd_131072_cfg2": {"fetch": 8542311, "write": 8389041, "valu": 2704820, "trans": 145928, "sha": "5de4aab0ad4df34e"},
-    "birkhoff_bwd_131072_cfg2": {"fetch": 16805880, "write": 8388911, "valu": 1122304, "trans": 24576, "sha": "5de4aab0ad4df34e"},
-    "birkhoff_fwd_1048576_cfg3": {"fetch": 67258854, "write": 67112764, "valu": 20974744, "trans": 1128750, "sha": "5de4aab0ad4df34e"},
-    "birkhoff_bwd_1048576_cfg3": {"fetch": 134231869, "write": 67109574, "valu": 8978432, "trans": 196608, "sha": "5de4aab0ad4df34e"},
-    "birkhoff_fwd_n8_131072_cfg2": {"fetch": 40903702, "write": 59770066, "valu": 22793498, "trans": 745229, "sha": "48cdc0bc8b0af7a7"},
-    "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67434335, "write": 33554904, "valu": 6424576, "trans": 14336, "sha": "48cdc0bc8b0af7a7"},
-    "birkhoff_fwd_bwd_131072_cfg2": {"fetch": 16947314, "write": 16777237, "valu": 3243424, "trans": 152072, "sha": "5de4aab0ad4df34e"},
-    "stream_mix_fwd_16384x4x4096": {"fetch": 537990666, "write": 537927767, "valu": 25710592, "trans": 68608, "sha": "3923325df41443f4"},
-    "stream_mix_bwd_16384x4x4096": {"fetch": 1074731338, "write": 537957722, "valu": 50135040, "trans": 0, "sha": "3923325df41443f4"},
-    "layer_step_65536x4x7168": {"fetch": 30728315744, "write": 9469199341, "sha": "5e702fe7a80ba9e2"},
+    "birkhoff_fwd_131072_cfg2": {"fetch": 8542301, "write": 8389041, "valu": 2635940, "trans": 145972, "sha": "54eb2d9ea2097034"},
+    "birkhoff_bwd_131072_cfg2": {"fetch": 16805860, "write": 8389153, "valu": 1122304, "trans": 24576, "sha": "54eb2d9ea2097034"},
+    "birkhoff_fwd_1048576_cfg3": {"fetch": 67258770, "write": 67112640, "valu": 20416372, "trans": 1128673, "sha": "54eb2d9ea2097034"},
+    "birkhoff_bwd_1048576_cfg3": {"fetch": 134231741, "write": 67109588, "valu": 8978432, "trans": 196608, "sha": "54eb2d9ea2097034"},
+    "birkhoff_fwd_n8_131072_cfg2": {"fetch": 40890306, "write": 59770041, "valu": 22793498, "trans": 745229, "sha": "e3d0b54e32ed857c"},
+    "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67434139, "write": 33554787, "valu": 6424576, "trans": 14336, "sha": "e3d0b54e32ed857c"},
+    "birkhoff_fwd_bwd_131072_cfg2": {"fetch": 16955557, "write": 16777348, "valu": 3184784, "trans": 152116, "sha": "54eb2d9ea2097034"},
+    "stream_mix_fwd_16384x4x4096": {"fetch": 537990369, "write": 537927663, "valu": 25710592, "trans": 68608, "sha": "d39c2582381b45d9"},
+    "stream_mix_bwd_16384x4x4096": {"fetch": 1074730982, "write": 537958554, "valu": 50135040, "trans": 0, "sha": "d39c2582381b45d9"},
+    "layer_step_65536x4x7168": {"fetch": 30740255334, "write": 9469211354, "sha": "ee127d12e372d29b"},
 }
 
 

@@ -33,7 +33,9 @@ __global__ __launch_bounds__(kBlock) void birkhoff_fwd_kernel(const float* logit
     if (first >= B) return;  // the whole wave is past the batch
     float a[16], p[16];
     load_records_v4<16>(logits, first, B, tiles[w], a, lane);
-    const uint32_t it = SOLVER == 0 ? project_newton(a, p, o) : project_sinkhorn(a, p, o);
+    // the tile keeps the logits until the store: the start reads rows of it
+    const float* rec = tiles[w] + lane * record_pitch<16>();
+    const uint32_t it = SOLVER == 0 ? project_newton<true>(a, p, o, rec) : project_sinkhorn(a, p, o);
     store_records_v4<16>(P, first, B, tiles[w], p, lane);
     if (iters != nullptr && first + lane < B) iters[first + lane] = (uint8_t)it;
 }
@@ -87,14 +89,18 @@ __global__ __launch_bounds__(kBlock) void birkhoff_solve_bwd_kernel(const float*
                                                                     uint8_t* __restrict__ iters,
                                                                     int64_t B, SolverOpts o)
 {
+    // G goes through a tile of its own, so the logits' tile is intact for
+    // the start's row reads (the same start as birkhoff_fwd_kernel's)
     __shared__ float tiles[kBlock / 64][stage_tile_floats<16>()];
+    __shared__ float gtiles[kBlock / 64][stage_tile_floats<16>()];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int64_t first = (int64_t)blockIdx.x * kBlock + 64 * w;
     if (first >= B) return;
     float a[16], g[16], p[16], d[16];
     load_records_v4<16>(logits, first, B, tiles[w], a, lane);
-    load_records_v4<16>(G, first, B, tiles[w], g, lane);
-    const uint32_t it = SOLVER == 0 ? project_newton(a, p, o) : project_sinkhorn(a, p, o);
+    load_records_v4<16>(G, first, B, gtiles[w], g, lane);
+    const float* rec = tiles[w] + lane * record_pitch<16>();
+    const uint32_t it = SOLVER == 0 ? project_newton<true>(a, p, o, rec) : project_sinkhorn(a, p, o);
     project_bwd(p, g, d);
     if (WRITE_P) store_records_v4<16>(P, first, B, tiles[w], p, lane);
     store_records_v4<16>(dA, first, B, tiles[w], d, lane);

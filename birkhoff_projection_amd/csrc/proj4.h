@@ -341,10 +341,16 @@ MHC_DEV void newton_take(NewtonLane& s, const Eval& E) { s.res = E.res; }
 // orientation of each of the 6 column pairs, rows 0 and 1 each of the 12
 // ordered pairs of the other two columns.  Shortest paths have at most 3
 // edges, so two rounds of Bellman-Ford after the direct edges are exact.
-// Everything is in the base-2 units of a; a non-finite result (a NaN or
+// The search works in the base-2 units of a.  The exchange lengths take the
+// owner rows either from a by select chains (ROWS_IN_LDS false) or, when the
+// caller still holds the lane's raw logits in LDS (rec: 16 floats,
+// row-major), by indexed LDS reads: a row's max-shift cancels in every length,
+// so those lengths, the paths and the balancing are in natural units and the
+// result is scaled by log2 e at the end.  A non-finite result (a NaN or
 // infinite logit) falls back to g = 0.
 constexpr int kBalanceSweeps = 2;
-MHC_DEV void assignment_start(const float* a, float& g0, float& g1, float& g2)
+template <bool ROWS_IN_LDS>
+MHC_DEV void assignment_start(const float* a, const float* rec, float& g0, float& g1, float& g2)
 {
     // column pairs (k, l), k < l, and the pair left over by each ordered
     // (j0, j1)
@@ -379,15 +385,30 @@ MHC_DEV void assignment_start(const float* a, float& g0, float& g1, float& g2)
     }
     // w[c][j]: length of the edge c -> j (row owning column c moves to j)
     float w[4][4];
+    if constexpr (ROWS_IN_LDS) {
+        // owner row of every column, two bits per column (row 0's are zero)
+        const int c3 = 6 - c0 - c1 - c2;
+        const uint32_t own = (1u << (2 * c1)) | (2u << (2 * c2)) | (3u << (2 * c3));
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const bool o0 = c0 == c, o1 = c1 == c, o2 = c2 == c;
-        float row[4];
+        for (int c = 0; c < 4; ++c) {
+            const float* r = rec + 4 * ((own >> (2 * c)) & 3u);
+            float row[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            row[j] = o0 ? a[j] : (o1 ? a[4 + j] : (o2 ? a[8 + j] : a[12 + j]));
+            for (int j = 0; j < 4; ++j) row[j] = r[j];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) w[c][j] = row[c] - row[j];
+            for (int j = 0; j < 4; ++j) w[c][j] = row[c] - row[j];
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const bool o0 = c0 == c, o1 = c1 == c, o2 = c2 == c;
+            float row[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                row[j] = o0 ? a[j] : (o1 ? a[4 + j] : (o2 ? a[8 + j] : a[12 + j]));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) w[c][j] = row[c] - row[j];
+        }
     }
     // to[j]: shortest 3 -> j (upper end of g_j); from[j]: shortest j -> 3
     // (minus the lower end)
@@ -431,7 +452,8 @@ MHC_DEV void assignment_start(const float* a, float& g0, float& g1, float& g2)
             h[j] = 0.5f * (in - out);
         }
     }
-    const float m0 = h[0] - h[3], m1 = h[1] - h[3], m2 = h[2] - h[3];
+    const float unit = ROWS_IN_LDS ? kLog2e : 1.f;
+    const float m0 = (h[0] - h[3]) * unit, m1 = (h[1] - h[3]) * unit, m2 = (h[2] - h[3]) * unit;
     // NaN, +-inf (or overflow of the sum) fall back to g = 0
     const bool finite = (mhc_abs(m0) + mhc_abs(m1)) + mhc_abs(m2) < __builtin_inff();
     g0 = finite ? m0 : 0.f;
@@ -439,7 +461,8 @@ MHC_DEV void assignment_start(const float* a, float& g0, float& g1, float& g2)
     g2 = finite ? m2 : 0.f;
 }
 
-MHC_DEV void newton_init(NewtonLane& s, const float* a_nat, const SolverOpts& o)
+template <bool ROWS_IN_LDS>
+MHC_DEV void newton_init(NewtonLane& s, const float* a_nat, const float* rec, const SolverOpts& o)
 {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -455,7 +478,7 @@ MHC_DEV void newton_init(NewtonLane& s, const float* a_nat, const SolverOpts& o)
     s.slow = !s.kfast;
 #pragma unroll
     for (int j = 0; j < 16; ++j) s.k[j] = mhc_exp2(s.a[j]);
-    assignment_start(s.a, s.g0, s.g1, s.g2);
+    assignment_start<ROWS_IN_LDS>(s.a, rec, s.g0, s.g1, s.g2);
     s.newton = 0;
     s.trials = 0;
     Eval E;
@@ -568,10 +591,15 @@ MHC_DEV void newton_step(NewtonLane& s, const SolverOpts& o)
 //   P_out : the projected matrix (row-stochastic; doubly stochastic to tol)
 //   returns the Newton iteration count (warm sweeps not counted), or
 //   kNotConverged when max_iters, the noise floor or the line search stopped it.
-MHC_DEV uint32_t project_newton(const float* a_nat, float* P_out, const SolverOpts& o)
+//
+// rec, with ROWS_IN_LDS: the same 16 logits in LDS, left unchanged until this
+// returns (the start reads rows of it by a per-lane index).
+template <bool ROWS_IN_LDS = false>
+MHC_DEV uint32_t project_newton(const float* a_nat, float* P_out, const SolverOpts& o,
+                                const float* rec = nullptr)
 {
     NewtonLane s;
-    newton_init(s, a_nat, o);
+    newton_init<ROWS_IN_LDS>(s, a_nat, rec, o);
     while (!s.done && !s.slow) newton_step<true>(s, o);
     while (!s.done) newton_step<false>(s, o);
     // P of the accepted point (the same arithmetic as when it was accepted)
