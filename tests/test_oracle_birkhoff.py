@@ -268,6 +268,31 @@ def test_fixed_sweeps_inaccurate_on_large_inputs():
     assert np.median(e10) > 100 * np.median(e1)
 
 
+def test_fixed_sweeps_exact_values():
+    """sinkhorn_fixed against hand-derived exact rationals after 1, 2 and 3
+    sweeps (tests/golden/closed_forms.json, 'sinkhorn_fixed_cases'): a sweep
+    divides rows by their sums, then columns (Deep Signal article,
+    Sinkhorn-Knopp section).  A columns-first order, one sweep more or fewer,
+    or a transposed operand each fail one of them."""
+    import json
+    import os
+    from fractions import Fraction
+    path = os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")
+    with open(path) as fh:
+        cases = json.load(fh)["sinkhorn_fixed_cases"]
+    assert len(cases) >= 5
+    for case in cases:
+        A = np.log(np.array(case["K"], dtype=np.float64))
+        want = np.array([[float(Fraction(v)) for v in row] for row in case["P"]])
+        got = sinkhorn_fixed(A[None], case["sweeps"])[0]
+        np.testing.assert_allclose(got, want, rtol=0, atol=1e-14, err_msg=case["name"])
+    # the batch dimension is independent: the cases stacked give the same values
+    sq = [c for c in cases if len(c["K"]) == 4 and c["sweeps"] == 1]
+    A = np.log(np.array([c["K"] for c in sq], dtype=np.float64))
+    want = np.array([[[float(Fraction(v)) for v in row] for row in c["P"]] for c in sq])
+    np.testing.assert_allclose(sinkhorn_fixed(A, 1), want, rtol=0, atol=1e-14)
+
+
 # --------------------------------------------------------------------------
 # backward
 # --------------------------------------------------------------------------
