@@ -36,10 +36,18 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb)
     return x < y + nb && y < x + na;
 }
 
-// Largest batch / token count accepted (2^36 matrices = 4 TiB of fp32); keeps
-// every grid far below the 2^31 - 1 workgroup limit.
-constexpr int64_t kMaxBatch = (int64_t)1 << 36;
-constexpr int64_t kMaxTokens = (int64_t)1 << 34;
+// Largest batch / token count one call accepts.  A launch's grid may hold
+// fewer than 2^32 work-items in total, and the widest launches use 4 lanes per
+// matrix (the 4x4 backward) and 16 per token (the stream-mix forward and the
+// layer's mix and dx passes), so these keep every grid below that.
+constexpr int64_t kMaxBatch = MHC_MAX_BATCH;
+constexpr int64_t kMaxTokens = MHC_MAX_TOKENS;
+static_assert(4 * kMaxBatch <= ((int64_t)1 << 32) - 256, "4x4 backward grid");
+static_assert(16 * kMaxTokens <= ((int64_t)1 << 32) - 256, "token grids");
+
+// Solver limits when mhc_proj_opts.max_iters is -1.
+constexpr int kDefaultNewtonIters = 30;
+constexpr int kDefaultSinkhornSweeps = 1000;
 
 mhc_status check_opts(const mhc_proj_opts* in, mhc::SolverOpts* out)
 {
@@ -48,8 +56,11 @@ mhc_status check_opts(const mhc_proj_opts* in, mhc::SolverOpts* out)
     if (in != nullptr) o = *in;
     if (o.solver != MHC_SOLVER_NEWTON && o.solver != MHC_SOLVER_SINKHORN)
         return fail(MHC_ERR_INVALID_ARGUMENT, "opts.solver must be 0 (Newton) or 1 (Sinkhorn)");
+    if (o.max_iters == -1)
+        o.max_iters = o.solver == MHC_SOLVER_NEWTON ? kDefaultNewtonIters : kDefaultSinkhornSweeps;
     if (o.max_iters < 1 || o.max_iters > 10000)
-        return fail(MHC_ERR_INVALID_ARGUMENT, "opts.max_iters must be in 1..10000");
+        return fail(MHC_ERR_INVALID_ARGUMENT,
+                    "opts.max_iters must be -1 (the solver's default) or in 1..10000");
     if (!(o.tol >= 0.f) || o.tol > 1.f)
         return fail(MHC_ERR_INVALID_ARGUMENT, "opts.tol must be in [0, 1]");
     if (o.warm_sweeps < -1 || o.warm_sweeps > 64)
@@ -72,7 +83,7 @@ mhc_status mhc_proj_opts_default(mhc_proj_opts* opts)
 {
     if (opts == nullptr) return fail(MHC_ERR_INVALID_ARGUMENT, "opts is NULL");
     opts->solver = MHC_SOLVER_NEWTON;
-    opts->max_iters = 30;
+    opts->max_iters = -1;
     opts->tol = 1e-6f;
     opts->warm_sweeps = -1;
     return MHC_OK;
@@ -334,19 +345,11 @@ mhc_status mhc_layer_fwd(const mhc_layer_args* a, void* stream)
                     "layer_fwd launch");
 }
 
-mhc_status mhc_layer_bwd(const mhc_layer_args* a, void* stream)
+// The backward's pointer checks: NULL, alignment, overlaps.  `ws`/`ws_bytes`
+// is the workspace to include in the overlap test (NULL: none).
+static mhc_status check_layer_bwd(const mhc_layer_args* a, const void* ws, size_t ws_bytes)
 {
-    if (a == nullptr) return fail(MHC_ERR_INVALID_ARGUMENT, "args is NULL");
-    mhc_status s = check_layer_shape(a->T, a->n, a->C);
-    if (s != MHC_OK) return s;
-    if (a->T == 0) return ok();
     const size_t T = (size_t)a->T, C = (size_t)a->C;
-    const int64_t need = mhc::layer_plan(a->T, a->C).bytes;
-    if (a->workspace_bytes < need)
-        return fail(MHC_ERR_INVALID_ARGUMENT, "workspace_bytes=%lld < %lld required",
-                    (long long)a->workspace_bytes, (long long)need);
-    if (((uintptr_t)a->workspace & 255u) != 0)
-        return fail(MHC_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
     const Buf b[] = {{a->x, T * 4 * C * 2, "x"},
                      {a->W, 24 * 4 * C * 2, "W"},
                      {a->f, T * C * 2, "f"},
@@ -361,14 +364,35 @@ mhc_status mhc_layer_bwd(const mhc_layer_args* a, void* stream)
                      {a->grad_f, T * C * 2, "grad_f"},
                      {a->grad_W, 24 * 4 * C * 4, "grad_W"},
                      {a->grad_logits, T * 96, "grad_logits"},
-                     {a->workspace, (size_t)need, "workspace"}};
-    s = check_buffers(b, sizeof(b) / sizeof(b[0]));
+                     {ws, ws_bytes, "workspace"}};
+    return check_buffers(b, sizeof(b) / sizeof(b[0]) - (ws == nullptr ? 1 : 0));
+}
+
+static mhc::LayerPtrs layer_bwd_ptrs(const mhc_layer_args* a, void* ws)
+{
+    return mhc::LayerPtrs{a->x,         a->W,      a->f,      nullptr,       nullptr,
+                          a->rms,       a->logits, a->H_pre,  a->H_post,     a->H_res,
+                          a->grad_x_out, a->grad_u, a->grad_x, a->grad_f,    a->grad_W,
+                          a->grad_logits, ws};
+}
+
+mhc_status mhc_layer_bwd(const mhc_layer_args* a, void* stream)
+{
+    if (a == nullptr) return fail(MHC_ERR_INVALID_ARGUMENT, "args is NULL");
+    mhc_status s = check_layer_shape(a->T, a->n, a->C);
     if (s != MHC_OK) return s;
-    const mhc::LayerPtrs p{a->x,         a->W,      a->f,      nullptr,       nullptr,
-                           a->rms,       a->logits, a->H_pre,  a->H_post,     a->H_res,
-                           a->grad_x_out, a->grad_u, a->grad_x, a->grad_f,    a->grad_W,
-                           a->grad_logits, a->workspace};
-    return launched(mhc::launch_layer_bwd(p, a->T, a->C, (hipStream_t)stream), "layer_bwd launch");
+    if (a->T == 0) return ok();
+    const int64_t need = mhc::layer_plan(a->T, a->C).bytes;
+    if (a->workspace_bytes < need)
+        return fail(MHC_ERR_INVALID_ARGUMENT, "workspace_bytes=%lld < %lld required",
+                    (long long)a->workspace_bytes, (long long)need);
+    if (((uintptr_t)a->workspace & 255u) != 0)
+        return fail(MHC_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    s = check_layer_bwd(a, a->workspace, (size_t)need);
+    if (s != MHC_OK) return s;
+    return launched(mhc::launch_layer_bwd(layer_bwd_ptrs(a, a->workspace), a->T, a->C,
+                                          (hipStream_t)stream),
+                    "layer_bwd launch");
 }
 
 const char* mhc_status_string(mhc_status s)

@@ -76,11 +76,13 @@ MHC_DEV void mix_chunk(const float* M, const uint4* xin, uint4* oout)
 // Forward.  Workgroup = kTokensPerBlock tokens.  Lanes 0..15 of wave 0 first
 // obtain the tokens' 4x4 matrices -- projecting the logits (PROJ = 1 Newton,
 // 2 Sinkhorn) or loading H (PROJ = 0) -- into LDS; then all 256 lanes stream
-// the tokens' chunks.
+// the tokens' chunks.  H_out may be the logits buffer itself (a lane reads its
+// token's logits before it writes that token's H), so neither pointer is
+// declared restrict.
 template <int PROJ>
 __global__ __launch_bounds__(kBlock) void stream_mix_fwd_kernel(
-    const uint4* __restrict__ x, const float* __restrict__ Hl, float* __restrict__ H_out,
-    uint4* __restrict__ out, int64_t T, int64_t C8, SolverOpts o)
+    const uint4* __restrict__ x, const float* Hl, float* H_out, uint4* __restrict__ out,
+    int64_t T, int64_t C8, SolverOpts o)
 {
     __shared__ float sH[kTokensPerBlock][16];
     const int64_t t0 = (int64_t)blockIdx.x * kTokensPerBlock;

@@ -21,8 +21,6 @@ def make_opts(solver="newton", max_iters=None, tol=None, warm_sweeps=None) -> Pr
     if solver not in SOLVERS:
         raise ValueError(f"solver must be one of {sorted(SOLVERS)}")
     o.solver = SOLVERS[solver]
-    if solver == "sinkhorn":
-        o.max_iters = 1000
     if max_iters is not None:
         o.max_iters = int(max_iters)
     if tol is not None:
@@ -51,17 +49,36 @@ def _need(t, name, dtype, last_dims=None):
         raise ValueError(f"{name} must have trailing shape {last_dims}, got {tuple(t.shape)}")
 
 
+def _same(t, name, like, like_name):
+    """t (already checked by _need) has exactly like's shape and device."""
+    if tuple(t.shape) != tuple(like.shape):
+        raise ValueError(f"{name} must have the shape of {like_name} {tuple(like.shape)}, "
+                         f"got {tuple(t.shape)}")
+    if t.device != like.device:
+        raise ValueError(f"{name} must be on {like.device}, got {t.device}")
+
+
+def _out(out, name, dtype, shape, device):
+    """A caller-provided output: a contiguous CUDA tensor of exactly ``shape``
+    and ``dtype`` on ``device`` (a short or misplaced buffer would let the
+    kernel write past its allocation), or a new one if ``out`` is None."""
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _need(out, name, dtype)
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(out.shape)}")
+    if out.device != device:
+        raise ValueError(f"{name} must be on {device}, got {out.device}")
+    return out
+
+
 def birkhoff_fwd(logits: torch.Tensor, *, solver="newton", max_iters=None, tol=None,
                  warm_sweeps=None, out=None, return_iters=False):
     """Project [..., 4, 4] fp32 logits onto the doubly stochastic matrices.
     Returns P (and the uint8 iteration codes if ``return_iters``)."""
     _need(logits, "logits", torch.float32, (4, 4))
     B = logits.numel() // 16
-    P = torch.empty_like(logits) if out is None else out
-    if out is not None:
-        _need(out, "out", torch.float32, (4, 4))
-        if out.shape != logits.shape or out.device != logits.device:
-            raise ValueError("out must match logits in shape and device")
+    P = _out(out, "out", torch.float32, logits.shape, logits.device)
     iters = torch.empty(logits.shape[:-2], dtype=torch.uint8, device=logits.device) if return_iters else None
     o = make_opts(solver, max_iters, tol, warm_sweeps)
     with torch.cuda.device(logits.device):
@@ -74,11 +91,8 @@ def birkhoff_bwd(P: torch.Tensor, grad_P: torch.Tensor, out=None):
     """dL/dlogits from P = projection(logits) and dL/dP (fp32 [..., 4, 4])."""
     _need(P, "P", torch.float32, (4, 4))
     _need(grad_P, "grad_P", torch.float32, (4, 4))
-    if P.shape != grad_P.shape or P.device != grad_P.device:
-        raise ValueError("P and grad_P must match in shape and device")
-    dA = torch.empty_like(P) if out is None else out
-    if out is not None:
-        _need(out, "out", torch.float32, (4, 4))
+    _same(grad_P, "grad_P", P, "P")
+    dA = _out(out, "out", torch.float32, P.shape, P.device)
     with torch.cuda.device(P.device):
         check(lib().mhc_birkhoff_bwd(_ptr(P), _ptr(grad_P), _ptr(dA), P.numel() // 16,
                                      _stream(P.device)))
@@ -94,11 +108,7 @@ def birkhoff_fwd_n(logits: torch.Tensor, *, solver="newton", max_iters=None, tol
     n = logits.shape[-1]
     _need(logits, "logits", torch.float32, (n, n))
     B = logits.numel() // (n * n)
-    P = torch.empty_like(logits) if out is None else out
-    if out is not None:
-        _need(out, "out", torch.float32, (n, n))
-        if out.shape != logits.shape or out.device != logits.device:
-            raise ValueError("out must match logits in shape and device")
+    P = _out(out, "out", torch.float32, logits.shape, logits.device)
     iters = torch.empty(logits.shape[:-2], dtype=torch.uint8, device=logits.device) if return_iters else None
     o = make_opts(solver, max_iters, tol, warm_sweeps)
     with torch.cuda.device(logits.device):
@@ -114,11 +124,8 @@ def birkhoff_bwd_n(P: torch.Tensor, grad_P: torch.Tensor, out=None):
     n = P.shape[-1]
     _need(P, "P", torch.float32, (n, n))
     _need(grad_P, "grad_P", torch.float32, (n, n))
-    if P.shape != grad_P.shape or P.device != grad_P.device:
-        raise ValueError("P and grad_P must match in shape and device")
-    dA = torch.empty_like(P) if out is None else out
-    if out is not None:
-        _need(out, "out", torch.float32, (n, n))
+    _same(grad_P, "grad_P", P, "P")
+    dA = _out(out, "out", torch.float32, P.shape, P.device)
     with torch.cuda.device(P.device):
         check(lib().mhc_birkhoff_bwd_n(_ptr(P), _ptr(grad_P), _ptr(dA), P.numel() // (n * n), n,
                                        _stream(P.device)))
@@ -132,11 +139,8 @@ def birkhoff_bwd_recompute(logits: torch.Tensor, grad_P: torch.Tensor, *, solver
     there, so P need not be kept between forward and backward."""
     _need(logits, "logits", torch.float32, (4, 4))
     _need(grad_P, "grad_P", torch.float32, (4, 4))
-    if logits.shape != grad_P.shape or logits.device != grad_P.device:
-        raise ValueError("logits and grad_P must match in shape and device")
-    dA = torch.empty_like(logits) if out is None else out
-    if out is not None:
-        _need(out, "out", torch.float32, (4, 4))
+    _same(grad_P, "grad_P", logits, "logits")
+    dA = _out(out, "out", torch.float32, logits.shape, logits.device)
     o = make_opts(solver, max_iters, tol, warm_sweeps)
     with torch.cuda.device(logits.device):
         check(lib().mhc_birkhoff_bwd_recompute(_ptr(logits), _ptr(grad_P), _ptr(dA),
@@ -153,14 +157,9 @@ def birkhoff_fwd_bwd(logits: torch.Tensor, grad_P: torch.Tensor, *, solver="newt
     out_P may be ``logits`` itself and out_grad ``grad_P`` itself."""
     _need(logits, "logits", torch.float32, (4, 4))
     _need(grad_P, "grad_P", torch.float32, (4, 4))
-    if logits.shape != grad_P.shape or logits.device != grad_P.device:
-        raise ValueError("logits and grad_P must match in shape and device")
-    P = torch.empty_like(logits) if out_P is None else out_P
-    dA = torch.empty_like(logits) if out_grad is None else out_grad
-    for t, name in ((P, "out_P"), (dA, "out_grad")):
-        _need(t, name, torch.float32, (4, 4))
-        if t.shape != logits.shape:
-            raise ValueError(f"{name} must have the shape of logits")
+    _same(grad_P, "grad_P", logits, "logits")
+    P = _out(out_P, "out_P", torch.float32, logits.shape, logits.device)
+    dA = _out(out_grad, "out_grad", torch.float32, logits.shape, logits.device)
     B = logits.numel() // 16
     it = torch.empty(logits.shape[:-2], dtype=torch.uint8, device=logits.device) if return_iters else None
     o = make_opts(solver, max_iters, tol, warm_sweeps)
@@ -207,12 +206,13 @@ def birkhoff_project(logits, **kw):
 
 
 def stream_mix(x: torch.Tensor, H: torch.Tensor = None, *, logits: torch.Tensor = None,
-               out=None, return_H=False, solver="newton", max_iters=None, tol=None,
+               out=None, return_H=False, H_out=None, solver="newton", max_iters=None, tol=None,
                warm_sweeps=None):
     """out[t,i,:] = sum_j H[t,i,j] x[t,j,:] for x [T,4,C] bf16.
 
     Pass either ``H`` [T,4,4] fp32, or ``logits`` [T,4,4] fp32 to project in
-    the same kernel (then ``return_H`` also returns the projected H)."""
+    the same kernel (then ``return_H`` also returns the projected H, written
+    into ``H_out`` if given)."""
     _need(x, "x", torch.bfloat16)
     if x.dim() != 3:
         raise ValueError("x must be [T, n, C]")
@@ -220,13 +220,15 @@ def stream_mix(x: torch.Tensor, H: torch.Tensor = None, *, logits: torch.Tensor 
     if (H is None) == (logits is None):
         raise ValueError("pass exactly one of H or logits")
     src = H if H is not None else logits
-    _need(src, "H" if H is not None else "logits", torch.float32, (n, n))
-    if src.shape[0] != T:
-        raise ValueError("H/logits must have T rows")
-    y = torch.empty_like(x) if out is None else out
-    H_out = None
+    _need(src, "H" if H is not None else "logits", torch.float32)
+    if tuple(src.shape) != (T, n, n) or src.device != x.device:
+        raise ValueError(f"H/logits must be [{T}, {n}, {n}] on {x.device}, got "
+                         f"{tuple(src.shape)} on {src.device}")
+    y = _out(out, "out", torch.bfloat16, x.shape, x.device)
+    if H_out is not None and not (logits is not None and return_H):
+        raise ValueError("H_out needs logits and return_H")
     if logits is not None and return_H:
-        H_out = torch.empty_like(logits)
+        H_out = _out(H_out, "H_out", torch.float32, logits.shape, x.device)
     o = make_opts(solver, max_iters, tol, warm_sweeps) if logits is not None else None
     with torch.cuda.device(x.device):
         check(lib().mhc_stream_mix(_ptr(x), _ptr(src), _ptr(H_out), _ptr(y), T, n, C,
@@ -239,17 +241,17 @@ def stream_mix_bwd(x: torch.Tensor, H: torch.Tensor, grad_out: torch.Tensor, out
     """(grad_x bf16 [T,4,C], grad_H fp32 [T,4,4]) of the stream mix; ``out``
     may be a preallocated (grad_x, grad_H) pair."""
     _need(x, "x", torch.bfloat16)
+    if x.dim() != 3:
+        raise ValueError("x must be [T, n, C]")
     _need(grad_out, "grad_out", torch.bfloat16)
+    _same(grad_out, "grad_out", x, "x")
     T, n, C = x.shape
-    _need(H, "H", torch.float32, (n, n))
-    if out is None:
-        gx, gH = torch.empty_like(x), torch.empty_like(H)
-    else:
-        gx, gH = out
-        _need(gx, "grad_x", torch.bfloat16)
-        _need(gH, "grad_H", torch.float32, (n, n))
-        if gx.shape != x.shape or gH.shape != H.shape:
-            raise ValueError("out must be (grad_x like x, grad_H like H)")
+    _need(H, "H", torch.float32)
+    if tuple(H.shape) != (T, n, n) or H.device != x.device:
+        raise ValueError(f"H must be [{T}, {n}, {n}] on {x.device}, got {tuple(H.shape)} on {H.device}")
+    gx, gH = (None, None) if out is None else out
+    gx = _out(gx, "grad_x", torch.bfloat16, x.shape, x.device)
+    gH = _out(gH, "grad_H", torch.float32, H.shape, x.device)
     with torch.cuda.device(x.device):
         check(lib().mhc_stream_mix_bwd(_ptr(x), _ptr(H), _ptr(grad_out), _ptr(gx), _ptr(gH), T,
                                        n, C, _stream(x.device)))
@@ -268,6 +270,8 @@ def _layer_args(x, W, f, eps, opts):
     _need(f, "f", torch.bfloat16)
     if tuple(W.shape) != (n * n + 2 * n, n * C) or tuple(f.shape) != (T, C):
         raise ValueError("W must be [n*n+2n, n*C] and f [T, C]")
+    if W.device != x.device or f.device != x.device:
+        raise ValueError("x, W and f must be on one device")
     a = LayerArgs()
     a.T, a.n, a.C, a.eps = T, n, C, float(eps)
     a.proj = ctypes.pointer(opts) if opts is not None else None
@@ -275,23 +279,39 @@ def _layer_args(x, W, f, eps, opts):
     return a
 
 
+def _fwd_shapes(T, n, C):
+    """Shapes and dtypes of the layer forward's outputs."""
+    return dict(u=((T, C), torch.bfloat16), x_out=((T, n, C), torch.bfloat16),
+                rms=((T,), torch.float32), logits=((T, N_MAPS), torch.float32),
+                H_pre=((T, n), torch.float32), H_post=((T, n), torch.float32),
+                H_res=((T, n, n), torch.float32))
+
+
+def _bwd_shapes(T, n, C):
+    """Shapes and dtypes of the layer backward's outputs."""
+    return dict(grad_x=((T, n, C), torch.bfloat16), grad_f=((T, C), torch.bfloat16),
+                grad_W=((N_MAPS, n * C), torch.float32),
+                grad_logits=((T, N_MAPS), torch.float32))
+
+
+def _dict_out(out, shapes, device):
+    """Every tensor of a caller-provided output dict checked (or allocated)."""
+    out = {} if out is None else out
+    return {k: _out(out.get(k), k, dt, sh, device) for k, (sh, dt) in shapes.items()}
+
+
 def layer_fwd(x, W, f, *, eps=1e-6, solver="newton", max_iters=None, tol=None,
-              warm_sweeps=None):
+              warm_sweeps=None, out=None):
     """Forward of one mHC layer step.  x [T,4,C], W [24,4C], f [T,C] bf16.
-    Returns dict(u, x_out, rms, logits, H_pre, H_post, H_res)."""
+    Returns dict(u, x_out, rms, logits, H_pre, H_post, H_res), written into
+    ``out``'s tensors when a previous result dict is passed."""
     o = make_opts(solver, max_iters, tol, warm_sweeps)
     a = _layer_args(x, W, f, eps, o)
     T, n, C = x.shape
     dev = x.device
-    out = dict(u=torch.empty((T, C), dtype=torch.bfloat16, device=dev),
-               x_out=torch.empty_like(x),
-               rms=torch.empty(T, dtype=torch.float32, device=dev),
-               logits=torch.empty((T, N_MAPS), dtype=torch.float32, device=dev),
-               H_pre=torch.empty((T, n), dtype=torch.float32, device=dev),
-               H_post=torch.empty((T, n), dtype=torch.float32, device=dev),
-               H_res=torch.empty((T, n, n), dtype=torch.float32, device=dev))
-    for k in ("u", "x_out", "rms", "logits", "H_pre", "H_post", "H_res"):
-        setattr(a, k, out[k].data_ptr())
+    out = _dict_out(out, _fwd_shapes(T, n, C), dev)
+    for k, t in out.items():
+        setattr(a, k, t.data_ptr())
     with torch.cuda.device(dev):
         check(lib().mhc_layer_fwd(ctypes.byref(a), _stream(dev)))
     return out
@@ -299,23 +319,13 @@ def layer_fwd(x, W, f, *, eps=1e-6, solver="newton", max_iters=None, tol=None,
 
 def layer_fwd_into(x, W, f, out, *, eps=1e-6, solver="newton"):
     """layer_fwd writing into the tensors of a previous result dict ``out``."""
-    o = make_opts(solver)
-    a = _layer_args(x, W, f, eps, o)
-    for k in ("u", "x_out", "rms", "logits", "H_pre", "H_post", "H_res"):
-        setattr(a, k, out[k].data_ptr())
-    with torch.cuda.device(x.device):
-        check(lib().mhc_layer_fwd(ctypes.byref(a), _stream(x.device)))
-    return out
+    return layer_fwd(x, W, f, eps=eps, solver=solver, out=out)
 
 
 def stream_mix_into(x, logits, H_out, out, solver="newton"):
     """Fused projection + stream mix into preallocated H_out and out."""
-    T, n, C = x.shape
-    o = make_opts(solver)
-    with torch.cuda.device(x.device):
-        check(lib().mhc_stream_mix(_ptr(x), _ptr(logits), _ptr(H_out), _ptr(out), T, n, C,
-                                   ctypes.byref(o), _stream(x.device)))
-    return out
+    y, _ = stream_mix(x, logits=logits, out=out, H_out=H_out, return_H=True, solver=solver)
+    return y
 
 
 def layer_workspace(T, C, device, n=4):
@@ -325,25 +335,42 @@ def layer_workspace(T, C, device, n=4):
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
 
 
-def layer_bwd(x, W, f, fwd, grad_x_out, grad_u, *, workspace=None, out=None):
-    """Backward of one mHC layer step given the forward's outputs ``fwd``.
-    Returns dict(grad_x, grad_f, grad_W, grad_logits)."""
+def _layer_bwd_args(x, W, f, fwd, grad_x_out, grad_u, out):
     a = _layer_args(x, W, f, 1e-6, None)
     T, n, C = x.shape
     dev = x.device
     _need(grad_x_out, "grad_x_out", torch.bfloat16)
+    _same(grad_x_out, "grad_x_out", x, "x")
     _need(grad_u, "grad_u", torch.bfloat16)
-    for k in ("rms", "logits", "H_pre", "H_post", "H_res"):
-        _need(fwd[k], k, torch.float32)
-        setattr(a, k, fwd[k].data_ptr())
+    _same(grad_u, "grad_u", f, "f")
+    for k, (sh, dt) in _fwd_shapes(T, n, C).items():
+        if k in ("u", "x_out"):
+            continue
+        t = fwd[k]
+        _need(t, k, dt)
+        if tuple(t.shape) != sh or t.device != dev:
+            raise ValueError(f"{k} must be {sh} on {dev}, got {tuple(t.shape)} on {t.device}")
+        setattr(a, k, t.data_ptr())
     a.grad_x_out, a.grad_u = grad_x_out.data_ptr(), grad_u.data_ptr()
-    if out is None:
-        out = dict(grad_x=torch.empty_like(x), grad_f=torch.empty_like(f),
-                   grad_W=torch.empty(W.shape, dtype=torch.float32, device=dev),
-                   grad_logits=torch.empty((T, N_MAPS), dtype=torch.float32, device=dev))
-    for k in ("grad_x", "grad_f", "grad_W", "grad_logits"):
-        setattr(a, k, out[k].data_ptr())
-    ws = layer_workspace(T, C, dev, n) if workspace is None else workspace
+    out = _dict_out(out, _bwd_shapes(T, n, C), dev)
+    for k, t in out.items():
+        setattr(a, k, t.data_ptr())
+    return a, out
+
+
+def layer_bwd(x, W, f, fwd, grad_x_out, grad_u, *, workspace=None, out=None):
+    """Backward of one mHC layer step given the forward's outputs ``fwd``.
+    Returns dict(grad_x, grad_f, grad_W, grad_logits)."""
+    a, out = _layer_bwd_args(x, W, f, fwd, grad_x_out, grad_u, out)
+    T, n, C = x.shape
+    dev = x.device
+    if workspace is None:
+        ws = layer_workspace(T, C, dev, n)
+    else:
+        ws = workspace
+        _need(ws, "workspace", torch.uint8)
+        if ws.device != dev:
+            raise ValueError(f"workspace must be on {dev}, got {ws.device}")
     a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
     with torch.cuda.device(dev):
         check(lib().mhc_layer_bwd(ctypes.byref(a), _stream(dev)))

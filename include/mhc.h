@@ -66,8 +66,21 @@ extern "C" {
 #endif
 
 /* Version history: 1 first release; 2 adds mhc_birkhoff_fwd_bwd and makes
- * -1 (the solver's own choice) the default of mhc_proj_opts.warm_sweeps. */
-#define MHC_ABI_VERSION 2
+ * -1 (the solver's own choice) the default of mhc_proj_opts.warm_sweeps; 3
+ * makes -1 the default of mhc_proj_opts.max_iters as well (30 Newton
+ * iterations, 1000 Sinkhorn sweeps) and bounds every call's batch by
+ * MHC_MAX_BATCH / MHC_MAX_TOKENS. */
+#define MHC_ABI_VERSION 3
+
+/* Largest batch one call accepts: B matrices for the projection calls, T
+ * tokens for the stream-mix and layer calls.  Larger values return
+ * MHC_ERR_INVALID_ARGUMENT before anything is enqueued.  They are the sizes
+ * whose launches stay below the 2^32 work-items one grid dimension can hold
+ * (the 4x4 backward runs four lanes per matrix, the token kernels sixteen
+ * per token); split larger batches into several calls.  At these limits one
+ * [B,4,4] fp32 tensor is 64 GiB and one [T,4,8] bf16 stream tensor 16 GiB. */
+#define MHC_MAX_BATCH ((int64_t)1073741760)  /* 2^30 - 64 */
+#define MHC_MAX_TOKENS ((int64_t)268435440)  /* 2^28 - 16 */
 
 typedef enum {
     MHC_OK = 0,
@@ -84,8 +97,9 @@ typedef enum {
 /* Forward-solver options.  mhc_proj_opts_default() fills the defaults. */
 typedef struct {
     int32_t solver;      /* mhc_solver; default MHC_SOLVER_NEWTON */
-    int32_t max_iters;   /* Newton iterations (default 30) or Sinkhorn sweeps
-                            (default 1000); 1 .. 10000 */
+    int32_t max_iters;   /* Newton iterations or Sinkhorn sweeps, 1 .. 10000,
+                            or -1 (the default) for the solver's own limit:
+                            30 Newton iterations, 1000 Sinkhorn sweeps */
     float tol;           /* stop once max_j |column sum_j - 1| <= tol (rows are
                             normalised last, so they sum to 1 up to rounding);
                             default 1e-6.  Sinkhorn with tol == 0 runs exactly
@@ -118,7 +132,7 @@ mhc_status mhc_proj_opts_default(mhc_proj_opts* opts);
  *
  *   logits  [B,4,4] fp32, device, 16-byte aligned (64 bytes per matrix)
  *   P       [B,4,4] fp32, device, 16-byte aligned; may alias logits exactly
- *   B       number of matrices, >= 0
+ *   B       number of matrices, 0 <= B <= MHC_MAX_BATCH
  *   opts    solver options, NULL = defaults; host pointer, read during the call
  *   iters   NULL or device [B] uint8: Newton iterations (or Sinkhorn sweeps)
  *           used, 254 = 254 or more, 255 = stopped with the column residual
@@ -141,7 +155,7 @@ mhc_status mhc_birkhoff_fwd(const float* logits, float* P, int64_t B,
  *   P            [B,4,4] fp32, device, as returned by mhc_birkhoff_fwd
  *   grad_P       [B,4,4] fp32, device
  *   grad_logits  [B,4,4] fp32, device; may alias grad_P exactly
- *   B >= 0, stream as above.
+ *   0 <= B <= MHC_MAX_BATCH, stream as above.
  */
 mhc_status mhc_birkhoff_bwd(const float* P, const float* grad_P, float* grad_logits,
                             int64_t B, void* stream);
@@ -165,7 +179,7 @@ mhc_status mhc_birkhoff_bwd(const float* P, const float* grad_P, float* grad_log
  *                grad_P exactly (each matrix is read whole before it is
  *                written), must not overlap them partially
  *   opts         solver options as for mhc_birkhoff_fwd (NULL = defaults)
- *   B >= 0, stream as above.  Errors as for mhc_birkhoff_fwd.
+ *   0 <= B <= MHC_MAX_BATCH, stream as above.  Errors as for mhc_birkhoff_fwd.
  */
 mhc_status mhc_birkhoff_bwd_recompute(const float* logits, const float* grad_P,
                                       float* grad_logits, int64_t B,
@@ -190,7 +204,7 @@ mhc_status mhc_birkhoff_bwd_recompute(const float* logits, const float* grad_P,
  *                grad_P exactly, must not overlap logits or P
  *   opts, iters  as for mhc_birkhoff_fwd (iters must not overlap any of the
  *                four arrays)
- *   B >= 0, stream as above.  Errors as for mhc_birkhoff_fwd.
+ *   0 <= B <= MHC_MAX_BATCH, stream as above.  Errors as for mhc_birkhoff_fwd.
  */
 mhc_status mhc_birkhoff_fwd_bwd(const float* logits, const float* grad_P, float* P,
                                 float* grad_logits, int64_t B, const mhc_proj_opts* opts,
@@ -231,7 +245,8 @@ mhc_status mhc_birkhoff_bwd_n(const float* P, const float* grad_P, float* grad_l
  *   H_out        NULL or [T,n,n] fp32, device: receives the projected H (only
  *                used when proj != NULL)
  *   out          [T,n,C] bf16, device; must not overlap x
- *   T >= 0 tokens, n == 4 (else MHC_ERR_UNSUPPORTED), C >= 8, C % 8 == 0
+ *   0 <= T <= MHC_MAX_TOKENS, n == 4 (else MHC_ERR_UNSUPPORTED), C >= 8,
+ *   C % 8 == 0
  *   proj         NULL or host pointer to solver options (see above)
  */
 mhc_status mhc_stream_mix(const void* x, const float* H_or_logits, float* H_out, void* out,
@@ -241,11 +256,16 @@ mhc_status mhc_stream_mix(const void* x, const float* H_or_logits, float* H_out,
 /* mhc_stream_mix_bwd -- gradients of the stream mix for upstream grad_out:
  *   grad_x[t,j,c] = sum_i H[t,i,j] grad_out[t,i,c]     (bf16, fp32 accumulation)
  *   grad_H[t,i,j] = sum_c grad_out[t,i,c] x[t,j,c]     (fp32)
+ * The mix is linear in x and in H (forpes.ru explainer, "Hyper-Connections":
+ * the n streams are mixed by an n x n matrix), so these are its two partial
+ * derivatives by the chain rule: the transposed mix of grad_out, and the
+ * per-token outer product of grad_out and x summed over the width C.  In mHC
+ * grad_H then flows into the projection's backward (mhc_birkhoff_bwd).
  *
  *   x, grad_out  [T,n,C] bf16, device;  H [T,n,n] fp32, device
  *   grad_x       [T,n,C] bf16, device, must not overlap the inputs
- *   grad_H       [T,n,n] fp32, device
- *   n == 4, C % 8 == 0 as above.
+ *   grad_H       [T,n,n] fp32, device, must not overlap any other tensor
+ *   0 <= T <= MHC_MAX_TOKENS, n == 4, C % 8 == 0 as above.
  */
 mhc_status mhc_stream_mix_bwd(const void* x, const float* H, const void* grad_out,
                               void* grad_x, float* grad_H, int64_t T, int32_t n, int64_t C,
@@ -265,7 +285,7 @@ mhc_status mhc_stream_mix_bwd(const void* x, const float* H, const void* grad_ou
  * + matmul + activation, mixed precision).  Layouts are row-major; bf16 for
  * the activations and W, fp32 for the small per-token tensors. */
 typedef struct {
-    int64_t T;        /* tokens, >= 0 */
+    int64_t T;        /* tokens, 0 .. MHC_MAX_TOKENS */
     int32_t n;        /* streams, must be 4 */
     int64_t C;        /* stream width, a positive multiple of 64 */
     float eps;        /* RMSNorm epsilon, > 0 (1e-6 in the reference workload) */

@@ -28,13 +28,13 @@ int main(void)
     mhc_proj_opts o;
     mhc_layer_args la;
 
-    CHECK(mhc_abi_version() == 2);
+    CHECK(mhc_abi_version() == 3);
     CHECK(strcmp(mhc_status_string(MHC_OK), "ok") == 0);
     CHECK(strcmp(mhc_status_string(MHC_ERR_INVALID_ARGUMENT), "invalid argument") == 0);
     CHECK(mhc_last_error() != NULL);
 
     CHECK(mhc_proj_opts_default(&o) == MHC_OK);
-    CHECK(o.solver == MHC_SOLVER_NEWTON && o.max_iters == 30 && o.warm_sweeps == -1);
+    CHECK(o.solver == MHC_SOLVER_NEWTON && o.max_iters == -1 && o.warm_sweeps == -1);
     CHECK(o.tol > 0.9e-6f && o.tol < 1.1e-6f);
     CHECK(mhc_proj_opts_default(NULL) == MHC_ERR_INVALID_ARGUMENT);
 
@@ -50,8 +50,16 @@ int main(void)
     CHECK(mhc_birkhoff_fwd(NULL, FAKE(0), 5, NULL, NULL, NULL) == MHC_ERR_INVALID_ARGUMENT);
     CHECK(mhc_birkhoff_fwd(FAKE(4), FAKE(4096), 5, NULL, NULL, NULL) == MHC_ERR_INVALID_ARGUMENT);
     CHECK(mhc_birkhoff_fwd(FAKE(0), FAKE(64), 5, NULL, NULL, NULL) == MHC_ERR_INVALID_ARGUMENT);
-    o.max_iters = -1;
+    o.max_iters = -2;
     CHECK(mhc_birkhoff_fwd(FAKE(0), FAKE(0), 5, &o, NULL, NULL) == MHC_ERR_INVALID_ARGUMENT);
+    o.max_iters = -1;
+    /* size limits */
+    CHECK(mhc_birkhoff_bwd(FAKE(0), FAKE(8192), FAKE(16384), MHC_MAX_BATCH + 1, NULL) ==
+          MHC_ERR_INVALID_ARGUMENT);
+    CHECK(strstr(mhc_last_error(), "out of range") != NULL);
+    CHECK(mhc_stream_mix(FAKE(0), FAKE(8192), NULL, FAKE(16384), MHC_MAX_TOKENS + 1, 4, 64, NULL,
+                         NULL) == MHC_ERR_INVALID_ARGUMENT);
+    CHECK(strstr(mhc_last_error(), "out of range") != NULL);
     CHECK(mhc_birkhoff_bwd(FAKE(0), NULL, FAKE(0), 3, NULL) == MHC_ERR_INVALID_ARGUMENT);
     CHECK(mhc_birkhoff_bwd_recompute(FAKE(0), FAKE(8192), FAKE(64), 3, NULL, NULL) ==
           MHC_ERR_INVALID_ARGUMENT);

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_strings(L):
-    assert L.mhc_abi_version() == 2
+    assert L.mhc_abi_version() == 3
     assert L.mhc_status_string(0) == b"ok"
     assert L.mhc_status_string(1) == b"invalid argument"
     assert L.mhc_status_string(2) == b"unsupported"
@@ -47,7 +47,8 @@ def test_abi_version_and_strings(L):
 def test_default_opts(L):
     o = ProjOpts()
     assert L.mhc_proj_opts_default(ctypes.byref(o)) == 0
-    assert (o.solver, o.max_iters, o.warm_sweeps) == (0, 30, -1)
+    # -1: the solver's own limits (30 Newton iterations, 1000 Sinkhorn sweeps)
+    assert (o.solver, o.max_iters, o.warm_sweeps) == (0, -1, -1)
     assert abs(o.tol - 1e-6) < 1e-12
     assert L.mhc_proj_opts_default(None) == INVALID
 
@@ -73,7 +74,7 @@ def test_fwd_argument_errors(L):
     # partial overlap of P and logits
     assert L.mhc_birkhoff_fwd(FAKE, FAKE + 64, 5, None, None, None) == INVALID
     assert "overlap" in _err(L)
-    for field, value in (("solver", 3), ("max_iters", 0), ("max_iters", 10001),
+    for field, value in (("solver", 3), ("max_iters", 0), ("max_iters", -2), ("max_iters", 10001),
                          ("tol", -1.0), ("tol", float("nan")), ("warm_sweeps", 65),
                          ("warm_sweeps", -2)):
         o = ProjOpts()
@@ -244,3 +245,55 @@ def test_layer_argument_errors(L):
     a.T = 0
     assert L.mhc_layer_fwd(ctypes.byref(a), None) == 0
     assert L.mhc_layer_bwd(ctypes.byref(a), None) == 0
+
+
+def _header_int(name):
+    m = re.search(r"#define\s+" + name + r"\s+\(\(int64_t\)(\d+)\)", open(HEADER).read())
+    assert m, name
+    return int(m.group(1))
+
+
+def test_size_limits_at_the_boundary(L):
+    """B and T one past MHC_MAX_BATCH / MHC_MAX_TOKENS are rejected as out of
+    range before anything else is looked at; at the limit the check passes and
+    the (misaligned) pointers are what fails.  The limits keep every launch
+    below 2^32 work-items: 4 lanes per matrix in the 4x4 backward, 16 per
+    token in the token kernels."""
+    MB, MT = _header_int("MHC_MAX_BATCH"), _header_int("MHC_MAX_TOKENS")
+    assert MB == (1 << 30) - 64 and 4 * MB < (1 << 32)
+    assert MT == (1 << 28) - 16 and 16 * MT < (1 << 32)
+    bad = FAKE + 2  # misaligned for every call (4x4: 16 bytes, n x n: 4): fails after the range check
+    calls = [
+        lambda b: L.mhc_birkhoff_fwd(bad, bad, b, None, None, None),
+        lambda b: L.mhc_birkhoff_bwd(bad, bad, bad, b, None),
+        lambda b: L.mhc_birkhoff_bwd_recompute(bad, bad, bad, b, None, None),
+        lambda b: L.mhc_birkhoff_fwd_bwd(bad, bad, bad, bad, b, None, None, None),
+        lambda b: L.mhc_birkhoff_fwd_n(bad, bad, b, 3, None, None, None),
+        lambda b: L.mhc_birkhoff_bwd_n(bad, bad, bad, b, 3, None),
+    ]
+    for call in calls:
+        assert call(MB + 1) == INVALID and "out of range" in _err(L)
+        assert call(MB) == INVALID and "out of range" not in _err(L)
+    tcalls = [
+        lambda t: L.mhc_stream_mix(bad, bad, None, bad, t, 4, 64, None, None),
+        lambda t: L.mhc_stream_mix_bwd(bad, bad, bad, bad, bad, t, 4, 64, None),
+    ]
+    for call in tcalls:
+        assert call(MT + 1) == INVALID and "out of range" in _err(L)
+        assert call(MT) == INVALID and "out of range" not in _err(L)
+    assert L.mhc_layer_workspace_bytes(MT + 1, 4, 64) == -1
+    assert L.mhc_layer_workspace_bytes(MT, 4, 64) > 0
+
+
+def test_sinkhorn_default_sweeps_resolved_by_the_library(L):
+    """max_iters = -1 (the default) with the Sinkhorn solver is accepted; an
+    explicit count is range-checked whatever the solver."""
+    o = ProjOpts()
+    L.mhc_proj_opts_default(ctypes.byref(o))
+    o.solver = 1
+    # passes option validation, then fails on the NULL pointers
+    assert L.mhc_birkhoff_fwd(None, FAKE, 5, ctypes.byref(o), None, None) == INVALID
+    assert "NULL" in _err(L)
+    o.max_iters = 10001
+    assert L.mhc_birkhoff_fwd(None, FAKE, 5, ctypes.byref(o), None, None) == INVALID
+    assert "max_iters" in _err(L)
