@@ -25,7 +25,7 @@ project takes where they are silent:
 Backward for upstream (dx_out, du), by the chain rule in float64, with the
 projection's gradient from oracle.birkhoff.birkhoff_project_bwd.  Pinned by
 central finite differences of a scalar loss on tiny shapes
-(tests/test_oracle_layer.py); beyond that composition the full-size layer is
+(tests/test_oracle_mix_layer.py); beyond that composition the full-size layer is
 parity unpinned except through its pinned parts.
 """
 from __future__ import annotations
@@ -41,10 +41,12 @@ def _sigmoid(z):
     return 1.0 / (1.0 + np.exp(-z))
 
 
-def layer_fwd(x, W, f, eps=EPS):
+def layer_fwd(x, W, f, eps=EPS, streams=True):
     """Forward of the layer step.  x [T,n,C], W [n*n+2n, n*C], f [T,C].
     Returns a dict with float64 arrays: rms [T], logits [T, n*n+2n],
-    H_pre [T,n], H_post [T,n], H_res [T,n,n], u [T,C], x_out [T,n,C]."""
+    H_pre [T,n], H_post [T,n], H_res [T,n,n], u [T,C], x_out [T,n,C].
+    With ``streams`` False, u and x_out are left out (the rest is computed
+    exactly as with them)."""
     x = np.asarray(x, dtype=np.float64)
     W = np.asarray(W, dtype=np.float64)
     f = np.asarray(f, dtype=np.float64)
@@ -57,16 +59,19 @@ def layer_fwd(x, W, f, eps=EPS):
     H_pre = _sigmoid(logits[:, :n])
     H_post = _sigmoid(logits[:, n:2 * n])
     H_res = birkhoff_project(logits[:, 2 * n:].reshape(T, n, n))
+    if not streams:
+        return dict(rms=rms, logits=logits, H_pre=H_pre, H_post=H_post, H_res=H_res)
     u = np.einsum("tj,tjc->tc", H_pre, x)
     x_out = H_post[:, :, None] * f[:, None, :] + np.einsum("tij,tjc->tic", H_res, x)
     return dict(rms=rms, logits=logits, H_pre=H_pre, H_post=H_post,
                 H_res=H_res, u=u, x_out=x_out)
 
 
-def layer_bwd(x, W, f, dx_out, du, fwd=None, eps=EPS):
+def layer_bwd(x, W, f, dx_out, du, fwd=None, eps=EPS, streams=True):
     """Backward of the layer step for upstream gradients dx_out [T,n,C] and
     du [T,C].  Returns dict(dx [T,n,C], dW [n*n+2n, n*C], df [T,C],
-    dlogits [T, n*n+2n])."""
+    dlogits [T, n*n+2n]).  With ``streams`` False, dx and df are left out
+    (dW and dlogits are computed exactly as with them)."""
     x = np.asarray(x, dtype=np.float64)
     W = np.asarray(W, dtype=np.float64)
     f = np.asarray(f, dtype=np.float64)
@@ -78,11 +83,9 @@ def layer_bwd(x, W, f, dx_out, du, fwd=None, eps=EPS):
     D = n * C
     H_pre, H_post, H_res, rms = fwd["H_pre"], fwd["H_post"], fwd["H_res"], fwd["rms"]
     # write-back and read-mix
-    df = np.einsum("ti,tic->tc", H_post, dx_out)
     dH_post = np.einsum("tic,tc->ti", dx_out, f)
     dH_res = np.einsum("tic,tjc->tij", dx_out, x)
     dH_pre = np.einsum("tc,tjc->tj", du, x)
-    dx = np.einsum("tij,tic->tjc", H_res, dx_out) + H_pre[:, :, None] * du[:, None, :]
     # maps -> logits
     dl_pre = dH_pre * H_pre * (1.0 - H_pre)
     dl_post = dH_post * H_post * (1.0 - H_post)
@@ -92,6 +95,10 @@ def layer_bwd(x, W, f, dx_out, du, fwd=None, eps=EPS):
     xf = x.reshape(T, D)
     xn = xf / rms[:, None]
     dW = dl.T @ xn
+    if not streams:
+        return dict(dW=dW, dlogits=dl)
+    df = np.einsum("ti,tic->tc", H_post, dx_out)
+    dx = np.einsum("tij,tic->tjc", H_res, dx_out) + H_pre[:, :, None] * du[:, None, :]
     dxn = dl @ W
     # xn = x / sqrt(mean(x^2) + eps)
     proj = (dxn * xn).sum(axis=1) / D

@@ -164,20 +164,28 @@ def test_closed_forms_on_gpu(gpu_lib):
 
 
 def test_extreme_logits(gpu_lib):
-    """Very large magnitudes (N(0,40^2), far beyond the workloads): outputs
-    stay finite and doubly stochastic to 1e-4; matrices the solver reports
-    converged match the oracle to 1e-5; at most a few percent stop at the
-    fp32 noise floor (flag 255)."""
+    """Very large magnitudes (N(0,40^2), far beyond the workloads).  Every
+    matrix, flagged or not, is within the 1e-5 projection bar of the oracle
+    with row and column sums within 1e-5.  A matrix is flagged 255 only at the
+    fp32 noise floor: its column residual is above tol = 1e-6 but below 4e-6,
+    where the solver stops because no trial lowers the residual any more.
+    Here the potentials reach the hundreds of base-2 units and the
+    max-shifted evaluation's rounding leaves about 1 % of the matrices there
+    (column residuals 1.0-2.2e-6, errors below 2e-6 against the oracle), so
+    at least 98.5 % must reach tol."""
     A = (40.0 * np.random.Generator(np.random.PCG64(34)).standard_normal((4096, 4, 4))).astype(np.float32)
     P, it = _fwd(gpu_lib, A)
     assert np.isfinite(P).all()
-    P64 = P.astype(np.float64)
-    assert np.abs(P64.sum(-1) - 1).max() <= 1e-4 and np.abs(P64.sum(-2) - 1).max() <= 1e-4
-    ok = it != 255
-    assert ok.mean() > 0.95
     ref = birkhoff_project(A.astype(np.float64))
-    assert_fwd(P[ok], ref[ok], label="N(0,40^2) converged")
-    assert np.abs(P64 - ref).max() <= 1e-4
+    assert_fwd(P, ref, label="N(0,40^2)")
+    ok = it != 255
+    assert ok.mean() >= 0.985, f"converged {ok.mean():.4f}"
+    cres = np.abs(P.astype(np.float64).sum(-2) - 1).max(-1)
+    # (the kernel's fp32 residual is <= tol; summing the stored entries in
+    # float64 moves it by a few roundings of 1)
+    assert cres[ok].max() <= 1.5e-6, f"converged column residual {cres[ok].max():.2e}"
+    if (~ok).any():
+        assert cres[~ok].max() <= 4e-6, f"flagged column residual {cres[~ok].max():.2e}"
 
 
 def test_inplace_alias(gpu_lib):
@@ -380,7 +388,12 @@ def test_huge_logits(gpu_lib, sigma):
     units, where the oracle's Jacobian turns singular: outputs finite, rows
     stochastic, at least 97 % of matrices converged with column sums within
     SUM_TOL, every column sum within 1e-4 (no column left empty).  At 100 the
-    potentials sit in the hundreds, where fp32 steps can stall."""
+    potentials sit in the hundreds, where fp32 steps can stall; there a
+    seeded sample of 64 converged matrices is also compared with the oracle at
+    the 1e-5 bar (P is unique, so the doubly stochastic properties alone could
+    pass a wrong matrix).  At 1000 the row spreads reach thousands of natural
+    units and the oracle's own 50-digit solve turns numerically singular, so
+    only the properties are checked."""
     A = (sigma * np.random.Generator(np.random.PCG64(42)).standard_normal((4096, 4, 4))).astype(np.float32)
     P, it = _fwd(gpu_lib, A)
     assert np.isfinite(P).all() and (P >= 0).all()
@@ -390,3 +403,8 @@ def test_huge_logits(gpu_lib, sigma):
     assert np.abs(P64.sum(-1) - 1).max() <= SUM_TOL
     assert np.abs(P64[ok].sum(-2) - 1).max() <= SUM_TOL
     assert np.abs(P64.sum(-2) - 1).max() <= 1e-4
+    if sigma == 100.0:
+        conv = np.nonzero(ok)[0]
+        idx = np.sort(np.random.Generator(np.random.PCG64(420)).choice(conv, 64, replace=False))
+        ref = birkhoff_project(A[idx].astype(np.float64))
+        assert_fwd(P[idx], ref, label="N(0,100^2) sample")

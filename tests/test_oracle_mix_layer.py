@@ -173,3 +173,27 @@ def test_layer_bwd_torch_autograd():
     np.testing.assert_allclose(g["dx"], tx.grad.numpy(), atol=1e-10)
     np.testing.assert_allclose(g["dW"], tW.grad.numpy(), atol=1e-10)
     np.testing.assert_allclose(g["df"], tf.grad.numpy(), atol=1e-10)
+
+
+def test_layer_without_streams_matches():
+    """layer_fwd / layer_bwd with streams=False return the same maps,
+    logits gradient and dW as the full computation (they only skip u, x_out,
+    dx and df)."""
+    from oracle.layer import layer_bwd, layer_fwd
+    g = np.random.Generator(np.random.PCG64(91))
+    T, C = 9, 16
+    x = g.standard_normal((T, 4, C))
+    W = g.standard_normal((24, 4 * C)) * 0.3
+    f = g.standard_normal((T, C))
+    dxo = g.standard_normal((T, 4, C))
+    du = g.standard_normal((T, C))
+    a = layer_fwd(x, W, f)
+    b = layer_fwd(x, W, f, streams=False)
+    assert set(b) == {"rms", "logits", "H_pre", "H_post", "H_res"}
+    for k in b:
+        np.testing.assert_array_equal(a[k], b[k])
+    ga = layer_bwd(x, W, f, dxo, du, fwd=a)
+    gb = layer_bwd(x, W, f, dxo, du, fwd=b, streams=False)
+    assert set(gb) == {"dW", "dlogits"}
+    for k in gb:
+        np.testing.assert_array_equal(ga[k], gb[k])
