@@ -55,6 +55,7 @@ SIGNATURES = {
     "mhc_layer_workspace_bytes": (c_int64, [c_int64, c_int32, c_int64]),
     "mhc_layer_fwd": (c_int32, [ctypes.POINTER(LayerArgs), c_void_p]),
     "mhc_layer_bwd": (c_int32, [ctypes.POINTER(LayerArgs), c_void_p]),
+    "mhc_layer_bwd_noalloc": (c_int32, [ctypes.POINTER(LayerArgs), c_void_p]),
     "mhc_status_string": (ctypes.c_char_p, [c_int32]),
     "mhc_last_error": (ctypes.c_char_p, []),
     "mhc_abi_version": (c_int32, []),

@@ -346,7 +346,8 @@ mhc_status mhc_layer_fwd(const mhc_layer_args* a, void* stream)
 }
 
 // The backward's pointer checks: NULL, alignment, overlaps.  `ws`/`ws_bytes`
-// is the workspace to include in the overlap test (NULL: none).
+// is the workspace to include in the overlap test (NULL: none, as for
+// mhc_layer_bwd_noalloc, whose workspace is the library's own).
 static mhc_status check_layer_bwd(const mhc_layer_args* a, const void* ws, size_t ws_bytes)
 {
     const size_t T = (size_t)a->T, C = (size_t)a->C;
@@ -393,6 +394,43 @@ mhc_status mhc_layer_bwd(const mhc_layer_args* a, void* stream)
     return launched(mhc::launch_layer_bwd(layer_bwd_ptrs(a, a->workspace), a->T, a->C,
                                           (hipStream_t)stream),
                     "layer_bwd launch");
+}
+
+static_assert(MHC_LAYER_NOALLOC_SCRATCH_BYTES == mhc::kLayerNoAllocScratchBytes,
+              "header and library agree on the no-alloc scratch size");
+
+mhc_status mhc_layer_bwd_noalloc(const mhc_layer_args* a, void* stream)
+{
+    if (a == nullptr) return fail(MHC_ERR_INVALID_ARGUMENT, "args is NULL");
+    mhc_status s = check_layer_shape(a->T, a->n, a->C);
+    if (s != MHC_OK) return s;
+    if (a->T == 0) return ok();
+    const int64_t need = mhc::layer_plan(a->T, a->C).bytes;
+    if (need > mhc::kLayerNoAllocScratchBytes)
+        return fail(MHC_ERR_INVALID_ARGUMENT,
+                    "T=%lld, C=%lld needs %lld bytes of scratch; mhc_layer_bwd_noalloc holds "
+                    "%lld (use mhc_layer_bwd with a workspace)",
+                    (long long)a->T, (long long)a->C, (long long)need,
+                    (long long)mhc::kLayerNoAllocScratchBytes);
+    s = check_layer_bwd(a, nullptr, 0);
+    if (s != MHC_OK) return s;
+    // the scratch array of the device the work runs on, which must be current
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return launched(e, "layer_bwd_noalloc: hipGetDevice");
+    if (stream != nullptr) {
+        int sdev = -1;
+        e = hipStreamGetDevice((hipStream_t)stream, &sdev);
+        if (e != hipSuccess) return launched(e, "layer_bwd_noalloc: hipStreamGetDevice");
+        if (sdev != dev)
+            return fail(MHC_ERR_INVALID_ARGUMENT,
+                        "stream belongs to device %d but device %d is current", sdev, dev);
+    }
+    void* ws = nullptr;
+    e = mhc::layer_noalloc_scratch(dev, &ws);
+    if (e != hipSuccess) return launched(e, "layer_bwd_noalloc: scratch address");
+    return launched(mhc::launch_layer_bwd(layer_bwd_ptrs(a, ws), a->T, a->C, (hipStream_t)stream),
+                    "layer_bwd_noalloc launch");
 }
 
 const char* mhc_status_string(mhc_status s)

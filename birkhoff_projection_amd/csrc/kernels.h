@@ -62,6 +62,14 @@ struct LayerPlan {
 };
 
 LayerPlan layer_plan(int64_t T, int64_t C);
+
+// Size of the device array that mhc_layer_bwd_noalloc uses as its workspace
+// (one per GPU, for the life of the process): shapes whose layer_plan bytes
+// exceed it are refused.
+constexpr int64_t kLayerNoAllocScratchBytes = (int64_t)64 << 20;
+// Device address of that array on `device`, which must be the current device
+// (looked up once per device, then cached; thread-safe).
+hipError_t layer_noalloc_scratch(int device, void** ptr);
 hipError_t launch_layer_fwd(const LayerPtrs& a, int64_t T, int64_t C, float eps,
                             const SolverOpts& o, hipStream_t stream);
 hipError_t launch_layer_bwd(const LayerPtrs& a, int64_t T, int64_t C, hipStream_t stream);

@@ -29,6 +29,9 @@
 // grad_logits is fp32 and enters MFMA as the sum of two bf16 halves (hi +
 // lo, about 16 significant bits), so its products keep fp32-level accuracy.
 // Accumulation is fp32 throughout.
+#include <atomic>
+#include <mutex>
+
 #include "kernels.h"
 #include "proj4.h"
 
@@ -918,6 +921,42 @@ hipError_t launch_layer_fwd(const LayerPtrs& a, int64_t T, int64_t C, float eps,
                        (const uint4*)a.f, a.H_pre, a.H_post, a.H_res, (uint4*)a.u,
                        (uint4*)a.x_out, T, C / 8);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free backward (mhc_layer_bwd_noalloc): the same
+// workspace layout as layer_plan's, held in this file-scope device array
+// instead of caller memory.  Every GPU the library runs on holds its own copy
+// (kLayerNoAllocScratchBytes, allocated when the code object is loaded and
+// kept until the process ends).  In host code `scratch` names a host-side
+// stand-in, not device memory, so its device address is looked up once per
+// device with hipGetSymbolAddress and only that address is ever passed on.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kLayerNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+}  // namespace
+
+hipError_t layer_noalloc_scratch(int device, void** ptr)
+{
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    void* p = g_scratch_ptr[device].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch_ptr[device].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            // the caller has made `device` current
+            const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (p == nullptr) return hipErrorInvalidSymbol;
+            g_scratch_ptr[device].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return hipSuccess;
 }
 
 hipError_t launch_layer_bwd(const LayerPtrs& a, int64_t T, int64_t C, hipStream_t stream)

@@ -375,3 +375,15 @@ def layer_bwd(x, W, f, fwd, grad_x_out, grad_u, *, workspace=None, out=None):
     with torch.cuda.device(dev):
         check(lib().mhc_layer_bwd(ctypes.byref(a), _stream(dev)))
     return out
+
+
+def layer_bwd_noalloc(x, W, f, fwd, grad_x_out, grad_u, *, out=None):
+    """layer_bwd through mhc_layer_bwd_noalloc: the same result, with the
+    library's own device scratch as the workspace (nothing is allocated by the
+    call; pass ``out`` to allocate nothing here either).  Calls that overlap
+    in time on one GPU share that scratch and race."""
+    a, out = _layer_bwd_args(x, W, f, fwd, grad_x_out, grad_u, out)
+    a.workspace, a.workspace_bytes = None, 0
+    with torch.cuda.device(x.device):
+        check(lib().mhc_layer_bwd_noalloc(ctypes.byref(a), _stream(x.device)))
+    return out

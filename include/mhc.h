@@ -332,6 +332,28 @@ mhc_status mhc_layer_fwd(const mhc_layer_args* a, void* stream);
  * use by another call that overlaps on the device. */
 mhc_status mhc_layer_bwd(const mhc_layer_args* a, void* stream);
 
+/* mhc_layer_bwd_noalloc -- mhc_layer_bwd for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  It computes exactly what mhc_layer_bwd computes,
+ * with the same kernels, but its workspace is a device array inside the
+ * library (MHC_LAYER_NOALLOC_SCRATCH_BYTES, one per GPU, held from the
+ * library's first use on that GPU until the process ends) instead of
+ * a->workspace, which is ignored together with a->workspace_bytes.  The call
+ * itself allocates nothing.
+ *
+ *  - Shapes whose workspace (mhc_layer_workspace_bytes) exceeds the array are
+ *    refused with MHC_ERR_INVALID_ARGUMENT; at C = 7168 that admits up to
+ *    about 200000 tokens per call.
+ *  - The work runs on the current device; a non-NULL stream must belong to
+ *    it (else MHC_ERR_INVALID_ARGUMENT).
+ *  - Every call on one GPU shares that GPU's array: calls that overlap in
+ *    time on one GPU (concurrent streams, several host threads) race and give
+ *    undefined results.  Calls ordered on one stream are safe.  Nothing in the
+ *    array needs to start at zero; each call overwrites what it reads.
+ * Other arguments, outputs and errors as for mhc_layer_bwd. */
+#define MHC_LAYER_NOALLOC_SCRATCH_BYTES ((int64_t)67108864) /* 64 MiB */
+mhc_status mhc_layer_bwd_noalloc(const mhc_layer_args* a, void* stream);
+
 const char* mhc_status_string(mhc_status s);
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char* mhc_last_error(void);

@@ -297,3 +297,31 @@ def test_sinkhorn_default_sweeps_resolved_by_the_library(L):
     o.max_iters = 10001
     assert L.mhc_birkhoff_fwd(None, FAKE, 5, ctypes.byref(o), None, None) == INVALID
     assert "max_iters" in _err(L)
+
+
+def test_layer_bwd_noalloc_refuses_before_touching_the_device(L):
+    """mhc_layer_bwd_noalloc checks the shape against its fixed scratch
+    (MHC_LAYER_NOALLOC_SCRATCH_BYTES) and the pointers on the host, before it
+    asks for a device (fake pointers, never dereferenced)."""
+    m = re.search(r"#define\s+MHC_LAYER_NOALLOC_SCRATCH_BYTES\s+\(\(int64_t\)(\d+)\)",
+                  open(HEADER).read())
+    assert m and int(m.group(1)) == 64 << 20
+    a = _lib.LayerArgs()
+    a.T, a.n, a.C, a.eps = 262144, 4, 7168, 1e-6
+    assert L.mhc_layer_workspace_bytes(a.T, 4, a.C) > 64 << 20
+    names = ["x", "W", "f", "u", "x_out", "rms", "logits", "H_pre", "H_post", "H_res",
+             "grad_x_out", "grad_u", "grad_x", "grad_f", "grad_W", "grad_logits"]
+    for i, nm in enumerate(names):
+        setattr(a, nm, FAKE + (i + 1) * (1 << 36))
+    assert L.mhc_layer_bwd_noalloc(ctypes.byref(a), None) == INVALID
+    assert "scratch" in _err(L)
+    a.T = 65536  # fits (49.6 MiB), but an output overlapping an input is refused
+    assert 0 < L.mhc_layer_workspace_bytes(a.T, 4, a.C) <= 64 << 20
+    a.grad_x = a.x
+    assert L.mhc_layer_bwd_noalloc(ctypes.byref(a), None) == INVALID
+    assert "overlaps" in _err(L)
+    a.n = 3
+    assert L.mhc_layer_bwd_noalloc(ctypes.byref(a), None) == UNSUPPORTED
+    a.n, a.T = 4, 0
+    assert L.mhc_layer_bwd_noalloc(ctypes.byref(a), None) == 0
+    assert L.mhc_layer_bwd_noalloc(None, None) == INVALID
