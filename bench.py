@@ -9,13 +9,18 @@ reads from HBM rather than from the 256 MB last-level cache.
 
 Prints one JSON line:
   value        projections per second (fwd+bwd), whole job
-  roofline     for the dominant kernel, the forward solve, which is bound by
-               vector-ALU issue: its VALU issue slots per launch (from the
-               counter run of this kernel on this workload) / its average
-               HIP-event duration, against the fp32 vector peak
+  roofline     for the dominant kernel, the forward solve: its algorithmic
+               bytes per launch (128 per matrix) / its average HIP-event
+               duration, against 8 TB/s, with the counter-measured HBM bytes
+               as `traffic`.  The kernel reaches neither that roof nor the
+               vector-ALU one (`roofline.valu` gives its issue-slot fraction):
+               it is limited by latency -- one generation of waves, two per
+               SIMD, whose load phase no solve overlaps
   hbm          algorithmic GB/s of fwd, bwd and the step against 8 TB/s, and
                the counter-measured HBM bytes per launch
   iters        Newton iterations per matrix and per wave (divergence)
+  config3      the same fwd+bwd step on 1,048,576 mixed-difficulty matrices,
+               timed in the same run (the other end of the 128K-1M range)
   cpu_baseline the float64 oracle (fwd+bwd) on the host cores, on a bounded
                sample of the same batch
 
@@ -44,6 +49,13 @@ VALU_PEAK_SLOTS = 157.3e12 / 128.0
 TRANS_SLOTS = 4
 FWD_BYTES = 128   # per matrix: 64 B logits in, 64 B P out
 BWD_BYTES = 192   # per matrix: P and dL/dP in, dL/dA out
+# Dense bf16 MFMA peak of MI355X (no sparsity), and the flops of one
+# v_mfma_f32_16x16x32_bf16 instruction (2 x 16 x 16 x 32).
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_FLOPS_PER_INSTR = 2 * 16 * 16 * 32
+# Host cores a one-GPU machine gives this process: the CPU baselines run at most
+# this many worker processes, whatever the machine's own count.
+CPU_SHARE = 16
 
 # Per-launch figures from rocprofv3 counter runs (profiles/ holds the
 # summaries and the commands): HBM bytes from FETCH_SIZE and WRITE_SIZE, each
@@ -107,11 +119,25 @@ def _cpu_worker(args):
     return A.shape[0]
 
 
+def host_cores():
+    """(worker processes used, cores visible to this process)."""
+    visible = len(os.sched_getaffinity(0))
+    return min(visible, CPU_SHARE), visible
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # threadpoolctl missing: report unknown
+        return None
+
+
 def cpu_baseline_projection(A, G, n_sample, label):
     """Time the oracle's fwd+bwd on n_sample matrices (the batch repeated if
     n_sample exceeds it) over a process pool on the host cores."""
     import multiprocessing as mp
-    cores = min(len(os.sched_getaffinity(0)), 16)
+    cores, visible = host_cores()
     n = n_sample
     idx = np.arange(n) % A.shape[0]
     chunks = np.array_split(idx, cores * 4)
@@ -126,16 +152,66 @@ def cpu_baseline_projection(A, G, n_sample, label):
     t1 = time.perf_counter()
     _cpu_worker((A[:n1], G[:n1]))
     dt1 = time.perf_counter() - t1
-    try:
-        from threadpoolctl import threadpool_info
-        blas = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:  # threadpoolctl missing: report unknown
-        blas = None
     return {"value": done / dt, "unit": "projections/s", "cores": cores, "kind": "oracle",
             "sample": f"{done} matrices ({done / A.shape[0]:g} passes over the {A.shape[0]} "
                       f"{label} batch), fwd+bwd, float64, {dt:.1f} s wall on {cores} processes",
             "single_core": {"value": n1 / dt1, "sample": f"first {n1} matrices, one process"},
-            "blas_threads": blas}
+            "host_cores_visible": visible,
+            "pool_note": f"process pool capped at the {CPU_SHARE}-core host share of one GPU",
+            "blas_threads": _blas_threads()}
+
+
+# Host copy of the token sample the per-token CPU baselines run on; worker
+# processes inherit it through fork and receive only index ranges.
+_TOKENS = None
+
+
+def _cpu_tokens_worker(args):
+    """Oracle on one range of the token sample, one BLAS thread per process:
+    'mix' = projection + stream mix (the fused workload), 'layer' = layer
+    step forward + backward."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    kind, lo, hi = args
+    with threadpool_limits(1):
+        if kind == "mix":
+            x, logits = _TOKENS
+            H = oracle.birkhoff_project(logits[lo:hi].astype(np.float64))
+            oracle.stream_mix(H, x[lo:hi].astype(np.float64))
+        else:
+            x, Wm, f, dxo, du = _TOKENS
+            x64, W64, f64 = (a.astype(np.float64) for a in (x[lo:hi], Wm, f[lo:hi]))
+            fw = oracle.layer_fwd(x64, W64, f64)
+            oracle.layer_bwd(x64, W64, f64, dxo[lo:hi].astype(np.float64),
+                             du[lo:hi].astype(np.float64), fwd=fw)
+    return hi - lo
+
+
+def cpu_baseline_tokens(kind, tokens, n, T_total, label):
+    """Per-token oracle throughput on the first ``n`` tokens of the host
+    sample ``tokens`` (a tuple of float32 arrays, the workload's own inputs)
+    over a process pool; the tokens/s is the sample's, and the whole
+    workload's time is extrapolated from it and labelled as such."""
+    import multiprocessing as mp
+    global _TOKENS
+    cores, visible = host_cores()
+    _TOKENS = tokens
+    bounds = np.linspace(0, n, 4 * cores + 1).astype(int)
+    work = [(kind, int(a), int(b)) for a, b in zip(bounds[:-1], bounds[1:]) if b > a]
+    ctx = mp.get_context("fork")
+    with ctx.Pool(cores) as pool:
+        t0 = time.perf_counter()
+        done = sum(pool.map(_cpu_tokens_worker, work))
+        dt = time.perf_counter() - t0
+    _TOKENS = None
+    rate = done / dt
+    return {"value": rate, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"the first {done} of the {T_total} tokens ({label}), float64, "
+                      f"{dt:.1f} s wall on {cores} processes with one BLAS thread each"
+                      + (f"; extrapolated, the whole workload would take {T_total / rate:.0f} s"
+                         if done < T_total else ""),
+            "extrapolated": done < T_total, "host_cores_visible": visible,
+            "pool_note": f"process pool capped at the {CPU_SHARE}-core host share of one GPU"}
 
 
 def time_projection(bp, torch, A_np, G_np, steps, warmup, solver="newton", recompute=False, n=4,
@@ -349,22 +425,7 @@ def bench_projection(args, bp, torch, config):
     kname = "birkhoff_fwd_bwd (fused Newton + backward)" if args.fused else "birkhoff_fwd (Newton)"
     m_fwd = measured(fwd_key)
     m_bwd = None if (args.recompute or args.fused) else measured(f"birkhoff_bwd{tag}_{B}_cfg{config}")
-    # the forward solve is bound by vector-ALU issue (transcendental-heavy
-    # Newton iterations), not by its 128 bytes per matrix
-    if m_fwd is not None:
-        slots = m_fwd["valu"] + (TRANS_SLOTS - 1) * m_fwd["trans"]
-        achieved = slots / (fwd_avg / 1e3)
-        roofline = {"bound": "alu", "kernel": kname, "achieved": achieved,
-                    "peak": VALU_PEAK_SLOTS, "unit": "wave64 VALU issue slots/s",
-                    "frac": achieved / VALU_PEAK_SLOTS,
-                    "traffic": m_fwd["fetch"] + m_fwd["write"]}
-        valu = {"instructions_per_launch": m_fwd["valu"], "transcendental": m_fwd["trans"],
-                "issue_slots_per_launch": slots, "slots_per_matrix": slots / B}
-    else:
-        roofline = {"bound": "alu", "kernel": kname, "achieved": None,
-                    "peak": VALU_PEAK_SLOTS, "unit": "wave64 VALU issue slots/s", "frac": None,
-                    "traffic": None, "note": "kernel changed since its counters were taken"}
-        valu = None
+    roofline, valu = forward_roofline(kname, fwd_bytes * B, fwd_avg, B, m_fwd)
     out = {
         "metric": "4x4 projections/sec fwd+bwd at 128K batch; achieved HBM GB/s vs peak",
         "value": value, "unit": "projections/s", "n_gpus": 1, "steps": args.steps,
@@ -390,10 +451,63 @@ def bench_projection(args, bp, torch, config):
         "valu": valu,
         "iters": iteration_stats(bp, torch, A, n),
     }
+    if config == 2 and n == 4 and not (args.recompute or args.fused) and not args.no_config3:
+        out["config3"] = config3_block(args, bp, torch)
     if not args.no_cpu_baseline:
         sample = args.cpu_sample if n == 4 else max(args.cpu_sample * 16 // (n * n * 4), 16384)
         out["cpu_baseline"] = cpu_baseline_projection(A, G, sample, label)
     return out
+
+
+def forward_roofline(kname, alg_bytes, fwd_ms, B, m):
+    """Roofline of the forward solve: algorithmic bytes per launch over its
+    average duration against the HBM peak, and beside it the vector-ALU view
+    (issue slots per launch from the counter run of this kernel on this
+    workload, over the same duration, against the fp32 vector issue peak).
+    It reaches neither roof: with one generation of waves, two per SIMD, the
+    load phase of every wave finishes before any solve starts and each wave
+    then runs until its slowest matrix is done (latency, not throughput)."""
+    achieved = alg_bytes / (fwd_ms / 1e3) / 1e9
+    roof = {"bound": "hbm", "kernel": kname, "achieved": achieved, "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+            "traffic": m["fetch"] + m["write"] if m else None,
+            "algorithmic_bytes": alg_bytes, "limiter": "latency"}
+    if m is None:
+        roof["valu"] = None
+        roof["note"] = "kernel changed since its counters were taken: traffic and VALU unknown"
+        return roof, None
+    slots = m["valu"] + (TRANS_SLOTS - 1) * m["trans"]
+    rate = slots / (fwd_ms / 1e3)
+    roof["valu"] = {"achieved": rate, "peak": VALU_PEAK_SLOTS, "unit": "wave64 VALU issue slots/s",
+                    "frac": rate / VALU_PEAK_SLOTS}
+    valu = {"instructions_per_launch": m["valu"], "transcendental": m["trans"],
+            "issue_slots_per_launch": slots, "slots_per_matrix": slots / B}
+    return roof, valu
+
+
+def config3_block(args, bp, torch):
+    """The fwd+bwd step on the 1,048,576-matrix mixed-difficulty batch,
+    timed in the same run as the headline (same method: rotated buffer sets
+    past the last-level cache, HIP-graph replay, HIP events)."""
+    import workloads as W
+    A, G, _ = W.config3()
+    B = A.shape[0]
+    r = time_projection(bp, torch, A, G, args.steps, args.warmup)
+    ms = r["total_ms"] / args.steps
+    fwd_ms, bwd_ms = float(r["fwd_ms"]), float(r["bwd_ms"])
+    step_gbs = (FWD_BYTES + BWD_BYTES) * B / (ms / 1e3) / 1e9
+    m_fwd = measured(f"birkhoff_fwd_{B}_cfg3")
+    roof, valu = forward_roofline("birkhoff_fwd (Newton)", FWD_BYTES * B, fwd_ms, B, m_fwd)
+    return {"workload": f"birkhoff fwd+bwd, {B} 4x4 fp32 matrices, mixed difficulty (50 % N(0,1), "
+                        f"40 % N(0,10^2), 10 % N(0,1) + 20 I)",
+            "value": B / (ms / 1e3), "unit": "projections/s", "ms_per_step": ms,
+            "fwd_us": fwd_ms * 1e3, "bwd_us": bwd_ms * 1e3,
+            "step_GBs": step_gbs, "step_frac": step_gbs / HBM_PEAK_GBS,
+            "fwd_GBs": FWD_BYTES * B / (fwd_ms / 1e3) / 1e9,
+            "bwd_GBs": BWD_BYTES * B / (bwd_ms / 1e3) / 1e9,
+            "bwd_frac": BWD_BYTES * B / (bwd_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "step_us_median_of_5": r["step_ms_median"] * 1e3, "roofline_fwd": roof, "valu": valu,
+            "iters": iteration_stats(bp, torch, A)}
 
 
 def _time_loop(torch, body, steps, warmup):
@@ -411,6 +525,11 @@ def _time_loop(torch, body, steps, warmup):
     return start.elapsed_time(stop) / steps
 
 
+def _host_tokens(idx, *tensors):
+    """Host float32 copies of the given tokens of each device tensor."""
+    return tuple(t[idx].float().cpu().numpy() for t in tensors)
+
+
 def bench_mix(args, bp, torch):
     """Fused projection + stream mix, T=16384, C=4096 (logits N(0,2^2))."""
     import workloads as W
@@ -422,7 +541,8 @@ def bench_mix(args, bp, torch):
     per_tok = 64 + 4 * C * 2 + 64 + 4 * C * 2
     gbs = per_tok * T / (ms / 1e3) / 1e9
     m = measured(f"stream_mix_fwd_{T}x4x{C}")
-    return {
+    traffic = m["fetch"] + m["write"] if m else None
+    out = {
         "metric": "fused projection + stream mix tokens/s; achieved HBM GB/s vs peak",
         "value": T / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
@@ -430,8 +550,14 @@ def bench_mix(args, bp, torch):
         "config": {"workload": f"fused projection + stream mix, T={T}, n=4, C={C} bf16"},
         "roofline": {"bound": "hbm", "kernel": "stream_mix_fwd (fused Newton)", "achieved": gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                     "traffic": m["fetch"] + m["write"] if m else None},
+                     "traffic": traffic, "algorithmic_bytes": per_tok * T,
+                     "traffic_ratio": traffic / (per_tok * T) if traffic else None},
     }
+    if not args.no_cpu_baseline:
+        n = min(T, args.cpu_tokens_mix)
+        out["cpu_baseline"] = cpu_baseline_tokens("mix", _host_tokens(slice(0, n), x, logits), n, T,
+                                                  "projection of the logits + stream mix")
+    return out
 
 
 def bench_mix_bwd(args, bp, torch):
@@ -459,6 +585,35 @@ def bench_mix_bwd(args, bp, torch):
     }
 
 
+# Layer-step kernels with MFMA work: (key in MEASURED, v_mfma_f32_16x16x32_bf16
+# instructions per launch counted by SQ_INSTS_MFMA, traced average duration in
+# us, useful GEMM flops per launch).  Useful flops at T tokens, width C: the
+# map GEMM 2 T 24 (4C); dx's dl W and dw's dl^T x the same each, counted once
+# although both feed dl as a bf16 hi + lo pair (two MFMAs per product).
+LAYER_MFMA_KERNELS = ("layer_maps_kernel<0>", "layer_dx_kernel", "layer_dw_kernel")
+
+
+def layer_mfma(T, C, m):
+    """MFMA utilisation of the layer's three contraction kernels from the
+    counter run (instructions) and the kernel trace (durations) stored for
+    this workload; None when the kernel sources changed since."""
+    if m is None or "mfma" not in m:
+        return None
+    useful = 2.0 * T * 24 * 4 * C
+    res = {}
+    for name in LAYER_MFMA_KERNELS:
+        instr, us = m["mfma"][name], m["us"][name]
+        issued = instr * MFMA_FLOPS_PER_INSTR / (us * 1e-6) / 1e12
+        res[name] = {"mfma_instructions": instr, "traced_us": us,
+                     "issued_TFLOPs": issued, "issued_frac": issued / MFMA_BF16_PEAK_TFLOPS,
+                     "useful_TFLOPs": useful / (us * 1e-6) / 1e12,
+                     "useful_frac": useful / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+    res["peak_TFLOPs"] = MFMA_BF16_PEAK_TFLOPS
+    res["note"] = ("v_mfma_f32_16x16x32_bf16 count x 16384 flops over the traced duration "
+                   "(profiles/layer_step_65536x4x7168.md); HBM-bound kernels, reported, not chased")
+    return res
+
+
 def bench_layer(args, bp, torch):
     """Full layer step fwd+bwd, T=65536, n=4, C=7168."""
     import workloads as W
@@ -474,18 +629,21 @@ def bench_layer(args, bp, torch):
                         args.steps, args.warmup)
     ms = fwd_ms + bwd_ms
     D = 4 * C
-    fwd_bytes = T * (2 * D + 196                               # maps: x; logits, maps out
-                     + 2 * D + 2 * C + 2 * C + 2 * D)          # mix: x, f; u, x_out
-    bwd_bytes = T * (2 * D + 2 * D + 2 * C + 2 * C             # dots: x, dxo, f, du
-                     + 2 * D + 2 * D + 2 * C + 2 * D + 2 * C  # dx: dxo, x, du; dx, df
-                     + 2 * D)                                  # dw: x
-    gbs = (fwd_bytes + bwd_bytes) / (ms / 1e3) / 1e9
-    # what any implementation must move: x, f read and u, x_out written once
-    # forward; x, grad_x_out, f, grad_u read and grad_x, grad_f written once
-    # backward (this one reads x three times and grad_x_out, grad_u twice)
-    min_bytes = T * ((2 * D + 2 * C + 2 * C + 2 * D) + (2 * D + 2 * D + 2 * C + 2 * C + 2 * D + 2 * C))
+    # Algorithmic bytes of the step: forward reads x twice (the maps need the
+    # whole token row before any map is known) and f, writes u and x_out,
+    # plus the 196 bytes of per-token maps; backward reads x, grad_x_out, f
+    # and grad_u once and writes grad_x and grad_f once.
+    fwd_alg = T * (2 * (2 * D) + 2 * C + 2 * C + 2 * D + 196)
+    bwd_alg = T * (2 * D + 2 * D + 2 * C + 2 * C + 2 * D + 2 * C)
+    alg = fwd_alg + bwd_alg
+    gbs = alg / (ms / 1e3) / 1e9
+    # bytes this implementation's passes move (it reads x three times and
+    # grad_x_out, grad_u twice in the backward)
+    pass_bytes = (T * (2 * D + 196 + 2 * D + 2 * C + 2 * C + 2 * D)
+                  + T * (2 * D + 2 * D + 2 * C + 2 * C + 2 * D + 2 * D + 2 * C + 2 * D + 2 * C + 2 * D))
     m = measured(f"layer_step_{T}x4x{C}")
-    return {
+    traffic = m["fetch"] + m["write"] if m else None
+    out = {
         "metric": "mHC layer step fwd+bwd tokens/s; achieved HBM GB/s vs peak",
         "value": T / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
@@ -493,15 +651,25 @@ def bench_layer(args, bp, torch):
         "config": {"workload": f"mHC layer step fwd+bwd, T={T}, n=4, C={C} bf16, W [24, {D}]"},
         "roofline": {"bound": "hbm", "kernel": "whole step (2 forward + 5 backward kernels)",
                      "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS,
-                     "traffic": m["fetch"] + m["write"] if m else None},
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes": alg,
+                     "traffic_ratio": traffic / alg if traffic else None},
         "kernels": {"fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
-                    "fwd_GBs": fwd_bytes / (fwd_ms / 1e3) / 1e9,
-                    "bwd_GBs": bwd_bytes / (bwd_ms / 1e3) / 1e9,
-                    "algorithmic_bytes": fwd_bytes + bwd_bytes,
-                    "one_pass_bytes": min_bytes,
-                    "one_pass_frac": min_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS},
+                    "fwd_GBs": fwd_alg / (fwd_ms / 1e3) / 1e9,
+                    "bwd_GBs": bwd_alg / (bwd_ms / 1e3) / 1e9,
+                    "fwd_frac": fwd_alg / (fwd_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                    "bwd_frac": bwd_alg / (bwd_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                    "pass_bytes": pass_bytes,
+                    "pass_GBs": pass_bytes / (ms / 1e3) / 1e9},
+        "mfma": layer_mfma(T, C, m),
     }
+    if not args.no_cpu_baseline:
+        n = min(T, args.cpu_tokens_layer)
+        xh, fh, dxoh, duh = _host_tokens(slice(0, n), x, f, dxo, du)
+        out["cpu_baseline"] = cpu_baseline_tokens(
+            "layer", (xh, Wt.float().cpu().numpy(), fh, dxoh, duh), n, T,
+            "layer step forward + backward")
+    return out
 
 
 def main():
@@ -515,6 +683,13 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain copy of this size first (counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens-mix", type=int, default=16384,
+                    help="config 4: tokens of the per-token oracle baseline (16384: all of them)")
+    ap.add_argument("--cpu-tokens-layer", type=int, default=16384,
+                    help="config 5: tokens of the per-token oracle baseline, extrapolated to "
+                         "the 65536 of the workload")
+    ap.add_argument("--no-config3", action="store_true",
+                    help="config 2: skip the 1M-matrix block timed beside the headline")
     ap.add_argument("--n", type=int, default=4, choices=range(1, 9), metavar="N",
                     help="configs 1-2: n x n matrices (1..8) through mhc_birkhoff_fwd_n/bwd_n")
     ap.add_argument("--mix-bwd", action="store_true",

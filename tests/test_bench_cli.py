@@ -36,3 +36,34 @@ def test_stored_counters_are_well_formed():
         group = bench.source_group(key)
         for f in bench.KERNEL_SOURCES[group]:
             assert os.path.exists(os.path.join(ROOT, "birkhoff_projection_amd", "csrc", f)), f
+
+
+def test_cpu_baselines_and_roofline_helpers():
+    """The per-token oracle baselines of configs 4 and 5 and the projection
+    baseline run on small host samples and report what they used; the
+    forward roofline is algorithmic bytes over time against 8 TB/s."""
+    import numpy as np
+    import bench
+    import workloads as W
+    g = np.random.Generator(np.random.PCG64(5))
+    T, C = 32, 64
+    x = g.standard_normal((T, 4, C)).astype(np.float32)
+    logits = (2 * g.standard_normal((T, 4, 4))).astype(np.float32)
+    mix = bench.cpu_baseline_tokens("mix", (x, logits), T, 16384, "test")
+    assert mix["value"] > 0 and mix["unit"] == "tokens/s" and mix["extrapolated"]  # 32 of 16384
+    assert 1 <= mix["cores"] <= bench.CPU_SHARE and mix["host_cores_visible"] >= mix["cores"]
+    Wm = (0.02 * g.standard_normal((24, 4 * C))).astype(np.float32)
+    f, du = (g.standard_normal((T, C)).astype(np.float32) for _ in range(2))
+    dxo = g.standard_normal((T, 4, C)).astype(np.float32)
+    lay = bench.cpu_baseline_tokens("layer", (x, Wm, f, dxo, du), T, 65536, "test")
+    assert lay["value"] > 0 and "32 of the 65536 tokens" in lay["sample"]
+    A = W.logits_batch("normal10", 256, 1)
+    G = W.grad_batch(256, 2)
+    proj = bench.cpu_baseline_projection(A, G, 512, "test")
+    assert proj["value"] > 0 and proj["unit"] == "projections/s"
+    roof, valu = bench.forward_roofline("k", 128 * 131072, 0.008, 131072, None)
+    assert roof["bound"] == "hbm" and abs(roof["achieved"] - 128 * 131072 / 8e-6 / 1e9) < 1e-6
+    assert abs(roof["frac"] - roof["achieved"] / 8000.0) < 1e-12 and valu is None
+    m = {"fetch": 1, "write": 2, "valu": 1000, "trans": 10}
+    roof, valu = bench.forward_roofline("k", 1024, 0.001, 8, m)
+    assert roof["traffic"] == 3 and valu["issue_slots_per_launch"] == 1030
