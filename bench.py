@@ -314,8 +314,12 @@ def time_projection(bp, torch, A_np, G_np, steps, warmup, solver="newton", recom
             if not (torch.equal(P, Pe) and torch.equal(dA, dAe)):
                 raise RuntimeError("graph replay differs from eager results")
         fwd_fn(sets[0][0], solver=solver)  # eager work between replays
-    for _ in range(2):  # warm replays
+    for _ in range(2):  # warm replays (a graph's first replays run slower)
         g_step.replay()
+        g_fwd.replay()
+        if g_bwd is not None:
+            g_bwd.replay()
+    torch.cuda.synchronize()
     total_ms = replay(g_step)  # the timed region: exactly `steps` steps
     fwd_ms = replay(g_fwd) / steps
     bwd_ms = 0.0 if fused else replay(g_bwd) / steps
@@ -324,6 +328,7 @@ def time_projection(bp, torch, A_np, G_np, steps, warmup, solver="newton", recom
     # hot cache: every step on the same buffer set (reported apart, never the
     # headline: the set fits in the 256 MB last-level cache)
     g_hot = capture(lambda k: step(0))
+    g_hot.replay()
     g_hot.replay()
     hot_ms = replay(g_hot) / steps
     return dict(total_ms=total_ms, fwd_ms=fwd_ms, bwd_ms=bwd_ms, nsets=nsets,

@@ -31,12 +31,20 @@ __global__ __launch_bounds__(kBlock) void birkhoff_fwd_kernel(const float* logit
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int64_t first = (int64_t)blockIdx.x * kBlock + 64 * w;
     if (first >= B) return;  // the whole wave is past the batch
-    float a[16], p[16];
+    float a[16];
     load_records_v4<16>(logits, first, B, tiles[w], a, lane);
-    // the tile keeps the logits until the store: the start reads rows of it
-    const float* rec = tiles[w] + lane * record_pitch<16>();
-    const uint32_t it = SOLVER == 0 ? project_newton<true>(a, p, o, rec) : project_sinkhorn(a, p, o);
-    store_records_v4<16>(P, first, B, tiles[w], p, lane);
+    // each lane's slot of the tile keeps its logits for the start's row
+    // reads, then receives its P (Newton); the store reads the tile
+    float* rec = tiles[w] + lane * record_pitch<16>();
+    uint32_t it;
+    if (SOLVER == 0) {
+        it = project_newton_lds(a, rec, o);
+        store_tile_v4<16>(P, first, B, tiles[w], lane);
+    } else {
+        float p[16];
+        it = project_sinkhorn(a, p, o);
+        store_records_v4<16>(P, first, B, tiles[w], p, lane);
+    }
     if (iters != nullptr && first + lane < B) iters[first + lane] = (uint8_t)it;
 }
 
@@ -99,10 +107,19 @@ __global__ __launch_bounds__(kBlock) void birkhoff_solve_bwd_kernel(const float*
     float a[16], g[16], p[16], d[16];
     load_records_v4<16>(logits, first, B, tiles[w], a, lane);
     load_records_v4<16>(G, first, B, gtiles[w], g, lane);
-    const float* rec = tiles[w] + lane * record_pitch<16>();
-    const uint32_t it = SOLVER == 0 ? project_newton<true>(a, p, o, rec) : project_sinkhorn(a, p, o);
+    float* rec = tiles[w] + lane * record_pitch<16>();
+    uint32_t it;
+    if (SOLVER == 0) {
+        // P is left in the lane's own slot of the tile (no cross-lane data)
+        it = project_newton_lds(a, rec, o);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) p[k] = rec[k];
+        if (WRITE_P) store_tile_v4<16>(P, first, B, tiles[w], lane);
+    } else {
+        it = project_sinkhorn(a, p, o);
+        if (WRITE_P) store_records_v4<16>(P, first, B, tiles[w], p, lane);
+    }
     project_bwd(p, g, d);
-    if (WRITE_P) store_records_v4<16>(P, first, B, tiles[w], p, lane);
     store_records_v4<16>(dA, first, B, tiles[w], d, lane);
     if (WRITE_P && iters != nullptr && first + lane < B) iters[first + lane] = (uint8_t)it;
 }

@@ -57,13 +57,15 @@ constexpr float kCurvature = 0.9f;
 // gains only a factor e and the potentials drift a constant distance per
 // iteration.  An accepted full first trial whose directional derivative
 // still has at least kFar of its initial magnitude doubles the next
-// iteration's first trial (up to kMaxGrow Newton steps); one that stopped
-// short of the line minimum (derivative still negative) keeps the current
-// multiple.  Either needs the trial to have cut the residual by at least
-// kGrowProgress: when the drift ends, the directional derivative keeps
-// looking far while the residual stalls, and longer trials there only
-// overshoot.  An overshoot, a stall or a backtracked iteration returns to the
-// plain Newton step.
+// iteration's first trial (up to kMaxGrow Newton steps), provided the trial
+// cut the residual by at least kGrowProgress: when the drift ends, the
+// directional derivative keeps looking far while the residual stalls, and
+// longer trials there only overshoot.  Every other outcome returns to the
+// plain Newton step.  (Keeping a grown multiple after a trial that merely
+// stopped short of the line minimum paid when drifts were long; from the
+// assignment start they last a trial or two, and the kept multiple then
+// overshoots once the iteration is quadratic: on 131072 N(0,10^2) matrices
+// it left 45 waves needing a fifth trial, against 11 without it.)
 // A drift step keeps about e^-1 = 0.37 of the directional derivative.  From
 // the assignment start long drifts are rare, and a first full step that
 // keeps 0.25-0.35 of it is mostly mild curvature change near the solution,
@@ -268,6 +270,17 @@ MHC_DEV float newton_ridge(const Weights& w)
 constexpr uint32_t kNotConverged = 255u;
 MHC_DEV uint32_t iters_code(int n) { return n > 254 ? 254u : (uint32_t)n; }
 
+// True if `pred` holds on any active lane of the wave (wave-uniform).
+MHC_DEV bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
+
+// Lane-private 16-float slot in LDS that receives P when the lane's solve
+// ends (SINK solvers); the lane's logits occupied it until the start read them.
+MHC_DEV void sink_store(float* sink, const float* P)
+{
+#pragma unroll
+    for (int k = 0; k < 16; ++k) sink[k] = P[k];
+}
+
 // Newton's method on the semi-dual for one matrix, as a state machine:
 //
 //   init():  base-2 logits with each row shifted to maximum 0; evaluate at
@@ -300,6 +313,7 @@ struct NewtonLane {
     int newton, trials;  // Newton directions taken, halvings this step
     uint32_t code;       // result when done
     bool done;
+    bool stored;         // P already written to the lane's LDS sink
 };
 
 // Newton direction at E (natural-units solve, returned in base-2 units),
@@ -461,8 +475,9 @@ MHC_DEV void assignment_start(const float* a, const float* rec, float& g0, float
     g2 = finite ? m2 : 0.f;
 }
 
-template <bool ROWS_IN_LDS>
-MHC_DEV void newton_init(NewtonLane& s, const float* a_nat, const float* rec, const SolverOpts& o)
+template <bool ROWS_IN_LDS, bool SINK>
+MHC_DEV void newton_init(NewtonLane& s, const float* a_nat, const float* rec, const SolverOpts& o,
+                         float* sink)
 {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -503,8 +518,9 @@ MHC_DEV void newton_init(NewtonLane& s, const float* a_nat, const float* rec, co
             s.done = s.res <= o.tol;
         }
     }
-    float tcap;
-    newton_direction(E, s.d0, s.d1, s.d2, s.slope, tcap);
+    float tcap = 0.f;
+    s.d0 = s.d1 = s.d2 = s.slope = 0.f;
+    if (!SINK || wave_any(!s.done)) newton_direction(E, s.d0, s.d1, s.d2, s.slope, tcap);
     s.grow = 1.f;
     s.t = mhc_min(1.f, tcap);
     if (!s.done && o.max_iters < 1) {
@@ -512,15 +528,23 @@ MHC_DEV void newton_init(NewtonLane& s, const float* a_nat, const float* rec, co
         s.code = kNotConverged;
     }
     s.newton = 1;
+    s.stored = false;
+    if (SINK && s.done && s.code == 0) {
+        sink_store(sink, E.P);
+        s.stored = true;
+    }
 }
 
 // One trial of a lane that is not done (the caller guarantees !s.done and,
-// for FACTORED, !s.slow).  Written without branches so that the whole trial
-// is one basic block the compiler can schedule across.  With FACTORED a trial
-// whose factored evaluation is out of range changes nothing but s.slow; the
-// lane then repeats it, and continues, with the max-shifted form.
-template <bool FACTORED>
-MHC_DEV void newton_step(NewtonLane& s, const SolverOpts& o)
+// for FACTORED, !s.slow).  Written without branches, except that the next
+// Newton direction is computed only if some lane of the wave goes on from an
+// accepted point: a wave's last trial, where every remaining lane converges
+// or stops, skips it.  With FACTORED a trial whose factored evaluation is out
+// of range changes nothing but s.slow; the lane then repeats it, and
+// continues, with the max-shifted form.  With SINK a lane that converges
+// writes its P (this trial's evaluation) to `sink` and sets s.stored.
+template <bool FACTORED, bool SINK>
+MHC_DEV void newton_step(NewtonLane& s, const SolverOpts& o, float* sink)
 {
     const float t0 = s.g0 + s.t * s.d0, t1 = s.g1 + s.t * s.d1, t2 = s.g2 + s.t * s.d2;
     Eval E;
@@ -529,8 +553,6 @@ MHC_DEV void newton_step(NewtonLane& s, const SolverOpts& o)
         ok = evaluate_factored(s.k, t0, t1, t2, E);
     else
         evaluate_shifted(s.a, t0, t1, t2, E);
-    float nd0, nd1, nd2, nslope, ncap;
-    newton_direction(E, nd0, nd1, nd2, nslope, ncap);
 
     const float dphi = -(E.b[0] * s.d0 + E.b[1] * s.d1 + E.b[2] * s.d2);
     // (bitwise & and | on bools: no short-circuit branches)
@@ -548,15 +570,12 @@ MHC_DEV void newton_step(NewtonLane& s, const SolverOpts& o)
     const bool pass = conv_t | ((near_floor | to_floor) & lower) | (!near_floor & curved);
     const bool accept = ok & pass;
     const bool reject = ok & !pass;
-    // next first trial: after a full first trial that at least halved the
-    // residual, doubled if it stayed far from the line minimum and kept if it
-    // stopped short of it; the Newton step otherwise
+    // next first trial: doubled after a full first trial that at least
+    // halved the residual and stayed far from the line minimum; the Newton
+    // step otherwise
     const bool first = (s.trials == 0) & (s.t >= s.grow) & (E.res < kGrowProgress * s.res);
     const bool far = first & (dphi <= kFar * s.slope);
-    const bool short_of_min = first & (dphi < 0.f);
-    const float grow_far = mhc_pin(mhc_min(2.f * s.grow, kMaxGrow));
-    const float grow_else = mhc_pin(short_of_min ? s.grow : 1.f);
-    const float grow = far ? grow_far : grow_else;
+    const float grow = mhc_pin(far ? mhc_min(2.f * s.grow, kMaxGrow) : 1.f);
     const bool conv = accept & conv_t;
     const bool maxed = accept & !conv & (s.newton >= o.max_iters);
     const int trials = s.trials + 1;
@@ -568,6 +587,14 @@ MHC_DEV void newton_step(NewtonLane& s, const SolverOpts& o)
     // every trial they cost 3 % of the ordinary forward, hence this path only.
     const bool still = !FACTORED && ((t0 == s.g0) & (t1 == s.g1) & (t2 == s.g2) & !conv_t);
     const bool stuck = (reject & ((near_floor & (s.t <= 1.f)) | (trials > 30))) | (ok & still);
+    const bool done = s.done | conv | maxed | stuck;
+
+    float nd0 = 0.f, nd1 = 0.f, nd2 = 0.f, nslope = 0.f, ncap = 0.f;
+    if (wave_any(accept & !done)) newton_direction(E, nd0, nd1, nd2, nslope, ncap);
+    if (SINK && conv) {
+        sink_store(sink, E.P);
+        s.stored = true;
+    }
 
     s.g0 = accept ? t0 : s.g0;
     s.g1 = accept ? t1 : s.g1;
@@ -582,7 +609,7 @@ MHC_DEV void newton_step(NewtonLane& s, const SolverOpts& o)
     s.trials = accept ? 0 : (reject ? trials : s.trials);
     s.newton += (accept & !conv & !maxed) ? 1 : 0;
     s.code = conv ? iters_code(s.newton) : ((maxed | stuck) ? kNotConverged : s.code);
-    s.done = s.done | conv | maxed | stuck;
+    s.done = done;
     s.slow = s.slow | !ok;
 }
 
@@ -599,14 +626,33 @@ MHC_DEV uint32_t project_newton(const float* a_nat, float* P_out, const SolverOp
                                 const float* rec = nullptr)
 {
     NewtonLane s;
-    newton_init<ROWS_IN_LDS>(s, a_nat, rec, o);
-    while (!s.done && !s.slow) newton_step<true>(s, o);
-    while (!s.done) newton_step<false>(s, o);
+    newton_init<ROWS_IN_LDS, false>(s, a_nat, rec, o, nullptr);
+    while (!s.done && !s.slow) newton_step<true, false>(s, o, nullptr);
+    while (!s.done) newton_step<false, false>(s, o, nullptr);
     // P of the accepted point (the same arithmetic as when it was accepted)
     Eval E;
     evaluate(s.a, s.k, s.kfast, s.g0, s.g1, s.g2, E);
 #pragma unroll
     for (int k = 0; k < 16; ++k) P_out[k] = E.P[k];
+    return s.code;
+}
+
+// The same projection for a lane whose logits sit in its own 16-float LDS
+// slot `rec` (as the staged kernels hold them): the start reads rows of it,
+// and P is left in it.  A lane writes its P there from the evaluation that
+// converged, so only lanes that stop without converging (flag 255) evaluate
+// again at their last accepted point; the others skip that evaluation.
+MHC_DEV uint32_t project_newton_lds(const float* a_nat, float* rec, const SolverOpts& o)
+{
+    NewtonLane s;
+    newton_init<true, true>(s, a_nat, rec, o, rec);
+    while (!s.done && !s.slow) newton_step<true, true>(s, o, rec);
+    while (!s.done) newton_step<false, true>(s, o, rec);
+    if (!s.stored) {
+        Eval E;
+        evaluate(s.a, s.k, s.kfast, s.g0, s.g1, s.g2, E);
+        sink_store(rec, E.P);
+    }
     return s.code;
 }
 

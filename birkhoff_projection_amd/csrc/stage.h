@@ -144,4 +144,27 @@ MHC_DEV void store_records_v4(float* __restrict__ g, int64_t first, int64_t B, f
     }
 }
 
+// store_records_v4 for records that are already in the tile (lane l's record
+// at tile + l * record_pitch<R>(), each written by its own lane): only the
+// coalesced global stores.
+template <int R>
+MHC_DEV void store_tile_v4(float* __restrict__ g, int64_t first, int64_t B, const float* tile,
+                           int lane)
+{
+    static_assert(R % 4 == 0, "records of whole float4s");
+    constexpr int kP = record_pitch<R>();
+    constexpr int kQ = R / 4;
+    const int64_t have = B - first;
+    float4* g4 = reinterpret_cast<float4*>(g);
+    mhc_wave_lds_fence();  // the reads below see the other lanes' writes
+#pragma unroll
+    for (int i = 0; i < kQ; ++i) {
+        const int e = 4 * (lane + 64 * i);
+        const int rec = e / R, col = e % R;
+        const float* t = tile + rec * kP + col;
+        const float4 q = make_float4(t[0], t[1], t[2], t[3]);
+        if (have >= 64 || rec < have) mhc_store_stream(g4 + kQ * first + lane + 64 * i, q);
+    }
+}
+
 }  // namespace mhc
