@@ -65,22 +65,22 @@ CPU_SHARE = 16
 # each entry carries the hash of the csrc files its kernels are built from
 # (KERNEL_SOURCES), and a mismatch reports it as null.
 KERNEL_SOURCES = {
-    "proj": ("devmath.h", "proj4.h", "stage.h", "kernels.h", "birkhoff.hip"),
-    "projn": ("devmath.h", "proj4.h", "projn.h", "stage.h", "kernels.h", "birkhoffn.hip"),
-    "mix": ("devmath.h", "proj4.h", "kernels.h", "mix.hip"),
+    "proj": ("devmath.h", "proj4.h", "stage.h", "birkhoff.hip"),
+    "projn": ("devmath.h", "proj4.h", "projn.h", "stage.h", "birkhoffn.hip"),
+    "mix": ("devmath.h", "proj4.h", "mix.hip"),
     "layer": ("devmath.h", "proj4.h", "kernels.h", "layer.hip"),
 }
 MEASURED = {
-    "birkhoff_fwd_131072_cfg2": {"fetch": 8542301, "write": 8389041, "valu": 2635940, "trans": 145972, "sha": "54eb2d9ea2097034"},
-    "birkhoff_bwd_131072_cfg2": {"fetch": 16805860, "write": 8389153, "valu": 1122304, "trans": 24576, "sha": "54eb2d9ea2097034"},
-    "birkhoff_fwd_1048576_cfg3": {"fetch": 67258770, "write": 67112640, "valu": 20416372, "trans": 1128673, "sha": "54eb2d9ea2097034"},
-    "birkhoff_bwd_1048576_cfg3": {"fetch": 134231741, "write": 67109588, "valu": 8978432, "trans": 196608, "sha": "54eb2d9ea2097034"},
-    "birkhoff_fwd_n8_131072_cfg2": {"fetch": 40890306, "write": 59770041, "valu": 22793498, "trans": 745229, "sha": "e3d0b54e32ed857c"},
-    "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67434139, "write": 33554787, "valu": 6424576, "trans": 14336, "sha": "e3d0b54e32ed857c"},
-    "birkhoff_fwd_bwd_131072_cfg2": {"fetch": 16955557, "write": 16777348, "valu": 3184784, "trans": 152116, "sha": "54eb2d9ea2097034"},
-    "stream_mix_fwd_16384x4x4096": {"fetch": 537990369, "write": 537927663, "valu": 25710592, "trans": 68608, "sha": "d39c2582381b45d9"},
-    "stream_mix_bwd_16384x4x4096": {"fetch": 1074730982, "write": 537958554, "valu": 50135040, "trans": 0, "sha": "d39c2582381b45d9"},
-    "layer_step_65536x4x7168": {"fetch": 30740255334, "write": 9469211354, "sha": "ee127d12e372d29b"},
+    "birkhoff_fwd_131072_cfg2": {"fetch": 8534119, "write": 8388969, "valu": 2428524, "trans": 122685, "sha": "826a4b73e55c307b"},
+    "birkhoff_bwd_131072_cfg2": {"fetch": 16805925, "write": 8388691, "valu": 1122304, "trans": 24576, "sha": "826a4b73e55c307b"},
+    "birkhoff_fwd_1048576_cfg3": {"fetch": 67252286, "write": 67116402, "valu": 18806282, "trans": 946129, "sha": "826a4b73e55c307b"},
+    "birkhoff_bwd_1048576_cfg3": {"fetch": 134231305, "write": 67109165, "valu": 8978432, "trans": 196608, "sha": "826a4b73e55c307b"},
+    "birkhoff_fwd_bwd_131072_cfg2": {"fetch": 16957581, "write": 16777216, "valu": 2977371, "trans": 128829, "sha": "826a4b73e55c307b"},
+    "birkhoff_fwd_n8_131072_cfg2": {"fetch": 40909582, "write": 59769900, "valu": 22793495, "trans": 745229, "sha": "717dd4767b586ebf"},
+    "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67434180, "write": 33555104, "valu": 6424576, "trans": 14336, "sha": "717dd4767b586ebf"},
+    "stream_mix_fwd_16384x4x4096": {"fetch": 538003954, "write": 537926485, "valu": 25666560, "trans": 64512, "sha": "2277bf78266d3f85"},
+    "stream_mix_bwd_16384x4x4096": {"fetch": 1074735298, "write": 537937045, "valu": 50135040, "trans": 0, "sha": "2277bf78266d3f85"},
+    "layer_step_65536x4x7168": {"fetch": 30714158805, "write": 9469203225, "mfma": {"layer_maps_kernel<0>": 7340032, "layer_dx_kernel": 14680064, "layer_dw_kernel": 14680064}, "us": {"layer_maps_kernel<0>": 666.72, "layer_dx_kernel": 2577.87, "layer_dw_kernel": 753.14}, "sha": "940294f1486bfe3d"},
 }
 
 
