@@ -19,6 +19,9 @@ Prints one JSON line:
   hbm          algorithmic GB/s of fwd, bwd and the step against 8 TB/s, and
                the counter-measured HBM bytes per launch
   iters        Newton iterations per matrix and per wave (divergence)
+  overlapped   the same steps with batch k's forward and batch k-1's
+               backward in one launch (mhc_birkhoff_pipeline_step;
+               bit-identical results; beside the headline, never as it)
   config3      the same fwd+bwd step on 1,048,576 mixed-difficulty matrices,
                timed in the same run (the other end of the 128K-1M range)
   cpu_baseline the float64 oracle (fwd+bwd) on the host cores, on a bounded
@@ -229,7 +232,7 @@ def cpu_baseline_tokens(kind, tokens, n, T_total, label):
 
 
 def time_projection(bp, torch, A_np, G_np, steps, warmup, solver="newton", recompute=False, n=4,
-                    fused=False):
+                    fused=False, overlap=False):
     """Rotate over buffer sets and time `steps` fwd+bwd steps back to back,
     then `steps` forward launches alone and `steps` backward launches alone.
 
@@ -272,6 +275,20 @@ def time_projection(bp, torch, A_np, G_np, steps, warmup, solver="newton", recom
         fwd(k)
         bwd(k)
 
+    # Pipelined schedule: one launch runs the forward of batch k and the
+    # backward of batch k-1 (mhc_birkhoff_pipeline_step), as a trainer that
+    # overlaps micro-batches would; a forward alone opens the sequence and a
+    # backward alone closes it.  Every batch still gets its forward, then
+    # its backward, and stream order alone keeps the dependencies: launch k
+    # writes P of set k and reads P of set k-1 (nsets >= 2).
+    def pipelined():
+        fwd(0)
+        for k in range(1, steps):
+            A, P, G, dA = sets[k % nsets]
+            Ap, Pp, Gp, dAp = sets[(k - 1) % nsets]
+            bp.birkhoff_pipeline_step(A, Pp, Gp, out=P, out_grad=dAp, solver=solver)
+        bwd(steps - 1)
+
     def events():
         return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
@@ -286,11 +303,14 @@ def time_projection(bp, torch, A_np, G_np, steps, warmup, solver="newton", recom
         torch.cuda.synchronize()
         return start.elapsed_time(stop)
 
-    def capture(body):
+    def capture(body, whole=False):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for k in range(steps):
-                body(k)
+            if whole:
+                body()
+            else:
+                for k in range(steps):
+                    body(k)
         torch.cuda.synchronize()
         return g
 
@@ -320,16 +340,20 @@ def time_projection(bp, torch, A_np, G_np, steps, warmup, solver="newton", recom
             Pe = fwd_fn(A, solver=solver)
             dAe = bp.birkhoff_bwd_recompute(A, G, solver=solver) if recompute else bwd_fn(Pe, G)
         ref.append((Pe, dAe))
-    for _ in range(2):
-        for A, P, G, dA in touched:
-            P.zero_()
-            dA.zero_()
-        g_step.replay()
-        torch.cuda.synchronize()
-        for (A, P, G, dA), (Pe, dAe) in zip(touched, ref):
-            if not (torch.equal(P, Pe) and torch.equal(dA, dAe)):
-                raise RuntimeError("graph replay differs from eager results")
-        fwd_fn(sets[0][0], solver=solver)  # eager work between replays
+    g_over = capture(pipelined, whole=True) if overlap else None
+    for g in (g_step, g_over):
+        if g is None:
+            continue
+        for _ in range(2):
+            for A, P, G, dA in touched:
+                P.zero_()
+                dA.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            for (A, P, G, dA), (Pe, dAe) in zip(touched, ref):
+                if not (torch.equal(P, Pe) and torch.equal(dA, dAe)):
+                    raise RuntimeError("graph replay differs from eager results")
+            fwd_fn(sets[0][0], solver=solver)  # eager work between replays
     for _ in range(2):  # warm replays (a graph's first replays run slower)
         g_step.replay()
         g_fwd.replay()
@@ -347,9 +371,14 @@ def time_projection(bp, torch, A_np, G_np, steps, warmup, solver="newton", recom
     g_hot.replay()
     g_hot.replay()
     hot_ms = replay(g_hot) / steps
+    over_ms = None
+    if g_over is not None:
+        g_over.replay()
+        g_over.replay()
+        over_ms = sorted(replay(g_over) / steps for _ in range(3))[1]
     return dict(total_ms=total_ms, fwd_ms=fwd_ms, bwd_ms=bwd_ms, nsets=nsets,
                 eager_ms_per_step=eager_ms / steps, step_ms_median=spread[2],
-                step_ms_min=spread[0], hot_ms_per_step=hot_ms)
+                step_ms_min=spread[0], hot_ms_per_step=hot_ms, overlapped_ms_per_step=over_ms)
 
 
 def copy_bandwidth(torch, mib=256, reps=20):
@@ -428,7 +457,7 @@ def bench_projection(args, bp, torch, config):
     if args.recompute and args.fused:
         raise SystemExit("--recompute and --fused exclude each other")
     r = time_projection(bp, torch, A, G, args.steps, args.warmup, recompute=args.recompute, n=n,
-                        fused=args.fused)
+                        fused=args.fused, overlap=n == 4 and not (args.fused or args.recompute))
     ms = r["total_ms"] / args.steps
     fwd_avg = float(r["fwd_ms"])
     bwd_avg = float(r["bwd_ms"])
@@ -472,12 +501,28 @@ def bench_projection(args, bp, torch, config):
         "valu": valu,
         "iters": iteration_stats(bp, torch, A, n),
     }
+    if r["overlapped_ms_per_step"] is not None:
+        out["overlapped"] = overlapped_block(r, B, fwd_bytes + bwd_bytes)
     if config == 2 and n == 4 and not (args.recompute or args.fused) and not args.no_config3:
         out["config3"] = config3_block(args, bp, torch)
     if not args.no_cpu_baseline:
         sample = args.cpu_sample if n == 4 else max(args.cpu_sample * 16 // (n * n * 4), 16384)
         out["cpu_baseline"] = cpu_baseline_projection(A, G, sample, label)
     return out
+
+
+def overlapped_block(r, B, step_bytes):
+    """The same steps with batch k's forward and batch k-1's backward in one
+    launch (mhc_birkhoff_pipeline_step; see time_projection).  Reported
+    beside the headline, never as it: the headline step keeps each batch's
+    forward and backward in two launches, one after the other."""
+    ms = r["overlapped_ms_per_step"]
+    gbs = step_bytes * B / (ms / 1e3) / 1e9
+    return {"schedule": "mhc_birkhoff_pipeline_step: forward of batch k and backward of batch "
+                        "k-1 in one launch (a forward alone opens the sequence, a backward "
+                        "alone closes it); results bit-identical to the serial steps",
+            "value": B / (ms / 1e3), "unit": "projections/s", "ms_per_step": ms,
+            "step_GBs": gbs, "step_frac": gbs / HBM_PEAK_GBS, "timing": "median of 3 replays"}
 
 
 def forward_roofline(kname, alg_bytes, fwd_ms, B, m):
@@ -513,7 +558,7 @@ def config3_block(args, bp, torch):
     import workloads as W
     A, G, _ = W.config3()
     B = A.shape[0]
-    r = time_projection(bp, torch, A, G, args.steps, args.warmup)
+    r = time_projection(bp, torch, A, G, args.steps, args.warmup, overlap=True)
     ms = r["total_ms"] / args.steps
     fwd_ms, bwd_ms = float(r["fwd_ms"]), float(r["bwd_ms"])
     step_gbs = (FWD_BYTES + BWD_BYTES) * B / (ms / 1e3) / 1e9
@@ -528,7 +573,8 @@ def config3_block(args, bp, torch):
             "bwd_GBs": BWD_BYTES * B / (bwd_ms / 1e3) / 1e9,
             "bwd_frac": BWD_BYTES * B / (bwd_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
             "step_us_median_of_5": r["step_ms_median"] * 1e3, "roofline_fwd": roof, "valu": valu,
-            "iters": iteration_stats(bp, torch, A)}
+            "iters": iteration_stats(bp, torch, A),
+            "overlapped": overlapped_block(r, B, FWD_BYTES + BWD_BYTES)}
 
 
 def _time_loop(torch, body, steps, warmup):

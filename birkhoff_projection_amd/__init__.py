@@ -8,12 +8,13 @@ for device memory and streams.
 """
 from ._lib import LIB_PATH, MHCError, lib
 from .ops import (BirkhoffProjection, birkhoff_bwd, birkhoff_bwd_n, birkhoff_bwd_recompute,
-                  birkhoff_fwd, birkhoff_fwd_bwd, birkhoff_fwd_n, birkhoff_project,
+                  birkhoff_fwd, birkhoff_fwd_bwd, birkhoff_fwd_n, birkhoff_pipeline_step,
+                  birkhoff_project,
                   layer_bwd, layer_bwd_noalloc, layer_fwd, layer_workspace, make_opts,
                   stream_mix, stream_mix_bwd)
 
 __all__ = ["LIB_PATH", "MHCError", "lib", "BirkhoffProjection", "birkhoff_bwd",
            "birkhoff_bwd_n", "birkhoff_bwd_recompute", "birkhoff_fwd_bwd", "birkhoff_fwd_n",
-           "birkhoff_fwd", "birkhoff_project", "layer_bwd", "layer_bwd_noalloc", "layer_fwd",
+           "birkhoff_fwd", "birkhoff_pipeline_step", "birkhoff_project", "layer_bwd", "layer_bwd_noalloc", "layer_fwd",
            "layer_workspace",
            "make_opts", "stream_mix", "stream_mix_bwd"]

@@ -45,6 +45,9 @@ SIGNATURES = {
                                              ctypes.POINTER(ProjOpts), c_void_p]),
     "mhc_birkhoff_fwd_bwd": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_int64,
                                        ctypes.POINTER(ProjOpts), c_void_p, c_void_p]),
+    "mhc_birkhoff_pipeline_step": (c_int32, [c_void_p, c_void_p, c_int64, ctypes.POINTER(ProjOpts),
+                                             c_void_p, c_void_p, c_void_p, c_void_p, c_int64,
+                                             c_void_p]),
     "mhc_birkhoff_fwd_n": (c_int32, [c_void_p, c_void_p, c_int64, c_int32,
                                      ctypes.POINTER(ProjOpts), c_void_p, c_void_p]),
     "mhc_birkhoff_bwd_n": (c_int32, [c_void_p, c_void_p, c_void_p, c_int64, c_int32, c_void_p]),

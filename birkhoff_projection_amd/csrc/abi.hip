@@ -75,6 +75,35 @@ mhc_status launched(hipError_t e, const char* what)
     return ok();
 }
 
+// The buffers of a 4x4 forward (B > 0).
+mhc_status check_fwd_buffers(const float* logits, const float* P, const uint8_t* iters, int64_t B)
+{
+    if (logits == nullptr || P == nullptr) return fail(MHC_ERR_INVALID_ARGUMENT, "logits and P must not be NULL");
+    if (!aligned16(logits) || !aligned16(P)) return fail(MHC_ERR_INVALID_ARGUMENT, "logits and P must be 16-byte aligned");
+    const size_t bytes = (size_t)B * 64;
+    if (logits != P && overlap(logits, bytes, P, bytes))
+        return fail(MHC_ERR_INVALID_ARGUMENT, "P partially overlaps logits");
+    if (iters != nullptr && (overlap(iters, (size_t)B, logits, bytes) || overlap(iters, (size_t)B, P, bytes)))
+        return fail(MHC_ERR_INVALID_ARGUMENT, "iters overlaps logits or P");
+    return MHC_OK;
+}
+
+// The buffers of a 4x4 backward from P (B > 0).
+mhc_status check_bwd_buffers(const float* P, const float* grad_P, const float* grad_logits,
+                             int64_t B)
+{
+    if (P == nullptr || grad_P == nullptr || grad_logits == nullptr)
+        return fail(MHC_ERR_INVALID_ARGUMENT, "P, grad_P and grad_logits must not be NULL");
+    if (!aligned16(P) || !aligned16(grad_P) || !aligned16(grad_logits))
+        return fail(MHC_ERR_INVALID_ARGUMENT, "P, grad_P and grad_logits must be 16-byte aligned");
+    const size_t bytes = (size_t)B * 64;
+    if (overlap(P, bytes, grad_logits, bytes))
+        return fail(MHC_ERR_INVALID_ARGUMENT, "grad_logits overlaps P");
+    if (grad_P != grad_logits && overlap(grad_P, bytes, grad_logits, bytes))
+        return fail(MHC_ERR_INVALID_ARGUMENT, "grad_logits partially overlaps grad_P");
+    return MHC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -94,16 +123,10 @@ mhc_status mhc_birkhoff_fwd(const float* logits, float* P, int64_t B, const mhc_
 {
     if (B < 0 || B > kMaxBatch) return fail(MHC_ERR_INVALID_ARGUMENT, "B=%lld out of range", (long long)B);
     mhc::SolverOpts o;
-    const mhc_status s = check_opts(opts, &o);
+    mhc_status s = check_opts(opts, &o);
     if (s != MHC_OK) return s;
     if (B == 0) return ok();
-    if (logits == nullptr || P == nullptr) return fail(MHC_ERR_INVALID_ARGUMENT, "logits and P must not be NULL");
-    if (!aligned16(logits) || !aligned16(P)) return fail(MHC_ERR_INVALID_ARGUMENT, "logits and P must be 16-byte aligned");
-    const size_t bytes = (size_t)B * 64;
-    if (logits != P && overlap(logits, bytes, P, bytes))
-        return fail(MHC_ERR_INVALID_ARGUMENT, "P partially overlaps logits");
-    if (iters != nullptr && (overlap(iters, (size_t)B, logits, bytes) || overlap(iters, (size_t)B, P, bytes)))
-        return fail(MHC_ERR_INVALID_ARGUMENT, "iters overlaps logits or P");
+    if ((s = check_fwd_buffers(logits, P, iters, B)) != MHC_OK) return s;
     return launched(mhc::launch_birkhoff_fwd(logits, P, iters, B, o, (hipStream_t)stream),
                     "birkhoff_fwd launch");
 }
@@ -113,17 +136,43 @@ mhc_status mhc_birkhoff_bwd(const float* P, const float* grad_P, float* grad_log
 {
     if (B < 0 || B > kMaxBatch) return fail(MHC_ERR_INVALID_ARGUMENT, "B=%lld out of range", (long long)B);
     if (B == 0) return ok();
-    if (P == nullptr || grad_P == nullptr || grad_logits == nullptr)
-        return fail(MHC_ERR_INVALID_ARGUMENT, "P, grad_P and grad_logits must not be NULL");
-    if (!aligned16(P) || !aligned16(grad_P) || !aligned16(grad_logits))
-        return fail(MHC_ERR_INVALID_ARGUMENT, "P, grad_P and grad_logits must be 16-byte aligned");
-    const size_t bytes = (size_t)B * 64;
-    if (overlap(P, bytes, grad_logits, bytes))
-        return fail(MHC_ERR_INVALID_ARGUMENT, "grad_logits overlaps P");
-    if (grad_P != grad_logits && overlap(grad_P, bytes, grad_logits, bytes))
-        return fail(MHC_ERR_INVALID_ARGUMENT, "grad_logits partially overlaps grad_P");
+    const mhc_status s = check_bwd_buffers(P, grad_P, grad_logits, B);
+    if (s != MHC_OK) return s;
     return launched(mhc::launch_birkhoff_bwd(P, grad_P, grad_logits, B, (hipStream_t)stream),
                     "birkhoff_bwd launch");
+}
+
+mhc_status mhc_birkhoff_pipeline_step(const float* logits, float* P, int64_t B,
+                                      const mhc_proj_opts* opts, uint8_t* iters,
+                                      const float* P_bwd, const float* grad_P,
+                                      float* grad_logits, int64_t B_bwd, void* stream)
+{
+    if (B < 0 || B > kMaxBatch) return fail(MHC_ERR_INVALID_ARGUMENT, "B=%lld out of range", (long long)B);
+    if (B_bwd < 0 || B_bwd > kMaxBatch)
+        return fail(MHC_ERR_INVALID_ARGUMENT, "B_bwd=%lld out of range", (long long)B_bwd);
+    mhc::SolverOpts o;
+    mhc_status s = check_opts(opts, &o);
+    if (s != MHC_OK) return s;
+    if (B == 0 && B_bwd == 0) return ok();
+    if (B > 0 && (s = check_fwd_buffers(logits, P, iters, B)) != MHC_OK) return s;
+    if (B_bwd > 0 && (s = check_bwd_buffers(P_bwd, grad_P, grad_logits, B_bwd)) != MHC_OK) return s;
+    if (B > 0 && B_bwd > 0) {
+        // the forward's outputs against every backward array, and the
+        // backward's output against every forward array; the inputs of the
+        // two halves may share memory (both only read it)
+        const size_t fb = (size_t)B * 64, bb = (size_t)B_bwd * 64;
+        if (overlap(P, fb, P_bwd, bb) || overlap(P, fb, grad_P, bb) || overlap(P, fb, grad_logits, bb))
+            return fail(MHC_ERR_INVALID_ARGUMENT, "P overlaps P_bwd, grad_P or grad_logits");
+        if (overlap(grad_logits, bb, logits, fb))
+            return fail(MHC_ERR_INVALID_ARGUMENT, "grad_logits overlaps logits");
+        if (iters != nullptr && (overlap(iters, (size_t)B, P_bwd, bb) ||
+                                 overlap(iters, (size_t)B, grad_P, bb) ||
+                                 overlap(iters, (size_t)B, grad_logits, bb)))
+            return fail(MHC_ERR_INVALID_ARGUMENT, "iters overlaps P_bwd, grad_P or grad_logits");
+    }
+    return launched(mhc::launch_birkhoff_pipeline(logits, P, iters, B, o, P_bwd, grad_P,
+                                                  grad_logits, B_bwd, (hipStream_t)stream),
+                    "birkhoff_pipeline_step launch");
 }
 
 mhc_status mhc_birkhoff_bwd_recompute(const float* logits, const float* grad_P,

@@ -20,16 +20,17 @@ namespace {
 
 constexpr int kBlock = 256;
 
-// logits and P may be the same buffer: a wave reads all of its matrices
-// before it writes any, and no wave touches another wave's matrices.
+using FwdTiles = float[kBlock / 64][stage_tile_floats<16>()];
+
+// One forward workgroup: matrices block*256 .. block*256+255.  logits and P
+// may be the same buffer: a wave reads all of its matrices before it writes
+// any, and no wave touches another wave's matrices.
 template <int SOLVER>
-__global__ __launch_bounds__(kBlock) void birkhoff_fwd_kernel(const float* logits, float* P,
-                                                              uint8_t* __restrict__ iters,
-                                                              int64_t B, SolverOpts o)
+MHC_DEV void fwd_block(const float* logits, float* P, uint8_t* __restrict__ iters, int64_t B,
+                       const SolverOpts& o, FwdTiles& tiles, int64_t block)
 {
-    __shared__ float tiles[kBlock / 64][stage_tile_floats<16>()];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int64_t first = (int64_t)blockIdx.x * kBlock + 64 * w;
+    const int64_t first = block * kBlock + 64 * w;
     if (first >= B) return;  // the whole wave is past the batch
     float a[16];
     load_records_v4<16>(logits, first, B, tiles[w], a, lane);
@@ -46,6 +47,15 @@ __global__ __launch_bounds__(kBlock) void birkhoff_fwd_kernel(const float* logit
         store_records_v4<16>(P, first, B, tiles[w], p, lane);
     }
     if (iters != nullptr && first + lane < B) iters[first + lane] = (uint8_t)it;
+}
+
+template <int SOLVER>
+__global__ __launch_bounds__(kBlock) void birkhoff_fwd_kernel(const float* logits, float* P,
+                                                              uint8_t* __restrict__ iters,
+                                                              int64_t B, SolverOpts o)
+{
+    __shared__ FwdTiles tiles;
+    fwd_block<SOLVER>(logits, P, iters, B, o, tiles, blockIdx.x);
 }
 
 // Backward: one row per lane (quad = one matrix), so loads and stores are
@@ -75,6 +85,69 @@ __global__ __launch_bounds__(kBlock) void birkhoff_bwd_kernel(const float4* __re
     float o[4];
     project_bwd_row(p, g, o);
     if (ok) mhc_store_stream(dA + r, make_float4(o[0], o[1], o[2], o[3]));
+}
+
+// The backward for the workgroups of birkhoff_pipeline_kernel: the same
+// row-per-lane arithmetic as birkhoff_bwd_kernel (bit-identical results), but
+// each lane takes kPipeRows rows, kBlock apart, with all of their loads issued
+// before the first is used, so that an eighth as many waves keep as many
+// bytes in flight in the SIMD slots the forward leaves free (at 131072
+// matrices: one backward workgroup per CU beside two forward ones; 8 rows
+// measured faster there than 1, 2, 4 or 16).  Every row index is a multiple
+// of 4 plus the lane's place in its quad, so quads stay whole.
+constexpr int kPipeRows = 8;
+
+MHC_DEV void bwd_block_rows(const float4* __restrict__ P, const float4* G, float4* dA, int64_t B,
+                            int64_t block)
+{
+    const int64_t rows = 4 * B;
+    const int64_t r0 = block * (kBlock * kPipeRows) + threadIdx.x;
+    float4 pv[kPipeRows], gv[kPipeRows];
+#pragma unroll
+    for (int j = 0; j < kPipeRows; ++j) {
+        const int64_t r = r0 + j * kBlock;
+        const int64_t rc = r < rows ? r : rows - 1;
+        pv[j] = mhc_load_stream(P + rc);
+        gv[j] = mhc_load_stream(G + rc);
+    }
+#pragma unroll
+    for (int j = 0; j < kPipeRows; ++j) {
+        const int64_t r = r0 + j * kBlock;
+        const bool ok = r < rows;
+        const float p[4] = {ok ? pv[j].x : 0.f, ok ? pv[j].y : 0.f, ok ? pv[j].z : 0.f,
+                            ok ? pv[j].w : 0.f};
+        const float g[4] = {ok ? gv[j].x : 0.f, ok ? gv[j].y : 0.f, ok ? gv[j].z : 0.f,
+                            ok ? gv[j].w : 0.f};
+        float d[4];
+        project_bwd_row(p, g, d);
+        if (ok) mhc_store_stream(dA + r, make_float4(d[0], d[1], d[2], d[3]));
+    }
+}
+
+// Forward of one batch and backward of another in one launch: workgroups
+// below fwd_blocks run birkhoff_fwd_kernel's work, the rest the backward.
+// The two halves complement each other on the chip: the forward is bound by
+// the latency of its solve at two waves per SIMD and leaves HBM mostly idle,
+// the backward is bound by HBM and needs few issue slots, so the backward's
+// workgroups fill the SIMD slots the forward leaves free.  Forward
+// workgroups come first, so they are dispatched first and spread evenly over
+// the CUs (orders that mix backward workgroups in among them, round-robin or
+// in rounds of eight, one per XCD, left some SIMDs with more forward waves
+// and measured 25-30 % slower at 131072 matrices).  The batches are
+// independent (the ABI rejects overlaps between them), as when a trainer
+// runs micro-batch k's forward while micro-batch k-1 goes backward, or
+// recomputes one layer's projection during another layer's backward.
+template <int SOLVER>
+__global__ __launch_bounds__(kBlock) void birkhoff_pipeline_kernel(
+    const float* logits, float* P, uint8_t* __restrict__ iters, int64_t B, SolverOpts o,
+    const float4* __restrict__ Pb, const float4* Gb, float4* dAb, int64_t Bb,
+    unsigned fwd_blocks)
+{
+    __shared__ FwdTiles tiles;
+    if (blockIdx.x < fwd_blocks)
+        fwd_block<SOLVER>(logits, P, iters, B, o, tiles, blockIdx.x);
+    else
+        bwd_block_rows(Pb, Gb, dAb, Bb, (int64_t)(blockIdx.x - fwd_blocks));
 }
 
 // Solve and differentiate in one pass: lane per matrix, the projection
@@ -147,6 +220,25 @@ hipError_t launch_birkhoff_bwd(const float* P, const float* G, float* dA, int64_
     hipLaunchKernelGGL(birkhoff_bwd_kernel, grid, dim3(kBlock), 0, stream,
                        reinterpret_cast<const float4*>(P), reinterpret_cast<const float4*>(G),
                        reinterpret_cast<float4*>(dA), B);
+    return hipGetLastError();
+}
+
+hipError_t launch_birkhoff_pipeline(const float* logits, float* P, uint8_t* iters, int64_t B,
+                                   const SolverOpts& o, const float* Pb, const float* Gb,
+                                   float* dAb, int64_t Bb, hipStream_t stream)
+{
+    const int64_t fwd_blocks = (B + kBlock - 1) / kBlock;
+    const int64_t bwd_blocks = (4 * Bb + kBlock * kPipeRows - 1) / (kBlock * kPipeRows);
+    const dim3 grid((unsigned)(fwd_blocks + bwd_blocks));
+    const float4* P4 = reinterpret_cast<const float4*>(Pb);
+    const float4* G4 = reinterpret_cast<const float4*>(Gb);
+    float4* dA4 = reinterpret_cast<float4*>(dAb);
+    if (o.solver == 0)
+        hipLaunchKernelGGL(birkhoff_pipeline_kernel<0>, grid, dim3(kBlock), 0, stream, logits, P,
+                           iters, B, o, P4, G4, dA4, Bb, (unsigned)fwd_blocks);
+    else
+        hipLaunchKernelGGL(birkhoff_pipeline_kernel<1>, grid, dim3(kBlock), 0, stream, logits, P,
+                           iters, B, o, P4, G4, dA4, Bb, (unsigned)fwd_blocks);
     return hipGetLastError();
 }
 

@@ -18,6 +18,10 @@ hipError_t launch_birkhoff_bwd_recompute(const float* logits, const float* G, fl
 hipError_t launch_birkhoff_fwd_bwd(const float* logits, const float* G, float* P, float* dA,
                                    uint8_t* iters, int64_t B, const SolverOpts& o,
                                    hipStream_t stream);
+// Forward of (logits, P, B) and backward of (Pb, Gb -> dAb, Bb) in one launch.
+hipError_t launch_birkhoff_pipeline(const float* logits, float* P, uint8_t* iters, int64_t B,
+                                   const SolverOpts& o, const float* Pb, const float* Gb,
+                                   float* dAb, int64_t Bb, hipStream_t stream);
 // n x n projection for n in {1, 2, 3, 5, 6, 7, 8} (4 has its own kernels).
 hipError_t launch_birkhoff_fwd_n(const float* logits, float* P, uint8_t* iters, int64_t B, int n,
                                  const SolverOpts& o, hipStream_t stream);

@@ -99,6 +99,33 @@ def birkhoff_bwd(P: torch.Tensor, grad_P: torch.Tensor, out=None):
     return dA
 
 
+def birkhoff_pipeline_step(logits: torch.Tensor, P_bwd: torch.Tensor, grad_P: torch.Tensor, *,
+                           solver="newton", max_iters=None, tol=None, warm_sweeps=None, out=None,
+                           out_grad=None, return_iters=False):
+    """The forward of one batch and the backward of another, independent one
+    in a single launch: P = projection(logits) and dL/dlogits of the other
+    batch from its P_bwd and dL/dP.  Bit for bit the results of birkhoff_fwd
+    and birkhoff_bwd; both batches are [..., 4, 4] fp32 on one device, and
+    either may be empty.  Returns (P, grad) (and the forward's iteration codes
+    if ``return_iters``)."""
+    _need(logits, "logits", torch.float32, (4, 4))
+    _need(P_bwd, "P_bwd", torch.float32, (4, 4))
+    _need(grad_P, "grad_P", torch.float32, (4, 4))
+    _same(grad_P, "grad_P", P_bwd, "P_bwd")
+    if P_bwd.device != logits.device:
+        raise ValueError(f"P_bwd must be on {logits.device}, got {P_bwd.device}")
+    P = _out(out, "out", torch.float32, logits.shape, logits.device)
+    dA = _out(out_grad, "out_grad", torch.float32, P_bwd.shape, P_bwd.device)
+    it = torch.empty(logits.shape[:-2], dtype=torch.uint8, device=logits.device) if return_iters else None
+    o = make_opts(solver, max_iters, tol, warm_sweeps)
+    with torch.cuda.device(logits.device):
+        check(lib().mhc_birkhoff_pipeline_step(_ptr(logits), _ptr(P), logits.numel() // 16,
+                                               ctypes.byref(o), _ptr(it), _ptr(P_bwd),
+                                               _ptr(grad_P), _ptr(dA), P_bwd.numel() // 16,
+                                               _stream(logits.device)))
+    return (P, dA, it) if return_iters else (P, dA)
+
+
 def birkhoff_fwd_n(logits: torch.Tensor, *, solver="newton", max_iters=None, tol=None,
                    warm_sweeps=None, out=None, return_iters=False):
     """Project [..., n, n] fp32 logits (1 <= n <= 8) onto the doubly

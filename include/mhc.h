@@ -16,6 +16,9 @@
  *   mhc_birkhoff_fwd_bwd
  *                       projection and gradient in one pass, for when dL/dP
  *                       is already known when the projection is computed
+ *   mhc_birkhoff_pipeline_step
+ *                       the projection of one batch and the gradient of
+ *                       another in one launch (overlapped micro-batches)
  *   mhc_stream_mix      out[t,i,:] = sum_j H[t,i,j] x[t,j,:], optionally with
  *                       the projection of H's logits fused in
  *   mhc_stream_mix_bwd  gradients of the stream mix
@@ -69,8 +72,9 @@ extern "C" {
  * -1 (the solver's own choice) the default of mhc_proj_opts.warm_sweeps; 3
  * makes -1 the default of mhc_proj_opts.max_iters as well (30 Newton
  * iterations, 1000 Sinkhorn sweeps) and bounds every call's batch by
- * MHC_MAX_BATCH / MHC_MAX_TOKENS. */
-#define MHC_ABI_VERSION 3
+ * MHC_MAX_BATCH / MHC_MAX_TOKENS; 4 adds mhc_birkhoff_pipeline_step and
+ * mhc_layer_bwd_noalloc. */
+#define MHC_ABI_VERSION 4
 
 /* Largest batch one call accepts: B matrices for the projection calls, T
  * tokens for the stream-mix and layer calls.  Larger values return
@@ -209,6 +213,36 @@ mhc_status mhc_birkhoff_bwd_recompute(const float* logits, const float* grad_P,
 mhc_status mhc_birkhoff_fwd_bwd(const float* logits, const float* grad_P, float* P,
                                 float* grad_logits, int64_t B, const mhc_proj_opts* opts,
                                 uint8_t* iters, void* stream);
+
+/* mhc_birkhoff_pipeline_step -- the forward of one batch and the backward of
+ * another, independent one, in a single launch.
+ *
+ * For schedules that overlap forward and backward work of different
+ * micro-batches, or recompute one layer's projection during another layer's
+ * backward instead of keeping it (neo-ai mHC paper summary, systems section:
+ * recomputation of the mHC intermediates and the extended DualPipe
+ * schedule).  The results are bit for bit those of mhc_birkhoff_fwd on
+ * (logits, P, B) and mhc_birkhoff_bwd on (P_bwd, grad_P, grad_logits, B_bwd);
+ * what changes is that both run at once.  The forward solve is bound by its
+ * own latency and leaves HBM mostly idle, the backward is bound by HBM, so
+ * the pair takes about as long as the forward alone where two launches in
+ * sequence take the sum.
+ *
+ *   logits, P, B, opts, iters
+ *                as for mhc_birkhoff_fwd (the forward batch)
+ *   P_bwd, grad_P, grad_logits, B_bwd
+ *                as P, grad_P, grad_logits, B of mhc_birkhoff_bwd (the
+ *                backward batch)
+ *   The forward's outputs (P, iters) must not overlap any backward array and
+ *   grad_logits must not overlap logits, P or iters; the two batches' inputs
+ *   may share memory.  Either batch may be empty (B = 0 or B_bwd = 0: only the
+ *   other half runs; its pointers are then not used).  Errors as for
+ *   mhc_birkhoff_fwd and mhc_birkhoff_bwd; nothing is enqueued on error.
+ */
+mhc_status mhc_birkhoff_pipeline_step(const float* logits, float* P, int64_t B,
+                                      const mhc_proj_opts* opts, uint8_t* iters,
+                                      const float* P_bwd, const float* grad_P,
+                                      float* grad_logits, int64_t B_bwd, void* stream);
 
 /* mhc_birkhoff_fwd_n / mhc_birkhoff_bwd_n -- the projection and its gradient
  * for a batch of n x n matrices, 1 <= n <= 8.

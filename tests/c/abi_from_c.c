@@ -28,7 +28,7 @@ int main(void)
     mhc_proj_opts o;
     mhc_layer_args la;
 
-    CHECK(mhc_abi_version() == 3);
+    CHECK(mhc_abi_version() == 4);
     CHECK(strcmp(mhc_status_string(MHC_OK), "ok") == 0);
     CHECK(strcmp(mhc_status_string(MHC_ERR_INVALID_ARGUMENT), "invalid argument") == 0);
     CHECK(mhc_last_error() != NULL);

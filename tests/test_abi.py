@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_strings(L):
-    assert L.mhc_abi_version() == 3
+    assert L.mhc_abi_version() == 4
     assert L.mhc_status_string(0) == b"ok"
     assert L.mhc_status_string(1) == b"invalid argument"
     assert L.mhc_status_string(2) == b"unsupported"
@@ -122,6 +122,48 @@ def test_fwd_bwd_argument_errors(L):
     o.warm_sweeps = -2
     assert f(A, G, P, D, 3, ctypes.byref(o), None, None) == INVALID
     assert "warm_sweeps" in _err(L)
+
+
+def test_pipeline_step_argument_errors(L):
+    """mhc_birkhoff_pipeline_step: both batches empty is a no-op; each half is
+    checked as mhc_birkhoff_fwd / mhc_birkhoff_bwd check it, and across the
+    halves every output is checked against every array of the other half
+    (inputs of both may share memory).  FAKE pointers are never dereferenced:
+    every call below fails validation."""
+    f = L.mhc_birkhoff_pipeline_step
+    A, P, Pb, G, D = FAKE, FAKE + 8192, FAKE + 16384, FAKE + 24576, FAKE + 32768
+    assert f(None, None, 0, None, None, None, None, None, 0, None) == 0
+    assert f(A, P, -1, None, None, Pb, G, D, 3, None) == INVALID
+    assert "B=-1" in _err(L)
+    assert f(A, P, 3, None, None, Pb, G, D, -1, None) == INVALID
+    assert "B_bwd" in _err(L)
+    # the forward half as mhc_birkhoff_fwd checks it
+    assert f(A, None, 3, None, None, Pb, G, D, 3, None) == INVALID
+    assert f(A, A + 64, 3, None, None, Pb, G, D, 3, None) == INVALID
+    assert "P partially overlaps logits" in _err(L)
+    # the backward half as mhc_birkhoff_bwd checks it
+    assert f(A, P, 3, None, None, Pb, G, Pb, 3, None) == INVALID
+    assert "grad_logits overlaps P" in _err(L)
+    assert f(A, P, 3, None, None, Pb, G + 4, D, 3, None) == INVALID
+    assert "aligned" in _err(L)
+    # across the halves
+    for Pf in (Pb, G + 64, D):
+        assert f(A, Pf, 3, None, None, Pb, G, D, 3, None) == INVALID
+        assert "P overlaps P_bwd, grad_P or grad_logits" in _err(L)
+    assert f(A, P, 3, None, None, Pb, G, A + 64, 3, None) == INVALID
+    assert "grad_logits overlaps logits" in _err(L)
+    assert f(A, P, 3, None, None, Pb, G, P, 3, None) == INVALID  # both write P's memory
+    assert "P overlaps P_bwd, grad_P or grad_logits" in _err(L)
+    assert f(A, P, 3, None, ctypes.c_void_p(G + 8), Pb, G, D, 3, None) == INVALID
+    assert "iters overlaps" in _err(L)
+    # a bad half is refused even when the other one is empty
+    assert f(A, A + 64, 3, None, None, None, None, None, 0, None) == INVALID
+    assert f(None, None, 0, None, None, Pb, G, Pb, 3, None) == INVALID
+    o = ProjOpts()
+    L.mhc_proj_opts_default(ctypes.byref(o))
+    o.max_iters = 0
+    assert f(A, P, 3, ctypes.byref(o), None, Pb, G, D, 3, None) == INVALID
+    assert "max_iters" in _err(L)
 
 
 def test_bwd_recompute_argument_errors(L):

@@ -88,3 +88,65 @@ def test_fused_recompute_and_n8_graph_replays(gpu_lib):
         assert torch.equal(P8, P8e) and torch.equal(dA8, dA8e), f"replay {rep}: 8x8"
         gpu_lib.birkhoff_fwd_n(A8[:100])  # eager work between replays
         torch.cuda.synchronize()
+
+
+def _overlapped(gpu_lib, sets, main, side):
+    """Forward of batch k on `main` while the backward of batch k-1 runs on
+    `side`; the forward of batch k waits for the backward of batch k-2."""
+    fwd_done = [torch.cuda.Event() for _ in sets]
+    bwd_done = [torch.cuda.Event() for _ in sets]
+    side.wait_stream(main)
+    for k, (A, P, G, dA) in enumerate(sets):
+        if k >= 2:
+            main.wait_event(bwd_done[k - 2])
+        gpu_lib.birkhoff_fwd(A, out=P)
+        fwd_done[k].record(main)
+        with torch.cuda.stream(side):
+            side.wait_event(fwd_done[k])
+            gpu_lib.birkhoff_bwd(P, G, out=dA)
+            bwd_done[k].record(side)
+    main.wait_stream(side)
+
+
+def test_two_stream_overlap(gpu_lib):
+    """Batches whose forward overlaps another batch's backward on a second
+    stream (eagerly and in a captured graph) give the serial results bit for
+    bit: the kernels share no state between launches."""
+    B = 20000  # more waves than one launch keeps resident alongside the other
+    sets = []
+    for k in range(5):
+        A = torch.from_numpy(W.logits_batch("normal10", B, 70 + k)).cuda()
+        G = torch.from_numpy(W.grad_batch(B, 80 + k)).cuda()
+        sets.append((A, torch.empty_like(A), G, torch.empty_like(A)))
+    ref = []
+    for A, P, G, dA in sets:
+        Pe = gpu_lib.birkhoff_fwd(A)
+        ref.append((Pe, gpu_lib.birkhoff_bwd(Pe, G)))
+    torch.cuda.synchronize()
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+
+    def check(label):
+        torch.cuda.synchronize()
+        for k, ((A, P, G, dA), (Pe, dAe)) in enumerate(zip(sets, ref)):
+            assert torch.equal(P, Pe), f"{label}: P of batch {k}"
+            assert torch.equal(dA, dAe), f"{label}: dA of batch {k}"
+
+    def clear():
+        for A, P, G, dA in sets:
+            P.fill_(float("nan"))
+            dA.fill_(float("nan"))
+
+    clear()
+    _overlapped(gpu_lib, sets, main, side)
+    check("eager")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        _overlapped(gpu_lib, sets, torch.cuda.current_stream(), side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        clear()
+        g.replay()
+        check(f"replay {rep}")
+        gpu_lib.birkhoff_fwd(sets[0][0][:100])  # eager work between replays
+        torch.cuda.synchronize()

@@ -1,0 +1,93 @@
+"""mhc_birkhoff_pipeline_step: the forward of one batch and the backward of
+another in one launch.  Its results must be bit for bit those of
+mhc_birkhoff_fwd and mhc_birkhoff_bwd called apart (same per-matrix and
+per-row arithmetic), for batch sizes that leave ragged tails in both halves
+and for either half empty; a sample is also compared with the float64 oracle
+at the projection bars (max |dP| <= 1e-5; gradient within
+1e-4 max|ref| + 1e-5 max|G|)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import birkhoff_project, birkhoff_project_bwd
+
+pytestmark = pytest.mark.gpu
+
+
+def _batch(kind, B, seed):
+    A = torch.from_numpy(W.logits_batch(kind, B, seed)).cuda()
+    G = torch.from_numpy(W.grad_batch(B, seed + 1)).cuda()
+    return A, G
+
+
+@pytest.mark.parametrize("Bf,Bb", [(3000, 5000), (5000, 3000), (1, 1), (65, 257), (257, 0),
+                                   (0, 65), (4099, 1023), (1024, 1024), (20000, 20000)])
+def test_pipeline_matches_separate_calls(gpu_lib, Bf, Bb):
+    bp = gpu_lib
+    A, _ = _batch("normal10", max(Bf, 1), 90)
+    A = A[:Bf]
+    Ab, Gb = _batch("normal2", max(Bb, 1), 92)
+    Ab, Gb = Ab[:Bb], Gb[:Bb]
+    Pb = bp.birkhoff_fwd(Ab)  # the backward batch's forward, done earlier
+    P_ref, it_ref = bp.birkhoff_fwd(A, return_iters=True)
+    dA_ref = bp.birkhoff_bwd(Pb, Gb)
+    P, dA, it = bp.birkhoff_pipeline_step(A, Pb, Gb, return_iters=True)
+    torch.cuda.synchronize()
+    assert torch.equal(P, P_ref)
+    assert torch.equal(it, it_ref)
+    assert torch.equal(dA, dA_ref)
+
+
+def test_pipeline_against_oracle(gpu_lib):
+    bp = gpu_lib
+    Bf, Bb = 700, 900
+    A, _ = _batch("normal10", Bf, 94)
+    Ab, Gb = _batch("diag20", Bb, 96)
+    Pb = bp.birkhoff_fwd(Ab)
+    P, dA = bp.birkhoff_pipeline_step(A, Pb, Gb)
+    torch.cuda.synchronize()
+    P_or = birkhoff_project(A.cpu().numpy().astype(np.float64))
+    assert np.abs(P.cpu().numpy() - P_or).max() <= 1e-5
+    Pb_or = birkhoff_project(Ab.cpu().numpy().astype(np.float64))
+    G64 = Gb.cpu().numpy().astype(np.float64)
+    ref = birkhoff_project_bwd(Pb_or, G64)
+    err = np.abs(dA.cpu().numpy() - ref).max(axis=(-2, -1))
+    bar = 1e-4 * np.abs(ref).max(axis=(-2, -1)) + 1e-5 * np.abs(G64).max(axis=(-2, -1))
+    assert (err <= bar).all(), f"worst {np.max(err / bar):.2f} of the bar"
+
+
+def test_pipeline_aliases_and_shared_inputs(gpu_lib):
+    """P may be the forward's logits and grad_logits the backward's grad_P
+    (each exactly), and both halves may read the same input memory."""
+    bp = gpu_lib
+    B = 2000
+    A, G = _batch("normal10", B, 98)
+    Ab, _ = _batch("normal1", B, 100)
+    Pb = bp.birkhoff_fwd(Ab)
+    P_ref = bp.birkhoff_fwd(A)
+    dA_ref = bp.birkhoff_bwd(Pb, G)
+    # the forward batch's logits double as the backward's dL/dP (read by both)
+    dA_shared_ref = bp.birkhoff_bwd(Pb, A)
+    P2, dA2 = bp.birkhoff_pipeline_step(A, Pb, A)
+    torch.cuda.synchronize()
+    assert torch.equal(P2, P_ref) and torch.equal(dA2, dA_shared_ref)
+    Ai, Gi = A.clone(), G.clone()
+    bp.birkhoff_pipeline_step(Ai, Pb, Gi, out=Ai, out_grad=Gi)
+    torch.cuda.synchronize()
+    assert torch.equal(Ai, P_ref) and torch.equal(Gi, dA_ref)
+
+
+def test_pipeline_binding_checks(gpu_lib):
+    bp = gpu_lib
+    A, G = _batch("normal10", 100, 102)
+    Pb = bp.birkhoff_fwd(A)
+    with pytest.raises(ValueError):
+        bp.birkhoff_pipeline_step(A, Pb, G[:99])
+    buf = torch.full((108, 4, 4), 7.0, device="cuda")
+    with pytest.raises(ValueError):
+        bp.birkhoff_pipeline_step(A, Pb, G, out=buf[:99])
+    with pytest.raises(ValueError):
+        bp.birkhoff_pipeline_step(A, Pb, G, out_grad=buf[:99])
+    torch.cuda.synchronize()
+    assert bool((buf == 7.0).all())
