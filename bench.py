@@ -88,16 +88,18 @@ KERNEL_SOURCES = {
     "layer": ("devmath.h", "proj4.h", "kernels.h", "layer.hip"),
 }
 MEASURED = {
-    "birkhoff_fwd_131072_cfg2": {"fetch": 8534119, "write": 8388969, "valu": 2428524, "trans": 122685, "sha": "826a4b73e55c307b"},
-    "birkhoff_bwd_131072_cfg2": {"fetch": 16805925, "write": 8388691, "valu": 1122304, "trans": 24576, "sha": "826a4b73e55c307b"},
-    "birkhoff_fwd_1048576_cfg3": {"fetch": 67252286, "write": 67116402, "valu": 18806282, "trans": 946129, "sha": "826a4b73e55c307b"},
-    "birkhoff_bwd_1048576_cfg3": {"fetch": 134231305, "write": 67109165, "valu": 8978432, "trans": 196608, "sha": "826a4b73e55c307b"},
-    "birkhoff_fwd_bwd_131072_cfg2": {"fetch": 16957581, "write": 16777216, "valu": 2977371, "trans": 128829, "sha": "826a4b73e55c307b"},
-    "birkhoff_fwd_n8_131072_cfg2": {"fetch": 40909582, "write": 59769900, "valu": 22793495, "trans": 745229, "sha": "717dd4767b586ebf"},
-    "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67434180, "write": 33555104, "valu": 6424576, "trans": 14336, "sha": "717dd4767b586ebf"},
-    "stream_mix_fwd_16384x4x4096": {"fetch": 538003954, "write": 537926485, "valu": 25666560, "trans": 64512, "sha": "2277bf78266d3f85"},
-    "stream_mix_bwd_16384x4x4096": {"fetch": 1074735298, "write": 537937045, "valu": 50135040, "trans": 0, "sha": "2277bf78266d3f85"},
-    "layer_step_65536x4x7168": {"fetch": 30714158805, "write": 9469203225, "mfma": {"layer_maps_kernel<0>": 7340032, "layer_dx_kernel": 14680064, "layer_dw_kernel": 14680064}, "us": {"layer_maps_kernel<0>": 666.72, "layer_dx_kernel": 2577.87, "layer_dw_kernel": 753.14}, "sha": "940294f1486bfe3d"},
+    "birkhoff_fwd_131072_cfg2": {"fetch": 8510578, "write": 8388960, "valu": 2428524, "trans": 122685, "sha": "fd609256ebeca36a"},
+    "birkhoff_bwd_131072_cfg2": {"fetch": 16805885, "write": 8389131, "valu": 1122304, "trans": 24576, "sha": "fd609256ebeca36a"},
+    "birkhoff_pipeline_131072_cfg2": {"fetch": 25396092, "write": 16777230, "valu": 3541595, "trans": 147261, "sha": "fd609256ebeca36a"},
+    "birkhoff_fwd_1048576_cfg3": {"fetch": 67233402, "write": 67115104, "valu": 18806279, "trans": 946129, "sha": "fd609256ebeca36a"},
+    "birkhoff_bwd_1048576_cfg3": {"fetch": 134231515, "write": 67109146, "valu": 8978432, "trans": 196608, "sha": "fd609256ebeca36a"},
+    "birkhoff_pipeline_1048576_cfg3": {"fetch": 201540637, "write": 134221596, "valu": 27710845, "trans": 1142737, "sha": "fd609256ebeca36a"},
+    "birkhoff_fwd_bwd_131072_cfg2": {"fetch": 16968802, "write": 16777482, "valu": 2977371, "trans": 128829, "sha": "fd609256ebeca36a"},
+    "birkhoff_fwd_n8_131072_cfg2": {"fetch": 40903655, "write": 59770142, "valu": 22793495, "trans": 745229, "sha": "717dd4767b586ebf"},
+    "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67434179, "write": 33555014, "valu": 6424576, "trans": 14336, "sha": "717dd4767b586ebf"},
+    "stream_mix_fwd_16384x4x4096": {"fetch": 538003847, "write": 537927403, "valu": 25666560, "trans": 64512, "sha": "2277bf78266d3f85"},
+    "stream_mix_bwd_16384x4x4096": {"fetch": 1074736109, "write": 537958827, "valu": 50135040, "trans": 0, "sha": "2277bf78266d3f85"},
+    "layer_step_65536x4x7168": {"fetch": 30744916441, "write": 9469207963, "mfma": {"layer_maps_kernel<0>": 7340032, "layer_dx_kernel": 14680064, "layer_dw_kernel": 14680064}, "us": {"layer_maps_kernel<0>": 671.32, "layer_dx_kernel": 2585.1, "layer_dw_kernel": 753.98}, "sha": "ba623a2b65a6821b"},
 }
 
 
@@ -502,7 +504,8 @@ def bench_projection(args, bp, torch, config):
         "iters": iteration_stats(bp, torch, A, n),
     }
     if r["overlapped_ms_per_step"] is not None:
-        out["overlapped"] = overlapped_block(r, B, fwd_bytes + bwd_bytes)
+        out["overlapped"] = overlapped_block(r, B, fwd_bytes + bwd_bytes,
+                                             f"birkhoff_pipeline_{B}_cfg{config}")
     if config == 2 and n == 4 and not (args.recompute or args.fused) and not args.no_config3:
         out["config3"] = config3_block(args, bp, torch)
     if not args.no_cpu_baseline:
@@ -511,7 +514,7 @@ def bench_projection(args, bp, torch, config):
     return out
 
 
-def overlapped_block(r, B, step_bytes):
+def overlapped_block(r, B, step_bytes, key=None):
     """The same steps with batch k's forward and batch k-1's backward in one
     launch (mhc_birkhoff_pipeline_step; see time_projection).  Reported
     beside the headline, never as it: the headline step keeps each batch's
@@ -522,7 +525,9 @@ def overlapped_block(r, B, step_bytes):
                         "k-1 in one launch (a forward alone opens the sequence, a backward "
                         "alone closes it); results bit-identical to the serial steps",
             "value": B / (ms / 1e3), "unit": "projections/s", "ms_per_step": ms,
-            "step_GBs": gbs, "step_frac": gbs / HBM_PEAK_GBS, "timing": "median of 3 replays"}
+            "step_GBs": gbs, "step_frac": gbs / HBM_PEAK_GBS, "timing": "median of 3 replays",
+            "traffic": (lambda m: m["fetch"] + m["write"] if m else None)(measured(key) if key else None),
+            "algorithmic_bytes": step_bytes * B}
 
 
 def forward_roofline(kname, alg_bytes, fwd_ms, B, m):
@@ -574,7 +579,7 @@ def config3_block(args, bp, torch):
             "bwd_frac": BWD_BYTES * B / (bwd_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
             "step_us_median_of_5": r["step_ms_median"] * 1e3, "roofline_fwd": roof, "valu": valu,
             "iters": iteration_stats(bp, torch, A),
-            "overlapped": overlapped_block(r, B, FWD_BYTES + BWD_BYTES)}
+            "overlapped": overlapped_block(r, B, FWD_BYTES + BWD_BYTES, f"birkhoff_pipeline_{B}_cfg3")}
 
 
 def _time_loop(torch, body, steps, warmup):
