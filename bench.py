@@ -84,8 +84,8 @@ def spin_ahead(torch):
 KERNEL_SOURCES = {
     "proj": ("devmath.h", "proj4.h", "stage.h", "birkhoff.hip"),
     "projn": ("devmath.h", "proj4.h", "projn.h", "stage.h", "birkhoffn.hip"),
-    "mix": ("devmath.h", "proj4.h", "mix.hip"),
-    "layer": ("devmath.h", "proj4.h", "kernels.h", "layer.hip"),
+    "mix": ("devmath.h", "proj4.h", "wave.h", "mix.hip"),
+    "layer": ("devmath.h", "proj4.h", "wave.h", "kernels.h", "layer.hip"),
 }
 MEASURED = {
     "birkhoff_fwd_131072_cfg2": {"fetch": 8510578, "write": 8388960, "valu": 2428524, "trans": 122685, "sha": "fd609256ebeca36a"},
@@ -97,9 +97,9 @@ MEASURED = {
     "birkhoff_fwd_bwd_131072_cfg2": {"fetch": 16968802, "write": 16777482, "valu": 2977371, "trans": 128829, "sha": "fd609256ebeca36a"},
     "birkhoff_fwd_n8_131072_cfg2": {"fetch": 40903655, "write": 59770142, "valu": 22793495, "trans": 745229, "sha": "717dd4767b586ebf"},
     "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67434179, "write": 33555014, "valu": 6424576, "trans": 14336, "sha": "717dd4767b586ebf"},
-    "stream_mix_fwd_16384x4x4096": {"fetch": 538003847, "write": 537927403, "valu": 25666560, "trans": 64512, "sha": "2277bf78266d3f85"},
-    "stream_mix_bwd_16384x4x4096": {"fetch": 1074736109, "write": 537958827, "valu": 50135040, "trans": 0, "sha": "2277bf78266d3f85"},
-    "layer_step_65536x4x7168": {"fetch": 30744916441, "write": 9469207963, "mfma": {"layer_maps_kernel<0>": 7340032, "layer_dx_kernel": 14680064, "layer_dw_kernel": 14680064}, "us": {"layer_maps_kernel<0>": 671.32, "layer_dx_kernel": 2585.1, "layer_dw_kernel": 753.98}, "sha": "ba623a2b65a6821b"},
+    "stream_mix_fwd_16384x4x4096": {"fetch": 537993670, "write": 537929429, "valu": 25666560, "trans": 64512, "sha": "1908a484b992311d"},
+    "stream_mix_bwd_16384x4x4096": {"fetch": 1074726402, "write": 537952992, "valu": 49479680, "trans": 0, "sha": "1908a484b992311d"},
+    "layer_step_65536x4x7168": {"fetch": 30737211015, "write": 9469199865, "mfma": {"layer_maps_kernel<0>": 7340032, "layer_dx_kernel": 14680064, "layer_dw_kernel": 14680064}, "us": {"layer_maps_kernel<0>": 665.79, "layer_dx_kernel": 2602.6, "layer_dw_kernel": 749.98}, "sha": "53e5ab677c7bb8e1"},
 }
 
 

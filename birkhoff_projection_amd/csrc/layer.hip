@@ -34,6 +34,7 @@
 
 #include "kernels.h"
 #include "proj4.h"
+#include "wave.h"
 
 namespace mhc {
 
@@ -90,25 +91,6 @@ MHC_DEV void split8(const float* v, bf16x8& hi, bf16x8& lo)
         hi[e] = h;
         lo[e] = (__bf16)(v[e] - (float)h);
     }
-}
-
-// Sum 32 per-lane partials over a wave64 by butterfly halving; afterwards
-// lane l holds the total of value ((l >> 1) & 31).
-MHC_DEV float wave_sum32(float* v)
-{
-#pragma unroll
-    for (int m = 32, n = 32; m >= 2; m >>= 1, n >>= 1) {
-        const bool up = (threadIdx.x & m) != 0;
-        const int h = n / 2;
-#pragma unroll
-        for (int k = 0; k < h; ++k) {
-            const float lo = mhc_opaque(v[k]), hi = mhc_opaque(v[k + h]);
-            const float keep = up ? hi : lo;
-            const float send = up ? lo : hi;
-            v[k] = keep + __shfl_xor(send, m);
-        }
-    }
-    return v[0] + __shfl_xor(v[0], 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -259,9 +241,7 @@ __global__ __launch_bounds__(kBlock) void layer_maps_kernel(
                 for (int v = 0; v < 4; ++v) sRed[w][16 * tile + 4 * kq + v][m] = acc[tile][ot][v];
             }
         }
-        float s = ssq[tile];
-        s += __shfl_xor(s, 16);
-        s += __shfl_xor(s, 32);
+        const float s = sum_bit5(sum_bit4(ssq[tile]));
         if (kq == 0) sSsq[w][16 * tile + row] = s;
     }
     __syncthreads();
@@ -430,7 +410,7 @@ MHC_DEV void dots_consume(const DotsLane& L, const DotsLoads& d, int64_t i, floa
         }
     }
     if (ci == L.nch - 1) {  // the token's last chunk: reduce its dots
-        const float sm = wave_sum32(acc);
+        const float sm = wave_sum_halving<32>(acc);
         const int idx = (L.lane >> 1) & 31;
         if ((L.lane & 1) == 0 && idx < kMaps) sDots[tl][idx] = sm;
 #pragma unroll

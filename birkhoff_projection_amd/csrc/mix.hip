@@ -15,6 +15,7 @@
 // 4x4 matrices that all lanes of a workgroup share.
 #include "kernels.h"
 #include "proj4.h"
+#include "wave.h"
 
 namespace mhc {
 
@@ -136,30 +137,6 @@ __global__ __launch_bounds__(kBlock) void stream_mix_fwd_kernel(
     }
 }
 
-// Sum 16 per-lane partials over the 64 lanes of a wave.  Each butterfly step
-// sends half of the remaining values to the partner lane and keeps the other
-// half, so 16 values need 8+4+2+1 exchanges, then 2 more for the last two lane
-// bits.  Afterwards lane l holds the total of value ((l >> 2) & 15).
-MHC_DEV float wave_sum16(float* v)
-{
-#pragma unroll
-    for (int m = 32, n = 16; m >= 4; m >>= 1, n >>= 1) {
-        const bool up = (threadIdx.x & m) != 0;
-        const int h = n / 2;
-#pragma unroll
-        for (int k = 0; k < h; ++k) {
-            const float lo = mhc_opaque(v[k]), hi = mhc_opaque(v[k + h]);
-            const float keep = up ? hi : lo;
-            const float send = up ? lo : hi;
-            v[k] = keep + __shfl_xor(send, m);
-        }
-    }
-    float s = v[0];
-    s += __shfl_xor(s, 2);
-    s += __shfl_xor(s, 1);
-    return s;
-}
-
 // Backward.  One wave per token at a time (grid-stride); a lane accumulates
 // its chunks' contribution to grad_H in 16 registers, the wave reduces them
 // once per token.
@@ -209,7 +186,7 @@ __global__ __launch_bounds__(kBlock) void stream_mix_bwd_kernel(
                     for (int cc = 0; cc < 8; ++cc)
                         acc[4 * i + j] = __builtin_fmaf(gf[i][cc], xf[j][cc], acc[4 * i + j]);
         }
-        const float s = wave_sum16(acc);
+        const float s = wave_sum_halving<16>(acc);
         if ((lane & 3) == 0) gH[16 * t + (lane >> 2)] = s;
     }
 }
