@@ -20,8 +20,8 @@ Prints one JSON line:
                the counter-measured HBM bytes per launch
   iters        Newton iterations per matrix and per wave (divergence)
   overlapped   the same steps with batch k's forward and batch k-1's
-               backward in one launch (mhc_birkhoff_pipeline_step;
-               bit-identical results; beside the headline, never as it)
+               backward in one launch (mhc_birkhoff_pipeline_step; beside
+               the headline, never as it)
   config3      the same fwd+bwd step on 1,048,576 mixed-difficulty matrices,
                timed in the same run (the other end of the 128K-1M range)
   cpu_baseline the float64 oracle (fwd+bwd) on the host cores, on a bounded
@@ -88,18 +88,18 @@ KERNEL_SOURCES = {
     "layer": ("devmath.h", "proj4.h", "wave.h", "kernels.h", "layer.hip"),
 }
 MEASURED = {
-    "birkhoff_fwd_131072_cfg2": {"fetch": 8510578, "write": 8388960, "valu": 2428524, "trans": 122685, "sha": "fd609256ebeca36a"},
-    "birkhoff_bwd_131072_cfg2": {"fetch": 16805885, "write": 8389131, "valu": 1122304, "trans": 24576, "sha": "fd609256ebeca36a"},
-    "birkhoff_pipeline_131072_cfg2": {"fetch": 25396092, "write": 16777230, "valu": 3541595, "trans": 147261, "sha": "fd609256ebeca36a"},
-    "birkhoff_fwd_1048576_cfg3": {"fetch": 67233402, "write": 67115104, "valu": 18806279, "trans": 946129, "sha": "fd609256ebeca36a"},
-    "birkhoff_bwd_1048576_cfg3": {"fetch": 134231515, "write": 67109146, "valu": 8978432, "trans": 196608, "sha": "fd609256ebeca36a"},
-    "birkhoff_pipeline_1048576_cfg3": {"fetch": 201540637, "write": 134221596, "valu": 27710845, "trans": 1142737, "sha": "fd609256ebeca36a"},
-    "birkhoff_fwd_bwd_131072_cfg2": {"fetch": 16968802, "write": 16777482, "valu": 2977371, "trans": 128829, "sha": "fd609256ebeca36a"},
-    "birkhoff_fwd_n8_131072_cfg2": {"fetch": 40903655, "write": 59770142, "valu": 22793495, "trans": 745229, "sha": "717dd4767b586ebf"},
-    "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67434179, "write": 33555014, "valu": 6424576, "trans": 14336, "sha": "717dd4767b586ebf"},
-    "stream_mix_fwd_16384x4x4096": {"fetch": 537993670, "write": 537929429, "valu": 25666560, "trans": 64512, "sha": "1908a484b992311d"},
-    "stream_mix_bwd_16384x4x4096": {"fetch": 1074726402, "write": 537952992, "valu": 49479680, "trans": 0, "sha": "1908a484b992311d"},
-    "layer_step_65536x4x7168": {"fetch": 30737211015, "write": 9469199865, "mfma": {"layer_maps_kernel<0>": 7340032, "layer_dx_kernel": 14680064, "layer_dw_kernel": 14680064}, "us": {"layer_maps_kernel<0>": 665.79, "layer_dx_kernel": 2602.6, "layer_dw_kernel": 749.98}, "sha": "53e5ab677c7bb8e1"},
+    "birkhoff_fwd_131072_cfg2": {"fetch": 8518722, "write": 8388960, "valu": 2428524, "trans": 122685, "sha": "58a2d67da8cf823d"},
+    "birkhoff_bwd_131072_cfg2": {"fetch": 16805804, "write": 8389276, "valu": 1122304, "trans": 24576, "sha": "58a2d67da8cf823d"},
+    "birkhoff_pipeline_131072_cfg2": {"fetch": 25356068, "write": 16778588, "valu": 3122779, "trans": 128829, "sha": "58a2d67da8cf823d"},
+    "birkhoff_fwd_1048576_cfg3": {"fetch": 67239969, "write": 67114048, "valu": 18806279, "trans": 946129, "sha": "58a2d67da8cf823d"},
+    "birkhoff_bwd_1048576_cfg3": {"fetch": 134231380, "write": 67110362, "valu": 8978432, "trans": 196608, "sha": "58a2d67da8cf823d"},
+    "birkhoff_pipeline_1048576_cfg3": {"fetch": 201500095, "write": 134222483, "valu": 24360317, "trans": 995281, "sha": "58a2d67da8cf823d"},
+    "birkhoff_fwd_bwd_131072_cfg2": {"fetch": 16966821, "write": 16777298, "valu": 2977371, "trans": 128829, "sha": "58a2d67da8cf823d"},
+    "birkhoff_fwd_n8_131072_cfg2": {"fetch": 40957318, "write": 59770885, "valu": 22793495, "trans": 745229, "sha": "717dd4767b586ebf"},
+    "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67434293, "write": 33555422, "valu": 6424576, "trans": 14336, "sha": "717dd4767b586ebf"},
+    "stream_mix_fwd_16384x4x4096": {"fetch": 537992431, "write": 537928853, "valu": 25666560, "trans": 64512, "sha": "1908a484b992311d"},
+    "stream_mix_bwd_16384x4x4096": {"fetch": 1074725377, "write": 537953419, "valu": 49479680, "trans": 0, "sha": "1908a484b992311d"},
+    "layer_step_65536x4x7168": {"fetch": 30735264244, "write": 9469201958, "mfma": {"layer_maps_kernel<0>": 7340032, "layer_dx_kernel": 14680064, "layer_dw_kernel": 14680064}, "us": {"layer_maps_kernel<0>": 667.08, "layer_dx_kernel": 2583.56, "layer_dw_kernel": 749.28}, "sha": "53e5ab677c7bb8e1"},
 }
 
 
@@ -280,16 +280,21 @@ def time_projection(bp, torch, A_np, G_np, steps, warmup, solver="newton", recom
     # Pipelined schedule: one launch runs the forward of batch k and the
     # backward of batch k-1 (mhc_birkhoff_pipeline_step), as a trainer that
     # overlaps micro-batches would; a forward alone opens the sequence and a
-    # backward alone closes it.  Every batch still gets its forward, then
-    # its backward, and stream order alone keeps the dependencies: launch k
-    # writes P of set k and reads P of set k-1 (nsets >= 2).
+    # pipeline launch with an empty forward closes it.  Every batch still
+    # gets its forward, then its backward, and stream order alone keeps the
+    # dependencies: launch k writes P of set k and reads P of set k-1
+    # (nsets >= 2).
+    no_fwd = torch.empty((0, 4, 4), dtype=torch.float32, device=A0.device)
+
     def pipelined():
         fwd(0)
         for k in range(1, steps):
             A, P, G, dA = sets[k % nsets]
             Ap, Pp, Gp, dAp = sets[(k - 1) % nsets]
             bp.birkhoff_pipeline_step(A, Pp, Gp, out=P, out_grad=dAp, solver=solver)
-        bwd(steps - 1)
+        # the last backward from the same kernel, its forward half empty
+        A, P, G, dA = sets[(steps - 1) % nsets]
+        bp.birkhoff_pipeline_step(no_fwd, P, G, out=no_fwd, out_grad=dA, solver=solver)
 
     def events():
         return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -343,7 +348,11 @@ def time_projection(bp, torch, A_np, G_np, steps, warmup, solver="newton", recom
             dAe = bp.birkhoff_bwd_recompute(A, G, solver=solver) if recompute else bwd_fn(Pe, G)
         ref.append((Pe, dAe))
     g_over = capture(pipelined, whole=True) if overlap else None
-    for g in (g_step, g_over):
+    # the pipeline launch forms the gradient one matrix per lane, bit for bit
+    # the recompute backward's for the same logits
+    ref_over = ([(Pe, bp.birkhoff_bwd_recompute(A, G, solver=solver))
+                 for (A, P, G, dA), (Pe, dAe) in zip(touched, ref)] if overlap else None)
+    for g, refs in ((g_step, ref), (g_over, ref_over)):
         if g is None:
             continue
         for _ in range(2):
@@ -352,7 +361,7 @@ def time_projection(bp, torch, A_np, G_np, steps, warmup, solver="newton", recom
                 dA.zero_()
             g.replay()
             torch.cuda.synchronize()
-            for (A, P, G, dA), (Pe, dAe) in zip(touched, ref):
+            for (A, P, G, dA), (Pe, dAe) in zip(touched, refs):
                 if not (torch.equal(P, Pe) and torch.equal(dA, dAe)):
                     raise RuntimeError("graph replay differs from eager results")
             fwd_fn(sets[0][0], solver=solver)  # eager work between replays
@@ -522,8 +531,10 @@ def overlapped_block(r, B, step_bytes, key=None):
     ms = r["overlapped_ms_per_step"]
     gbs = step_bytes * B / (ms / 1e3) / 1e9
     return {"schedule": "mhc_birkhoff_pipeline_step: forward of batch k and backward of batch "
-                        "k-1 in one launch (a forward alone opens the sequence, a backward "
-                        "alone closes it); results bit-identical to the serial steps",
+                        "k-1 in one launch (a forward alone opens the sequence, a pipeline "
+                        "launch with an empty forward closes it); P bit-identical to the serial "
+                        "steps', the gradient to mhc_birkhoff_bwd_recompute's (one matrix per "
+                        "lane)",
             "value": B / (ms / 1e3), "unit": "projections/s", "ms_per_step": ms,
             "step_GBs": gbs, "step_frac": gbs / HBM_PEAK_GBS, "timing": "median of 3 replays",
             "traffic": (lambda m: m["fetch"] + m["write"] if m else None)(measured(key) if key else None),

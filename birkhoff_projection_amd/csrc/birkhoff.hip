@@ -87,67 +87,88 @@ __global__ __launch_bounds__(kBlock) void birkhoff_bwd_kernel(const float4* __re
     if (ok) mhc_store_stream(dA + r, make_float4(o[0], o[1], o[2], o[3]));
 }
 
-// The backward for the workgroups of birkhoff_pipeline_kernel: the same
-// row-per-lane arithmetic as birkhoff_bwd_kernel (bit-identical results), but
-// each lane takes kPipeRows rows, kBlock apart, with all of their loads issued
-// before the first is used, so that an eighth as many waves keep as many
-// bytes in flight in the SIMD slots the forward leaves free (at 131072
-// matrices: one backward workgroup per CU beside two forward ones; 8 rows
-// measured faster there than 1, 2, 4 or 16).  Every row index is a multiple
-// of 4 plus the lane's place in its quad, so quads stay whole.
-constexpr int kPipeRows = 8;
-
-MHC_DEV void bwd_block_rows(const float4* __restrict__ P, const float4* G, float4* dA, int64_t B,
-                            int64_t block)
+// The backward for the workgroups of birkhoff_pipeline_kernel: one lane per
+// matrix, as in birkhoff_solve_bwd_kernel, so the 3x3 solve runs once per
+// matrix instead of in every lane of a quad (about half the VALU
+// instructions of birkhoff_bwd_kernel, which matters here: beside the
+// forward, the two halves share the SIMDs' issue slots).  A wave issues the
+// loads of its 64 P records and 64 G records first, then moves each set
+// through its LDS tile to one record per lane; dA goes back the same way.
+// The result is bit for bit what birkhoff_solve_bwd_kernel's project_bwd
+// gives for the same P and G.
+MHC_DEV void bwd_block_lanes(const float* P, const float* G, float* dA, int64_t B,
+                             FwdTiles& tiles, int64_t block)
 {
-    const int64_t rows = 4 * B;
-    const int64_t r0 = block * (kBlock * kPipeRows) + threadIdx.x;
-    float4 pv[kPipeRows], gv[kPipeRows];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t first = block * kBlock + 64 * w;
+    if (first >= B) return;  // the whole wave is past the batch
+    constexpr int kP = record_pitch<16>();
+    const int64_t have = B - first;
+    const int64_t last = 4 * B - 1;  // last float4 of the batch
+    const float4* P4 = reinterpret_cast<const float4*>(P);
+    const float4* G4 = reinterpret_cast<const float4*>(G);
+    float4 v[2][4];
 #pragma unroll
-    for (int j = 0; j < kPipeRows; ++j) {
-        const int64_t r = r0 + j * kBlock;
-        const int64_t rc = r < rows ? r : rows - 1;
-        pv[j] = mhc_load_stream(P + rc);
-        gv[j] = mhc_load_stream(G + rc);
+    for (int i = 0; i < 4; ++i) {
+        const int64_t idx = 4 * first + lane + 64 * i;
+        v[0][i] = mhc_load_stream(P4 + (idx < last ? idx : last));
     }
 #pragma unroll
-    for (int j = 0; j < kPipeRows; ++j) {
-        const int64_t r = r0 + j * kBlock;
-        const bool ok = r < rows;
-        const float p[4] = {ok ? pv[j].x : 0.f, ok ? pv[j].y : 0.f, ok ? pv[j].z : 0.f,
-                            ok ? pv[j].w : 0.f};
-        const float g[4] = {ok ? gv[j].x : 0.f, ok ? gv[j].y : 0.f, ok ? gv[j].z : 0.f,
-                            ok ? gv[j].w : 0.f};
-        float d[4];
-        project_bwd_row(p, g, d);
-        if (ok) mhc_store_stream(dA + r, make_float4(d[0], d[1], d[2], d[3]));
+    for (int i = 0; i < 4; ++i) {
+        const int64_t idx = 4 * first + lane + 64 * i;
+        v[1][i] = mhc_load_stream(G4 + (idx < last ? idx : last));
     }
+    float* tile = tiles[w];
+    float pg[2][16];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        mhc_wave_lds_fence();  // earlier reads of the tile come first
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = 4 * (lane + 64 * i);  // float index in the wave's 64 records
+            const int rec = e / 16, col = e % 16;
+            const bool in = rec < have;
+            float* t = tile + rec * kP + col;
+            t[0] = in ? v[s][i].x : 0.f;
+            t[1] = in ? v[s][i].y : 0.f;
+            t[2] = in ? v[s][i].z : 0.f;
+            t[3] = in ? v[s][i].w : 0.f;
+        }
+        mhc_wave_lds_fence();  // the reads below see the other lanes' writes
+#pragma unroll
+        for (int k = 0; k < 16; ++k) pg[s][k] = tile[lane * kP + k];
+    }
+    float d[16];
+    project_bwd(pg[0], pg[1], d);
+    store_records_v4<16>(dA, first, B, tile, d, lane);
 }
 
 // Forward of one batch and backward of another in one launch: workgroups
-// below fwd_blocks run birkhoff_fwd_kernel's work, the rest the backward.
-// The two halves complement each other on the chip: the forward is bound by
-// the latency of its solve at two waves per SIMD and leaves HBM mostly idle,
-// the backward is bound by HBM and needs few issue slots, so the backward's
-// workgroups fill the SIMD slots the forward leaves free.  Forward
-// workgroups come first, so they are dispatched first and spread evenly over
-// the CUs (orders that mix backward workgroups in among them, round-robin or
-// in rounds of eight, one per XCD, left some SIMDs with more forward waves
-// and measured 25-30 % slower at 131072 matrices).  The batches are
-// independent (the ABI rejects overlaps between them), as when a trainer
-// runs micro-batch k's forward while micro-batch k-1 goes backward, or
-// recomputes one layer's projection during another layer's backward.
+// below fwd_blocks run birkhoff_fwd_kernel's work, the rest the backward
+// (bwd_block_lanes, 256 matrices per workgroup).  The two halves complement
+// each other on the chip: the forward is bound by the latency of its solve at
+// two waves per SIMD and leaves HBM mostly idle, the backward is bound by HBM,
+// so the backward's workgroups fill the SIMD slots the forward leaves free
+// (at 131072 matrices two forward and two backward waves per SIMD, all
+// resident at once).  Forward workgroups come first, so they are dispatched
+// first and spread evenly over the CUs (orders that mix backward workgroups
+// in among them, round-robin or in rounds of eight, one per XCD, left some
+// SIMDs with more forward waves and measured 25-30 % slower at 131072
+// matrices).  The batches are independent (the ABI rejects overlaps between
+// them), as when a trainer runs micro-batch k's forward while micro-batch
+// k-1 goes backward, or recomputes one layer's projection during another
+// layer's backward.  grad_logits may be grad_P itself: a wave reads all of its
+// records before it writes any.
 template <int SOLVER>
 __global__ __launch_bounds__(kBlock) void birkhoff_pipeline_kernel(
     const float* logits, float* P, uint8_t* __restrict__ iters, int64_t B, SolverOpts o,
-    const float4* __restrict__ Pb, const float4* Gb, float4* dAb, int64_t Bb,
-    unsigned fwd_blocks)
+    const float* __restrict__ Pb, const float* Gb, float* dAb, int64_t Bb, unsigned fwd_blocks)
 {
     __shared__ FwdTiles tiles;
     if (blockIdx.x < fwd_blocks)
         fwd_block<SOLVER>(logits, P, iters, B, o, tiles, blockIdx.x);
     else
-        bwd_block_rows(Pb, Gb, dAb, Bb, (int64_t)(blockIdx.x - fwd_blocks));
+        bwd_block_lanes(Pb, Gb, dAb, Bb, tiles, (int64_t)(blockIdx.x - fwd_blocks));
 }
 
 // Solve and differentiate in one pass: lane per matrix, the projection
@@ -228,17 +249,14 @@ hipError_t launch_birkhoff_pipeline(const float* logits, float* P, uint8_t* iter
                                    float* dAb, int64_t Bb, hipStream_t stream)
 {
     const int64_t fwd_blocks = (B + kBlock - 1) / kBlock;
-    const int64_t bwd_blocks = (4 * Bb + kBlock * kPipeRows - 1) / (kBlock * kPipeRows);
+    const int64_t bwd_blocks = (Bb + kBlock - 1) / kBlock;
     const dim3 grid((unsigned)(fwd_blocks + bwd_blocks));
-    const float4* P4 = reinterpret_cast<const float4*>(Pb);
-    const float4* G4 = reinterpret_cast<const float4*>(Gb);
-    float4* dA4 = reinterpret_cast<float4*>(dAb);
     if (o.solver == 0)
         hipLaunchKernelGGL(birkhoff_pipeline_kernel<0>, grid, dim3(kBlock), 0, stream, logits, P,
-                           iters, B, o, P4, G4, dA4, Bb, (unsigned)fwd_blocks);
+                           iters, B, o, Pb, Gb, dAb, Bb, (unsigned)fwd_blocks);
     else
         hipLaunchKernelGGL(birkhoff_pipeline_kernel<1>, grid, dim3(kBlock), 0, stream, logits, P,
-                           iters, B, o, P4, G4, dA4, Bb, (unsigned)fwd_blocks);
+                           iters, B, o, Pb, Gb, dAb, Bb, (unsigned)fwd_blocks);
     return hipGetLastError();
 }
 

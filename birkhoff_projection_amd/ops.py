@@ -104,10 +104,12 @@ def birkhoff_pipeline_step(logits: torch.Tensor, P_bwd: torch.Tensor, grad_P: to
                            out_grad=None, return_iters=False):
     """The forward of one batch and the backward of another, independent one
     in a single launch: P = projection(logits) and dL/dlogits of the other
-    batch from its P_bwd and dL/dP.  Bit for bit the results of birkhoff_fwd
-    and birkhoff_bwd; both batches are [..., 4, 4] fp32 on one device, and
-    either may be empty.  Returns (P, grad) (and the forward's iteration codes
-    if ``return_iters``)."""
+    batch from its P_bwd and dL/dP.  P is bit for bit birkhoff_fwd's; the
+    gradient is birkhoff_bwd_recompute's arithmetic (bit for bit when P_bwd
+    is the forward's P of those logits) and birkhoff_bwd's up to fp32
+    rounding.  Both batches are [..., 4, 4] fp32 on one device, either may be
+    empty, out may be logits and out_grad grad_P.  Returns (P, grad) (and the
+    forward's iteration codes if ``return_iters``)."""
     _need(logits, "logits", torch.float32, (4, 4))
     _need(P_bwd, "P_bwd", torch.float32, (4, 4))
     _need(grad_P, "grad_P", torch.float32, (4, 4))

@@ -221,11 +221,15 @@ mhc_status mhc_birkhoff_fwd_bwd(const float* logits, const float* grad_P, float*
  * micro-batches, or recompute one layer's projection during another layer's
  * backward instead of keeping it (neo-ai mHC paper summary, systems section:
  * recomputation of the mHC intermediates and the extended DualPipe
- * schedule).  The results are bit for bit those of mhc_birkhoff_fwd on
- * (logits, P, B) and mhc_birkhoff_bwd on (P_bwd, grad_P, grad_logits, B_bwd);
- * what changes is that both run at once.  The forward solve is bound by its
- * own latency and leaves HBM mostly idle, the backward is bound by HBM, so
- * the pair takes about as long as the forward alone where two launches in
+ * schedule).  P is bit for bit mhc_birkhoff_fwd's on (logits, B).  The
+ * gradient is formed one matrix per lane, the arithmetic of
+ * mhc_birkhoff_bwd_recompute and mhc_birkhoff_fwd_bwd: bit for bit what those
+ * give when P_bwd is the forward's P of their logits, and equal to
+ * mhc_birkhoff_bwd's on (P_bwd, grad_P) up to fp32 rounding (the same
+ * implicit-differentiation formula, gist.science summary section 2.2,
+ * evaluated in another order).  The forward solve is bound by its own
+ * latency and leaves HBM mostly idle, the backward is bound by HBM, so the
+ * pair takes about as long as the forward alone where two launches in
  * sequence take the sum.
  *
  *   logits, P, B, opts, iters
