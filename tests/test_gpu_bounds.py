@@ -50,6 +50,14 @@ def test_projection_4x4_writes_only_its_batch(gpu_lib, B):
     gpu_lib.birkhoff_fwd_bwd(A, G, out_P=headP, out_grad=headD)
     _check(fullP, B, "fused fwd+bwd P")
     _check(fullD, B, "fused fwd+bwd dA")
+    # pipeline step: the forward and the backward batch of different sizes
+    Bo = B + 37
+    Ao = torch.from_numpy(W.logits_batch("normal10", Bo, 900 + B)).cuda()
+    fullP, headP = _out(Bo, (4, 4))
+    fullD, headD = _out(B, (4, 4))
+    gpu_lib.birkhoff_pipeline_step(Ao, P, G, out=headP, out_grad=headD)
+    _check(fullP, Bo, "pipeline P")
+    _check(fullD, B, "pipeline dA")
 
 
 @pytest.mark.parametrize("n", [2, 3, 5, 8])

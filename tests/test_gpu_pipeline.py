@@ -103,3 +103,21 @@ def test_pipeline_binding_checks(gpu_lib):
         bp.birkhoff_pipeline_step(A, Pb, G, out_grad=buf[:99])
     torch.cuda.synchronize()
     assert bool((buf == 7.0).all())
+
+
+def test_pipeline_sinkhorn_solver(gpu_lib):
+    """The Sinkhorn instantiation: P bit for bit birkhoff_fwd's with the same
+    options (converged and fixed-count), the gradient the recompute
+    backward's for the same logits and options."""
+    bp = gpu_lib
+    Bf, Bb = 1500, 2100
+    A, _ = _batch("normal1", Bf, 104)
+    Ab, Gb = _batch("normal1", Bb, 106)
+    for opts in (dict(solver="sinkhorn"), dict(solver="sinkhorn", max_iters=20, tol=0.0)):
+        Pb = bp.birkhoff_fwd(Ab, **opts)
+        P, dA, it = bp.birkhoff_pipeline_step(A, Pb, Gb, return_iters=True, **opts)
+        P_ref, it_ref = bp.birkhoff_fwd(A, return_iters=True, **opts)
+        dA_ref = bp.birkhoff_bwd_recompute(Ab, Gb, **opts)
+        torch.cuda.synchronize()
+        assert torch.equal(P, P_ref) and torch.equal(it, it_ref), opts
+        assert torch.equal(dA, dA_ref), opts
