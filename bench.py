@@ -88,18 +88,18 @@ KERNEL_SOURCES = {
     "layer": ("devmath.h", "proj4.h", "wave.h", "kernels.h", "layer.hip"),
 }
 MEASURED = {
-    "birkhoff_fwd_131072_cfg2": {"fetch": 8518722, "write": 8388960, "valu": 2428524, "trans": 122685, "sha": "58a2d67da8cf823d"},
-    "birkhoff_bwd_131072_cfg2": {"fetch": 16805804, "write": 8389276, "valu": 1122304, "trans": 24576, "sha": "58a2d67da8cf823d"},
-    "birkhoff_pipeline_131072_cfg2": {"fetch": 25356068, "write": 16778588, "valu": 3122779, "trans": 128829, "sha": "58a2d67da8cf823d"},
-    "birkhoff_fwd_1048576_cfg3": {"fetch": 67239969, "write": 67114048, "valu": 18806279, "trans": 946129, "sha": "58a2d67da8cf823d"},
-    "birkhoff_bwd_1048576_cfg3": {"fetch": 134231380, "write": 67110362, "valu": 8978432, "trans": 196608, "sha": "58a2d67da8cf823d"},
-    "birkhoff_pipeline_1048576_cfg3": {"fetch": 201500095, "write": 134222483, "valu": 24360317, "trans": 995281, "sha": "58a2d67da8cf823d"},
-    "birkhoff_fwd_bwd_131072_cfg2": {"fetch": 16966821, "write": 16777298, "valu": 2977371, "trans": 128829, "sha": "58a2d67da8cf823d"},
-    "birkhoff_fwd_n8_131072_cfg2": {"fetch": 40957318, "write": 59770885, "valu": 22793495, "trans": 745229, "sha": "717dd4767b586ebf"},
-    "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67434293, "write": 33555422, "valu": 6424576, "trans": 14336, "sha": "717dd4767b586ebf"},
-    "stream_mix_fwd_16384x4x4096": {"fetch": 537992431, "write": 537928853, "valu": 25666560, "trans": 64512, "sha": "1908a484b992311d"},
-    "stream_mix_bwd_16384x4x4096": {"fetch": 1074725377, "write": 537953419, "valu": 49479680, "trans": 0, "sha": "1908a484b992311d"},
-    "layer_step_65536x4x7168": {"fetch": 30735264244, "write": 9469201958, "mfma": {"layer_maps_kernel<0>": 7340032, "layer_dx_kernel": 14680064, "layer_dw_kernel": 14680064}, "us": {"layer_maps_kernel<0>": 667.08, "layer_dx_kernel": 2583.56, "layer_dw_kernel": 749.28}, "sha": "53e5ab677c7bb8e1"},
+    "birkhoff_fwd_131072_cfg2": {"fetch": 8518735, "write": 8388960, "valu": 2428524, "trans": 122685, "sha": "c922610c3f315bf8"},
+    "birkhoff_bwd_131072_cfg2": {"fetch": 16805810, "write": 8388711, "valu": 1122304, "trans": 24576, "sha": "c922610c3f315bf8"},
+    "birkhoff_pipeline_131072_cfg2": {"fetch": 25356075, "write": 16800537, "valu": 3122779, "trans": 128829, "sha": "c922610c3f315bf8"},
+    "birkhoff_fwd_1048576_cfg3": {"fetch": 67239853, "write": 67117052, "valu": 18806279, "trans": 946129, "sha": "c922610c3f315bf8"},
+    "birkhoff_bwd_1048576_cfg3": {"fetch": 134231118, "write": 67109085, "valu": 8978432, "trans": 196608, "sha": "c922610c3f315bf8"},
+    "birkhoff_pipeline_1048576_cfg3": {"fetch": 201499584, "write": 134224492, "valu": 24360317, "trans": 995281, "sha": "c922610c3f315bf8"},
+    "birkhoff_fwd_bwd_131072_cfg2": {"fetch": 16966832, "write": 16777276, "valu": 2977371, "trans": 128829, "sha": "c922610c3f315bf8"},
+    "birkhoff_fwd_n8_131072_cfg2": {"fetch": 40897258, "write": 59769985, "valu": 22793495, "trans": 745229, "sha": "c81fc94510d4dee0"},
+    "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67434096, "write": 33555018, "valu": 6424576, "trans": 14336, "sha": "c81fc94510d4dee0"},
+    "stream_mix_fwd_16384x4x4096": {"fetch": 537993114, "write": 537927744, "valu": 25666560, "trans": 64512, "sha": "1908a484b992311d"},
+    "stream_mix_bwd_16384x4x4096": {"fetch": 1074727811, "write": 537951093, "valu": 49479680, "trans": 0, "sha": "1908a484b992311d"},
+    "layer_step_65536x4x7168": {"fetch": 30712082712, "write": 9469206752, "mfma": {"layer_maps_kernel<0>": 7340032, "layer_dx_kernel": 14680064, "layer_dw_kernel": 14680064}, "us": {"layer_maps_kernel<0>": 667.18, "layer_dx_kernel": 2578.94, "layer_dw_kernel": 752.88}, "sha": "53e5ab677c7bb8e1"},
 }
 
 

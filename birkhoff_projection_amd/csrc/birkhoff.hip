@@ -102,45 +102,14 @@ MHC_DEV void bwd_block_lanes(const float* P, const float* G, float* dA, int64_t 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int64_t first = block * kBlock + 64 * w;
     if (first >= B) return;  // the whole wave is past the batch
-    constexpr int kP = record_pitch<16>();
-    const int64_t have = B - first;
-    const int64_t last = 4 * B - 1;  // last float4 of the batch
-    const float4* P4 = reinterpret_cast<const float4*>(P);
-    const float4* G4 = reinterpret_cast<const float4*>(G);
-    float4 v[2][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t idx = 4 * first + lane + 64 * i;
-        v[0][i] = mhc_load_stream(P4 + (idx < last ? idx : last));
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t idx = 4 * first + lane + 64 * i;
-        v[1][i] = mhc_load_stream(G4 + (idx < last ? idx : last));
-    }
-    float* tile = tiles[w];
-    float pg[2][16];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        mhc_wave_lds_fence();  // earlier reads of the tile come first
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = 4 * (lane + 64 * i);  // float index in the wave's 64 records
-            const int rec = e / 16, col = e % 16;
-            const bool in = rec < have;
-            float* t = tile + rec * kP + col;
-            t[0] = in ? v[s][i].x : 0.f;
-            t[1] = in ? v[s][i].y : 0.f;
-            t[2] = in ? v[s][i].z : 0.f;
-            t[3] = in ? v[s][i].w : 0.f;
-        }
-        mhc_wave_lds_fence();  // the reads below see the other lanes' writes
-#pragma unroll
-        for (int k = 0; k < 16; ++k) pg[s][k] = tile[lane * kP + k];
-    }
-    float d[16];
-    project_bwd(pg[0], pg[1], d);
-    store_records_v4<16>(dA, first, B, tile, d, lane);
+    float4 vp[4], vg[4];
+    issue_records_v4<16>(P, first, B, vp, lane);
+    issue_records_v4<16>(G, first, B, vg, lane);
+    float p[16], g[16], d[16];
+    scatter_records_v4<16>(vp, first, B, tiles[w], p, lane);
+    scatter_records_v4<16>(vg, first, B, tiles[w], g, lane);
+    project_bwd(p, g, d);
+    store_records_v4<16>(dA, first, B, tiles[w], d, lane);
 }
 
 // Forward of one batch and backward of another in one launch: workgroups

@@ -87,23 +87,33 @@ MHC_DEV void store_records(float* __restrict__ g, int64_t first, int64_t B, floa
     }
 }
 
-// 16-byte elements: R a multiple of 4 and a 16-byte aligned base.
+// 16-byte elements: R a multiple of 4 and a 16-byte aligned base.  The load
+// is split in two so that a caller can issue the loads of several record
+// sets before it moves any of them through the tile: issue_records_v4 starts
+// the wave's R/4 float4 loads (clamped past the batch), scatter_records_v4
+// moves them through the tile to one record per lane (zeros past B).
 template <int R>
-MHC_DEV void load_records_v4(const float* __restrict__ g, int64_t first, int64_t B, float* tile,
-                             float* out, int lane)
+MHC_DEV void issue_records_v4(const float* __restrict__ g, int64_t first, int64_t B,
+                              float4 (&v)[R / 4], int lane)
 {
     static_assert(R % 4 == 0, "records of whole float4s");
-    constexpr int kP = record_pitch<R>();
     constexpr int kQ = R / 4;  // float4 loads per lane
-    const int64_t have = B - first;
     const float4* g4 = reinterpret_cast<const float4*>(g);
     const int64_t last = kQ * B - 1;
-    float4 v[kQ];
 #pragma unroll
     for (int i = 0; i < kQ; ++i) {
         const int64_t idx = kQ * first + lane + 64 * i;
         v[i] = mhc_load_stream(g4 + (idx < last ? idx : last));
     }
+}
+
+template <int R>
+MHC_DEV void scatter_records_v4(const float4 (&v)[R / 4], int64_t first, int64_t B, float* tile,
+                                float* out, int lane)
+{
+    constexpr int kP = record_pitch<R>();
+    constexpr int kQ = R / 4;
+    const int64_t have = B - first;
     mhc_wave_lds_fence();
 #pragma unroll
     for (int i = 0; i < kQ; ++i) {
@@ -119,6 +129,15 @@ MHC_DEV void load_records_v4(const float* __restrict__ g, int64_t first, int64_t
     mhc_wave_lds_fence();
 #pragma unroll
     for (int k = 0; k < R; ++k) out[k] = tile[lane * kP + k];
+}
+
+template <int R>
+MHC_DEV void load_records_v4(const float* __restrict__ g, int64_t first, int64_t B, float* tile,
+                             float* out, int lane)
+{
+    float4 v[R / 4];
+    issue_records_v4<R>(g, first, B, v, lane);
+    scatter_records_v4<R>(v, first, B, tile, out, lane);
 }
 
 template <int R>
