@@ -23,10 +23,14 @@ project takes where they are silent:
   the widened stream is projected down before F and expanded after).
 
 Backward for upstream (dx_out, du), by the chain rule in float64, with the
-projection's gradient from oracle.birkhoff.birkhoff_project_bwd.  Pinned by
-central finite differences of a scalar loss on tiny shapes
-(tests/test_oracle_mix_layer.py); beyond that composition the full-size layer is
-parity unpinned except through its pinned parts.
+projection's gradient from oracle.birkhoff.birkhoff_project_bwd.
+
+Pins (tests/test_oracle_mix_layer.py): the forward by closed forms on one-hot
+maps W (logit m = x_k / r, sigmoid maps, and the projection of a matrix with
+one nonzero entry, solved by symmetry), by the scale invariance of the
+normalised logits, and u / x_out by explicit loops; the backward by central
+finite differences of a scalar loss and by torch float64 autograd through
+unrolled Sinkhorn sweeps.
 """
 from __future__ import annotations
 

@@ -118,6 +118,75 @@ def test_layer_identity_residual_limit():
     np.testing.assert_allclose(out["u"], 0.5 * x.sum(axis=1), atol=1e-13)
 
 
+def test_layer_logits_scale_invariant():
+    """With eps = 0 the RMS-normalised stream, hence every logit and map, is
+    unchanged when x is scaled; u scales with x.  A logit formed from the raw
+    stream, or normalised over one stream instead of all n C values, fails
+    this."""
+    x, W, f, _, _ = _layer_case(seed=12)
+    a = layer_fwd(x, W, f, eps=0.0)
+    b = layer_fwd(3.0 * x, W, f, eps=0.0)
+    for k in ("logits", "H_pre", "H_post", "H_res"):
+        np.testing.assert_allclose(b[k], a[k], rtol=1e-13, atol=1e-14, err_msg=k)
+    np.testing.assert_allclose(b["u"], 3.0 * a["u"], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(b["rms"], 3.0 * a["rms"], rtol=1e-14)
+
+
+def _one_hot_res(a):
+    """Projection of the 4 x 4 logit matrix with the single nonzero entry a at
+    (i, j): swapping any two other rows or columns leaves the kernel
+    exp(L) unchanged, so P is p at (i, j), (1 - p)/3 elsewhere in row i and
+    column j, and (2 + p)/9 everywhere else, and the scaling condition
+    P_ij P_kl / (P_il P_kj) = e^a for k != i, l != j gives
+    p (2 + p) = e^a (1 - p)^2, solved here for the root in (0, 1)."""
+    e = np.exp(a)
+    qa, qb, qc = 1.0 - e, 2.0 + 2.0 * e, -e
+    with np.errstate(divide="ignore", invalid="ignore"):
+        root = (-qb + np.sqrt(qb * qb - 4.0 * qa * qc)) / (2.0 * qa)
+    return np.where(np.abs(qa) < 1e-12, 0.25, root)
+
+
+@pytest.mark.parametrize("m", [0, 5, 8, 8 + 4 * 1 + 2, 8 + 4 * 3 + 0])
+def test_layer_one_hot_map(m):
+    """W with a single 1 at row m, column k: logit m is x_flat[k] / r and every
+    other logit 0.  So H_pre and H_post are 1/2 except sigmoid(x_k / r) at
+    entry m (pre rows 0:4, post rows 4:8), and for a residual row
+    m = 8 + 4 i + j, H_res is the closed-form projection of a matrix with one
+    nonzero entry at (i, j).  Catches a transposed W, a misplaced block or a
+    misordered residual matrix."""
+    x, _, f, _, _ = _layer_case(T=6, C=5, seed=13)
+    T, n, C = x.shape
+    k = 7
+    W = np.zeros((n * n + 2 * n, n * C))
+    W[m, k] = 1.0
+    out = layer_fwd(x, W, f)
+    xf = x.reshape(T, -1)
+    lm = xf[:, k] / out["rms"]
+    expect = np.zeros((T, n * n + 2 * n))
+    expect[:, m] = lm
+    np.testing.assert_allclose(out["logits"], expect, atol=1e-15, rtol=1e-14)
+    sig = 1.0 / (1.0 + np.exp(-lm))
+    pre = np.full((T, n), 0.5)
+    post = np.full((T, n), 0.5)
+    if m < n:
+        pre[:, m] = sig
+    elif m < 2 * n:
+        post[:, m - n] = sig
+    np.testing.assert_allclose(out["H_pre"], pre, atol=1e-15)
+    np.testing.assert_allclose(out["H_post"], post, atol=1e-15)
+    if m >= 2 * n:
+        i, j = divmod(m - 2 * n, n)
+        p = _one_hot_res(lm)
+        H = np.empty((T, n, n))
+        H[:] = ((2.0 + p) / 9.0)[:, None, None]
+        H[:, i, :] = ((1.0 - p) / 3.0)[:, None]
+        H[:, :, j] = ((1.0 - p) / 3.0)[:, None]
+        H[:, i, j] = p
+        np.testing.assert_allclose(out["H_res"], H, atol=1e-12)
+    else:
+        np.testing.assert_allclose(out["H_res"], 0.25, atol=1e-14)
+
+
 def _loss(x, W, f, dx_out, du):
     out = layer_fwd(x, W, f)
     return (out["x_out"] * dx_out).sum() + (out["u"] * du).sum()
