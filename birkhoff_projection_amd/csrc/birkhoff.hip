@@ -29,7 +29,7 @@ template <int SOLVER>
 MHC_DEV void fwd_block(const float* logits, float* P, uint8_t* __restrict__ iters, int64_t B,
                        const SolverOpts& o, FwdTiles& tiles, int64_t block)
 {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, w = wave_index();
     const int64_t first = block * kBlock + 64 * w;
     if (first >= B) return;  // the whole wave is past the batch
     float a[16];
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(kBlock) void birkhoff_bwd_kernel(const float4* __re
 MHC_DEV void bwd_block_lanes(const float* P, const float* G, float* dA, int64_t B,
                              FwdTiles& tiles, int64_t block)
 {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, w = wave_index();
     const int64_t first = block * kBlock + 64 * w;
     if (first >= B) return;  // the whole wave is past the batch
     float4 vp[4], vg[4];
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(kBlock) void birkhoff_solve_bwd_kernel(const float*
     // the start's row reads (the same start as birkhoff_fwd_kernel's)
     __shared__ float tiles[kBlock / 64][stage_tile_floats<16>()];
     __shared__ float gtiles[kBlock / 64][stage_tile_floats<16>()];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, w = wave_index();
     const int64_t first = (int64_t)blockIdx.x * kBlock + 64 * w;
     if (first >= B) return;
     float a[16], g[16], p[16], d[16];

@@ -48,6 +48,7 @@ constexpr float kMaxStep = 8.f;
 // sum of four row-softmax entries) a trial is judged by the residual alone,
 // and one that does not lower it marks the noise floor and ends the solve.
 constexpr float kNoiseFloor = 4e-6f;
+constexpr float kNoiseFloor2 = kNoiseFloor * kLog2e;  // the same in Eval::res units
 // Curvature test of the line search: accept a trial whose directional
 // derivative is at most this fraction of the initial one's magnitude.
 constexpr float kCurvature = 0.9f;
@@ -91,20 +92,25 @@ struct SolverOpts {
 struct Eval {
     float P[16];
     float c[4];
-    float b[4];  // 1 - c_j
-    float res;   // max_j |c_j - 1|
+    float b[4];  // (1 - c_j) log2 e
+    float res;   // max_j |b_j| = max_j |c_j - 1| log2 e
 };
 
-// Column sums of E.P, their defects b_j = 1 - c_j and the residual
-// max_j |b_j|.  Contraction is off so that the sums add the stored entries
-// (which the Hessian weights use too) instead of re-multiplying them.
+// Column sums of E.P, their defects and the residual.  The defects are kept
+// in the base-2 units of the potentials, b_j = (1 - c_j) log2 e (one fused
+// multiply-add, a single rounding), so that the Newton system solved with
+// them gives the base-2 direction directly; the residual is in the same
+// units, and every tolerance it is compared with is scaled by log2 e
+// (kLog2e * o.tol, kNoiseFloor2).  Contraction is off so that the sums add
+// the stored entries (which the Hessian weights use too) instead of
+// re-multiplying them.
 MHC_DEV void column_sums(Eval& E)
 {
 #pragma clang fp contract(off)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         E.c[j] = (E.P[j] + E.P[4 + j]) + (E.P[8 + j] + E.P[12 + j]);
-        E.b[j] = 1.f - E.c[j];
+        E.b[j] = __builtin_fmaf(-kLog2e, E.c[j], kLog2e);
     }
     E.res = mhc_max(mhc_max(mhc_abs(E.b[0]), mhc_abs(E.b[1])),
                     mhc_max(mhc_abs(E.b[2]), mhc_abs(E.b[3])));
@@ -249,8 +255,8 @@ MHC_DEV float ridge(const Weights& w)
     return __builtin_fmaf(8.f * kFltEps, tr, 1e-30f);
 }
 
-// Ridge of the forward's Newton solve: the relative ridge plus an absolute
-// one of kDirRidge.  A computed column residual carries rounding noise of a
+// Ridge of the forward's Newton solve: a constant kDirRidge on the degree of
+// every free vertex.  A computed column residual carries rounding noise of a
 // couple of ulps of 1, so along a direction whose curvature is below that
 // (a column tied to the others only by weights of 1e-12, as near a
 // permutation matrix) the plain solve turns noise into steps of hundreds of
@@ -258,13 +264,11 @@ MHC_DEV float ridge(const Weights& w)
 // useful part of the direction with it, to a few percent.  With the floor such
 // a direction moves about noise / kDirRidge, under a unit.  Directions with
 // curvature well above it are unchanged, so the final quadratic convergence
-// is kept.  (The backward solves the exact system and keeps ridge().)
+// is kept.  The relative part of ridge() (8 eps times the trace, at most
+// about 6e-6 here) changed no iteration count on the benchmark batches and
+// costs six instructions per direction, so the forward does without it.
+// (The backward solves the exact system and keeps ridge().)
 constexpr float kDirRidge = 2.f * kFltEps;
-MHC_DEV float newton_ridge(const Weights& w)
-{
-    const float tr = 2.f * (w.w01 + w.w02 + w.w12) + (w.w03 + w.w13 + w.w23);
-    return __builtin_fmaf(8.f * kFltEps, tr, kDirRidge);
-}
 
 // Iteration counter encoding for the optional per-matrix output.
 constexpr uint32_t kNotConverged = 255u;
@@ -299,7 +303,7 @@ MHC_DEV void sink_store(float* sink, const float* P)
 //            Newton step ends the solve.  A rejected trial halves t.  Every
 //            trial reaching the tolerance is accepted.
 // The Newton direction solves the Laplacian system of the Hessian with a
-// ridge (newton_ridge, Kron reduction); its first trial step is capped at
+// ridge (kDirRidge, Kron reduction); its first trial step is capped at
 // kMaxStep.
 struct NewtonLane {
     float a[16];         // base-2 logits, rows shifted to max 0
@@ -311,30 +315,34 @@ struct NewtonLane {
     float t, res, slope; // step length, residual, psi'(0) along d
     float grow;          // first-trial multiple of the Newton step (>= 1)
     int newton, trials;  // Newton directions taken, halvings this step
-    uint32_t code;       // result when done
+    bool failed;         // stopped without converging (iteration code 255)
     bool done;
     bool stored;         // P already written to the lane's LDS sink
 };
 
-// Newton direction at E (natural-units solve, returned in base-2 units),
-// slope psi'(0) along it, and the longest first step kMaxStep / max|d|.
+// Newton direction at E in base-2 units (the Laplacian solve with the
+// defects already in those units, Eval::b), the slope psi'(0) along it (in
+// the same scaled units as Eval::res), and the longest first step
+// kMaxStep / max|d|.
 MHC_DEV void newton_direction(const Eval& E, float& d0, float& d1, float& d2, float& slope,
                               float& tcap)
 {
     const Weights w = laplacian_weights(E.P);
-    const float lam = newton_ridge(w);
-    float n0, n1, n2;
-    laplacian_solve(w.w01, w.w02, w.w03, w.w12, w.w13, w.w23, lam, E.b[0], E.b[1], E.b[2], n0,
-                    n1, n2);
-    d0 = n0 * kLog2e;
-    d1 = n1 * kLog2e;
-    d2 = n2 * kLog2e;
+    laplacian_solve(w.w01, w.w02, w.w03, w.w12, w.w13, w.w23, kDirRidge, E.b[0], E.b[1], E.b[2], d0,
+                    d1, d2);
     slope = -(E.b[0] * d0 + E.b[1] * d1 + E.b[2] * d2);
     const float dmax = mhc_max(mhc_max(mhc_abs(d0), mhc_abs(d1)), mhc_abs(d2));
     tcap = kMaxStep * mhc_rcp(dmax);
 }
 
 MHC_DEV void newton_take(NewtonLane& s, const Eval& E) { s.res = E.res; }
+
+// Iteration code of a finished lane: the Newton directions it took before
+// converging (0 at the start), or kNotConverged.
+MHC_DEV uint32_t newton_code(const NewtonLane& s)
+{
+    return s.failed ? kNotConverged : iters_code(s.newton);
+}
 
 // Starting potentials from the assignment problem.  A doubly stochastic
 // matrix is a convex combination of permutation matrices (neo-ai news
@@ -354,7 +362,9 @@ MHC_DEV void newton_take(NewtonLane& s, const Eval& E) { s.res = E.res; }
 // The permutation is found by brute force: rows 2 and 3 take the better
 // orientation of each of the 6 column pairs, rows 0 and 1 each of the 12
 // ordered pairs of the other two columns.  Shortest paths have at most 3
-// edges, so two rounds of Bellman-Ford after the direct edges are exact.
+// edges; one round of Bellman-Ford after the direct edges finds those of up
+// to 2, and a second round (exact) changed no iteration count on N(0,10^2)
+// or mixed batches once the balancing sweeps follow, so it is left out.
 // The search works in the base-2 units of a.  The exchange lengths take the
 // owner rows either from a by select chains (ROWS_IN_LDS false) or, when the
 // caller still holds the lane's raw logits in LDS (rec: 16 floats,
@@ -371,16 +381,26 @@ MHC_DEV void assignment_start(const float* a, const float* rec, float& g0, float
     constexpr int pk[6] = {0, 0, 0, 1, 1, 2};
     constexpr int pl[6] = {1, 2, 3, 2, 3, 3};
     float m23[6];
-    int r2col[6];  // column of row 2 in the better orientation of pair p
+    uint32_t r2bits = 0;  // 2 bits per pair p: column of row 2 in its better orientation
 #pragma unroll
     for (int p = 0; p < 6; ++p) {
         const float v1 = a[8 + pk[p]] + a[12 + pl[p]];
         const float v2 = a[8 + pl[p]] + a[12 + pk[p]];
         m23[p] = mhc_max(v1, v2);
-        r2col[p] = v2 > v1 ? pl[p] : pk[p];
+        r2bits |= (v2 > v1 ? (uint32_t)pl[p] : (uint32_t)pk[p]) << (2 * p);
     }
+    // The 12 ordered pairs (j0, j1) of rows 0 and 1, numbered q in loop
+    // order.  Each candidate sum carries q in its 4 lowest mantissa bits, so
+    // one max over the tagged sums gives the best one and its number
+    // (candidates within 2^-19 of each other, relatively, are not told
+    // apart; either is a valid start).  A -inf sum turns into a NaN, which
+    // the max skips.  kJ0 and kJ1 hold j0 and j1 of each q (2 bits each), kPq
+    // the leftover pair p (3 bits each); q is clamped to the table in case
+    // every candidate was skipped.
+    constexpr uint32_t kJ0 = 0xfea540u, kJ1 = 0x934e39u;
+    constexpr uint64_t kPq = 0x5850aae5ull;  // 36 bits (the top entry is 0)
     float best = -__builtin_inff();
-    int c0 = 0, c1 = 1, c2 = 2;  // columns of rows 0, 1, 2 (identity if no value compares)
+    int q = 0;
 #pragma unroll
     for (int j0 = 0; j0 < 4; ++j0) {
 #pragma unroll
@@ -390,13 +410,15 @@ MHC_DEV void assignment_start(const float* a, const float* rec, float& g0, float
             const int hi = (j0 != 3 && j1 != 3) ? 3 : ((j0 != 2 && j1 != 2) ? 2 : 1);
             const int p = lo == 0 ? hi - 1 : (lo == 1 ? hi + 1 : 5);
             const float v = a[j0] + a[4 + j1] + m23[p];
-            const bool take = v > best;
-            best = mhc_max(best, v);
-            c0 = take ? j0 : c0;
-            c1 = take ? j1 : c1;
-            c2 = take ? r2col[p] : c2;
+            best = mhc_max(best, __uint_as_float((__float_as_uint(v) & ~15u) | (uint32_t)q));
+            ++q;
         }
     }
+    const uint32_t qb = __float_as_uint(best) & 15u;
+    const uint32_t qi = qb < 11u ? qb : 11u;
+    const int c0 = (int)((kJ0 >> (2 * qi)) & 3u);  // columns of rows 0, 1, 2
+    const int c1 = (int)((kJ1 >> (2 * qi)) & 3u);
+    const int c2 = (int)((r2bits >> (2 * (uint32_t)((kPq >> (3 * qi)) & 7u))) & 3u);
     // w[c][j]: length of the edge c -> j (row owning column c moves to j)
     float w[4][4];
     if constexpr (ROWS_IN_LDS) {
@@ -433,7 +455,7 @@ MHC_DEV void assignment_start(const float* a, const float* rec, float& g0, float
         from[j] = w[j][3];
     }
 #pragma unroll
-    for (int round = 0; round < 2; ++round) {
+    for (int round = 0; round < 1; ++round) {
 #pragma unroll
         for (int j = 0; j < 3; ++j) {
 #pragma unroll
@@ -499,8 +521,9 @@ MHC_DEV void newton_init(NewtonLane& s, const float* a_nat, const float* rec, co
     Eval E;
     evaluate(s.a, s.k, s.kfast, s.g0, s.g1, s.g2, E);
     newton_take(s, E);
-    s.done = s.res <= o.tol;
-    s.code = 0;
+    const float tol2 = kLog2e * o.tol;
+    s.done = s.res <= tol2;
+    s.failed = false;
     const int warm = o.warm_sweeps < 0 ? 0 : o.warm_sweeps;  // -1: none after this start
     for (int w = 0; w < warm; ++w) {
         const float l3 = mhc_log2(mhc_max(E.c[3], kMinMass));
@@ -515,7 +538,7 @@ MHC_DEV void newton_init(NewtonLane& s, const float* a_nat, const float* rec, co
             s.g2 = n2;
             newton_take(s, F);
             E = F;
-            s.done = s.res <= o.tol;
+            s.done = s.res <= tol2;
         }
     }
     float tcap = 0.f;
@@ -523,13 +546,13 @@ MHC_DEV void newton_init(NewtonLane& s, const float* a_nat, const float* rec, co
     if (!SINK || wave_any(!s.done)) newton_direction(E, s.d0, s.d1, s.d2, s.slope, tcap);
     s.grow = 1.f;
     s.t = mhc_min(1.f, tcap);
+    s.newton = s.done ? 0 : 1;  // a lane converged at the start reports 0
     if (!s.done && o.max_iters < 1) {
         s.done = true;
-        s.code = kNotConverged;
+        s.failed = true;
     }
-    s.newton = 1;
     s.stored = false;
-    if (SINK && s.done && s.code == 0) {
+    if (SINK && s.done && !s.failed) {
         sink_store(sink, E.P);
         s.stored = true;
     }
@@ -556,24 +579,29 @@ MHC_DEV void newton_step(NewtonLane& s, const SolverOpts& o, float* sink)
 
     const float dphi = -(E.b[0] * s.d0 + E.b[1] * s.d1 + E.b[2] * s.d2);
     // (bitwise & and | on bools: no short-circuit branches)
-    const bool near_floor = s.res <= kNoiseFloor;
+    const bool near_floor = s.res <= kNoiseFloor2;
     const bool lower = E.res < s.res;
     const bool curved = dphi <= kCurvature * mhc_abs(s.slope);
-    const bool conv_t = E.res <= o.tol;
+    const bool conv_t = E.res <= kLog2e * o.tol;
     // On the max-shifted path (lanes whose logits span more than ~87 natural
     // units, where the potentials reach the hundreds) two fp32 stalls are
     // cut short; the factored loop, all ordinary inputs, skips both tests.
     // A trial that takes the residual from above the noise floor into it is
     // judged by the residual (the directional derivative is quantised there
     // and can read as an overshoot).
-    const bool to_floor = !FACTORED && (E.res <= kNoiseFloor);
-    const bool pass = conv_t | ((near_floor | to_floor) & lower) | (!near_floor & curved);
+    const bool to_floor = !FACTORED && (E.res <= kNoiseFloor2);
+    // (above_floor is its own comparison rather than !near_floor, so that
+    // the test stays a combination of lane masks instead of a per-lane
+    // select, which costs five vector instructions)
+    const bool above_floor = s.res > kNoiseFloor2;
+    const bool pass = conv_t | ((near_floor | to_floor) & lower) | (above_floor & curved);
     const bool accept = ok & pass;
     const bool reject = ok & !pass;
     // next first trial: doubled after a full first trial that at least
     // halved the residual and stayed far from the line minimum; the Newton
-    // step otherwise
-    const bool first = (s.trials == 0) & (s.t >= s.grow) & (E.res < kGrowProgress * s.res);
+    // step otherwise.  (A first trial has t = min(grow, cap) <= grow and a
+    // rejection halves t, so t >= grow holds only on an uncapped first trial.)
+    const bool first = (s.t >= s.grow) & (E.res < kGrowProgress * s.res);
     const bool far = first & (dphi <= kFar * s.slope);
     const float grow = mhc_pin(far ? mhc_min(2.f * s.grow, kMaxGrow) : 1.f);
     const bool conv = accept & conv_t;
@@ -589,8 +617,18 @@ MHC_DEV void newton_step(NewtonLane& s, const SolverOpts& o, float* sink)
     const bool stuck = (reject & ((near_floor & (s.t <= 1.f)) | (trials > 30))) | (ok & still);
     const bool done = s.done | conv | maxed | stuck;
 
-    float nd0 = 0.f, nd1 = 0.f, nd2 = 0.f, nslope = 0.f, ncap = 0.f;
-    if (wave_any(accept & !done)) newton_direction(E, nd0, nd1, nd2, nslope, ncap);
+    // The direction, its slope and the next trial length change only here:
+    // a lane that accepts while no lane of its wave goes on is done, and
+    // its direction is never read again.
+    if (wave_any(accept & !done)) {
+        float nd0, nd1, nd2, nslope, ncap;
+        newton_direction(E, nd0, nd1, nd2, nslope, ncap);
+        s.d0 = accept ? nd0 : s.d0;
+        s.d1 = accept ? nd1 : s.d1;
+        s.d2 = accept ? nd2 : s.d2;
+        s.slope = accept ? nslope : s.slope;
+        s.t = accept ? mhc_min(grow, ncap) : s.t;
+    }
     if (SINK && conv) {
         sink_store(sink, E.P);
         s.stored = true;
@@ -600,15 +638,11 @@ MHC_DEV void newton_step(NewtonLane& s, const SolverOpts& o, float* sink)
     s.g1 = accept ? t1 : s.g1;
     s.g2 = accept ? t2 : s.g2;
     s.res = accept ? E.res : s.res;
-    s.d0 = accept ? nd0 : s.d0;
-    s.d1 = accept ? nd1 : s.d1;
-    s.d2 = accept ? nd2 : s.d2;
-    s.slope = accept ? nslope : s.slope;
     s.grow = accept ? grow : s.grow;
-    s.t = accept ? mhc_min(grow, ncap) : (reject ? 0.5f * s.t : s.t);
+    s.t = reject ? 0.5f * s.t : s.t;
     s.trials = accept ? 0 : (reject ? trials : s.trials);
     s.newton += (accept & !conv & !maxed) ? 1 : 0;
-    s.code = conv ? iters_code(s.newton) : ((maxed | stuck) ? kNotConverged : s.code);
+    s.failed = s.failed | maxed | stuck;
     s.done = done;
     s.slow = s.slow | !ok;
 }
@@ -634,7 +668,7 @@ MHC_DEV uint32_t project_newton(const float* a_nat, float* P_out, const SolverOp
     evaluate(s.a, s.k, s.kfast, s.g0, s.g1, s.g2, E);
 #pragma unroll
     for (int k = 0; k < 16; ++k) P_out[k] = E.P[k];
-    return s.code;
+    return newton_code(s);
 }
 
 // The same projection for a lane whose logits sit in its own 16-float LDS
@@ -653,7 +687,7 @@ MHC_DEV uint32_t project_newton_lds(const float* a_nat, float* rec, const Solver
         evaluate(s.a, s.k, s.kfast, s.g0, s.g1, s.g2, E);
         sink_store(rec, E.P);
     }
-    return s.code;
+    return newton_code(s);
 }
 
 // Forward projection of one matrix by Sinkhorn-Knopp sweeps (each sweep:

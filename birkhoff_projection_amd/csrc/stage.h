@@ -15,11 +15,19 @@
 // input.  Only lanes of one wave share a tile, so the exchanges need no
 // barrier, only a compiler fence (the compiler models lanes as threads).
 // All accesses are streaming (nontemporal): every record is moved once.
+//
+// The wave's position (`first`) must be the same in every lane; kernels take
+// the wave index from wave_index(), which the compiler then knows to be
+// uniform, so the full-wave tests below are scalar branches and a full wave
+// (the common case) runs no per-lane bounds arithmetic.
 #pragma once
 
 #include "devmath.h"
 
 namespace mhc {
+
+// Index of the calling wave in its workgroup, as a wave-uniform value.
+MHC_DEV int wave_index() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
 template <int R>
 constexpr int record_pitch()
@@ -99,6 +107,11 @@ MHC_DEV void issue_records_v4(const float* __restrict__ g, int64_t first, int64_
     static_assert(R % 4 == 0, "records of whole float4s");
     constexpr int kQ = R / 4;  // float4 loads per lane
     const float4* g4 = reinterpret_cast<const float4*>(g);
+    if (B - first >= 64) {
+#pragma unroll
+        for (int i = 0; i < kQ; ++i) v[i] = mhc_load_stream(g4 + kQ * first + lane + 64 * i);
+        return;
+    }
     const int64_t last = kQ * B - 1;
 #pragma unroll
     for (int i = 0; i < kQ; ++i) {
@@ -115,16 +128,28 @@ MHC_DEV void scatter_records_v4(const float4 (&v)[R / 4], int64_t first, int64_t
     constexpr int kQ = R / 4;
     const int64_t have = B - first;
     mhc_wave_lds_fence();
+    if (have >= 64) {
 #pragma unroll
-    for (int i = 0; i < kQ; ++i) {
-        const int e = 4 * (lane + 64 * i);
-        const int rec = e / R, col = e % R;
-        const bool in = rec < have;
-        float* t = tile + rec * kP + col;
-        t[0] = in ? v[i].x : 0.f;
-        t[1] = in ? v[i].y : 0.f;
-        t[2] = in ? v[i].z : 0.f;
-        t[3] = in ? v[i].w : 0.f;
+        for (int i = 0; i < kQ; ++i) {
+            const int e = 4 * (lane + 64 * i);
+            float* t = tile + (e / R) * kP + e % R;
+            t[0] = v[i].x;
+            t[1] = v[i].y;
+            t[2] = v[i].z;
+            t[3] = v[i].w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kQ; ++i) {
+            const int e = 4 * (lane + 64 * i);
+            const int rec = e / R, col = e % R;
+            const bool in = rec < have;
+            float* t = tile + rec * kP + col;
+            t[0] = in ? v[i].x : 0.f;
+            t[1] = in ? v[i].y : 0.f;
+            t[2] = in ? v[i].z : 0.f;
+            t[3] = in ? v[i].w : 0.f;
+        }
     }
     mhc_wave_lds_fence();
 #pragma unroll
