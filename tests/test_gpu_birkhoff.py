@@ -219,6 +219,20 @@ def test_max_iters_flags_and_nan(gpu_lib):
     assert_fwd(P2[good], birkhoff_project(A2[good].astype(np.float64)), label="nan neighbours")
 
 
+def test_warm_sweeps_option(gpu_lib):
+    """opts.warm_sweeps = 1 and 2: log-domain Sinkhorn sweeps after the
+    assignment start, before the first Newton direction (an option; the
+    default runs none).  Against the oracle on N(0,1) and N(0,10^2) logits,
+    with a ragged batch, and every matrix converged."""
+    for kind in ("normal1", "normal10"):
+        A = W.logits_batch(kind, 1000, 43)
+        ref = birkhoff_project(A.astype(np.float64))
+        for warm in (1, 2):
+            P, it = _fwd(gpu_lib, A, warm_sweeps=warm)
+            assert (it != 255).all(), (kind, warm)
+            assert_fwd(P, ref, label=f"{kind} warm {warm}")
+
+
 def test_sinkhorn_mode(gpu_lib):
     """Sinkhorn solver: to tolerance on N(0,1), and the fixed 20-sweep mode
     against the oracle's own fixed-count Sinkhorn (float64)."""
