@@ -525,32 +525,23 @@ MHC_DEV void newton_init(NewtonLane& s, const float* a_nat, const float* rec, co
     s.done = s.res <= tol2;
     s.failed = false;
     const int warm = o.warm_sweeps < 0 ? 0 : o.warm_sweeps;  // -1: none after this start
-    if (warm > 0) {
-        // The sweeps carry only the column sums from one to the next, and E
-        // is evaluated again at the final point: holding two whole
-        // evaluations across this loop set the register count of every
+    for (int w = 0; w < warm; ++w) {
+        // A lane that is done re-evaluates its own point (bit for bit the
+        // same E), so that the sweep can overwrite E in place: holding two
+        // whole evaluations across this loop set the register count of every
         // forward kernel, the default (no sweeps) included.
-        float c0 = E.c[0], c1 = E.c[1], c2 = E.c[2], c3 = E.c[3];
-        for (int w = 0; w < warm; ++w) {
-            const float l3 = mhc_log2(mhc_max(c3, kMinMass));
-            const float n0 = s.g0 + (l3 - mhc_log2(mhc_max(c0, kMinMass)));
-            const float n1 = s.g1 + (l3 - mhc_log2(mhc_max(c1, kMinMass)));
-            const float n2 = s.g2 + (l3 - mhc_log2(mhc_max(c2, kMinMass)));
-            Eval F;
-            evaluate(s.a, s.k, s.kfast, n0, n1, n2, F);
-            if (!s.done) {
-                s.g0 = n0;
-                s.g1 = n1;
-                s.g2 = n2;
-                newton_take(s, F);
-                c0 = F.c[0];
-                c1 = F.c[1];
-                c2 = F.c[2];
-                c3 = F.c[3];
-                s.done = s.res <= tol2;
-            }
+        const float l3 = mhc_log2(mhc_max(E.c[3], kMinMass));
+        const float n0 = s.done ? s.g0 : s.g0 + (l3 - mhc_log2(mhc_max(E.c[0], kMinMass)));
+        const float n1 = s.done ? s.g1 : s.g1 + (l3 - mhc_log2(mhc_max(E.c[1], kMinMass)));
+        const float n2 = s.done ? s.g2 : s.g2 + (l3 - mhc_log2(mhc_max(E.c[2], kMinMass)));
+        evaluate(s.a, s.k, s.kfast, n0, n1, n2, E);
+        if (!s.done) {
+            s.g0 = n0;
+            s.g1 = n1;
+            s.g2 = n2;
+            newton_take(s, E);
+            s.done = s.res <= tol2;
         }
-        evaluate(s.a, s.k, s.kfast, s.g0, s.g1, s.g2, E);
     }
     float tcap = 0.f;
     s.d0 = s.d1 = s.d2 = s.slope = 0.f;

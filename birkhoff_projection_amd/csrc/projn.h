@@ -359,17 +359,18 @@ MHC_DEV void newton_init_n(NewtonLaneN<N>& s, const float* a_nat, const SolverOp
     // Newton trials without it, 3.0 with it), unlike for n = 4.
     const int warm = o.warm_sweeps < 0 ? 1 : o.warm_sweeps;
     for (int sw = 0; sw < warm; ++sw) {
+        // a lane that is done re-evaluates its own point (bit for bit the same
+        // E), so that E is overwritten in place and one evaluation is live here
         const float ln = mhc_log2(mhc_max(E.c[N - 1], kMinMass));
         float ng[N - 1];
 #pragma unroll
-        for (int j = 0; j < N - 1; ++j) ng[j] = s.g[j] + (ln - mhc_log2(mhc_max(E.c[j], kMinMass)));
-        EvalN<N> F;
-        evaluate_n<N>(s.a, s.k, s.kfast, ng, F);
+        for (int j = 0; j < N - 1; ++j)
+            ng[j] = s.done ? s.g[j] : s.g[j] + (ln - mhc_log2(mhc_max(E.c[j], kMinMass)));
+        evaluate_n<N>(s.a, s.k, s.kfast, ng, E);
         if (!s.done) {
 #pragma unroll
             for (int j = 0; j < N - 1; ++j) s.g[j] = ng[j];
-            s.res = F.res;
-            E = F;
+            s.res = E.res;
             s.done = s.res <= o.tol;
         }
     }
