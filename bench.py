@@ -88,18 +88,18 @@ KERNEL_SOURCES = {
     "layer": ("devmath.h", "proj4.h", "wave.h", "kernels.h", "layer.hip"),
 }
 MEASURED = {
-    "birkhoff_fwd_131072_cfg2": {"fetch": 8518735, "write": 8388960, "valu": 2428524, "trans": 122685, "sha": "c922610c3f315bf8"},
-    "birkhoff_bwd_131072_cfg2": {"fetch": 16805810, "write": 8388711, "valu": 1122304, "trans": 24576, "sha": "c922610c3f315bf8"},
-    "birkhoff_pipeline_131072_cfg2": {"fetch": 25356075, "write": 16800537, "valu": 3122779, "trans": 128829, "sha": "c922610c3f315bf8"},
-    "birkhoff_fwd_1048576_cfg3": {"fetch": 67239853, "write": 67117052, "valu": 18806279, "trans": 946129, "sha": "c922610c3f315bf8"},
-    "birkhoff_bwd_1048576_cfg3": {"fetch": 134231118, "write": 67109085, "valu": 8978432, "trans": 196608, "sha": "c922610c3f315bf8"},
-    "birkhoff_pipeline_1048576_cfg3": {"fetch": 201499584, "write": 134224492, "valu": 24360317, "trans": 995281, "sha": "c922610c3f315bf8"},
-    "birkhoff_fwd_bwd_131072_cfg2": {"fetch": 16966832, "write": 16777276, "valu": 2977371, "trans": 128829, "sha": "c922610c3f315bf8"},
-    "birkhoff_fwd_n8_131072_cfg2": {"fetch": 40897258, "write": 59769985, "valu": 22793495, "trans": 745229, "sha": "c81fc94510d4dee0"},
-    "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67434096, "write": 33555018, "valu": 6424576, "trans": 14336, "sha": "c81fc94510d4dee0"},
-    "stream_mix_fwd_16384x4x4096": {"fetch": 537993114, "write": 537927744, "valu": 25666560, "trans": 64512, "sha": "1908a484b992311d"},
-    "stream_mix_bwd_16384x4x4096": {"fetch": 1074727811, "write": 537951093, "valu": 49479680, "trans": 0, "sha": "1908a484b992311d"},
-    "layer_step_65536x4x7168": {"fetch": 30712082712, "write": 9469206752, "mfma": {"layer_maps_kernel<0>": 7340032, "layer_dx_kernel": 14680064, "layer_dw_kernel": 14680064}, "us": {"layer_maps_kernel<0>": 667.18, "layer_dx_kernel": 2578.94, "layer_dw_kernel": 752.88}, "sha": "53e5ab677c7bb8e1"},
+    "birkhoff_fwd_131072_cfg2": {"fetch": 8530011, "write": 8388960, "valu": 2077837, "trans": 122619, "sha": "06fe431b82dd2223"},
+    "birkhoff_bwd_131072_cfg2": {"fetch": 16805842, "write": 8388702, "valu": 1122304, "trans": 24576, "sha": "06fe431b82dd2223"},
+    "birkhoff_pipeline_131072_cfg2": {"fetch": 25360205, "write": 16777267, "valu": 2649196, "trans": 128763, "sha": "06fe431b82dd2223"},
+    "birkhoff_fwd_1048576_cfg3": {"fetch": 67250930, "write": 67118441, "valu": 16073142, "trans": 945927, "sha": "06fe431b82dd2223"},
+    "birkhoff_bwd_1048576_cfg3": {"fetch": 134231236, "write": 67109184, "valu": 8978432, "trans": 196608, "sha": "06fe431b82dd2223"},
+    "birkhoff_pipeline_1048576_cfg3": {"fetch": 201504454, "write": 134222219, "valu": 20644003, "trans": 995079, "sha": "06fe431b82dd2223"},
+    "birkhoff_fwd_bwd_131072_cfg2": {"fetch": 16973961, "write": 16777430, "valu": 2583660, "trans": 128763, "sha": "06fe431b82dd2223"},
+    "birkhoff_fwd_n8_131072_cfg2": {"fetch": 35345359, "write": 36700564, "valu": 22115047, "trans": 745229, "sha": "a86b73ac501fd1c4"},
+    "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67432093, "write": 33555993, "valu": 6424576, "trans": 14336, "sha": "a86b73ac501fd1c4"},
+    "stream_mix_fwd_16384x4x4096": {"fetch": 538001008, "write": 537928107, "valu": 25572352, "trans": 64512, "sha": "cc30e49415216764"},
+    "stream_mix_bwd_16384x4x4096": {"fetch": 1074726509, "write": 537955179, "valu": 49479680, "trans": 0, "sha": "cc30e49415216764"},
+    "layer_step_65536x4x7168": {"fetch": 30723477759, "write": 9469241453, "mfma": {"layer_maps_kernel<0>": 7340032, "layer_dx_kernel": 14680064, "layer_dw_kernel": 14680064}, "us": {"layer_maps_kernel<0>": 664.41, "layer_dx_kernel": 2583.83, "layer_dw_kernel": 749.94}, "sha": "0f8ff8e8be12b95f"},
 }
 
 
