@@ -79,8 +79,9 @@ def spin_ahead(torch):
 # scaled by what the counter reads for a plain copy of known size, and VALU
 # instructions (SQ_INSTS_VALU, of which SQ_INSTS_VALU_TRANS_F32 are
 # transcendental).  They hold only for the kernel sources they were taken on:
-# each entry carries the hash of the csrc files its kernels are built from
-# (KERNEL_SOURCES), and a mismatch reports it as null.
+# each entry carries the hash of the code (comments stripped) of the csrc
+# files its kernels are built from (KERNEL_SOURCES), and a mismatch reports it
+# as null.
 KERNEL_SOURCES = {
     "proj": ("devmath.h", "proj4.h", "stage.h", "birkhoff.hip"),
     "projn": ("devmath.h", "proj4.h", "projn.h", "stage.h", "birkhoffn.hip"),
@@ -88,18 +89,18 @@ KERNEL_SOURCES = {
     "layer": ("devmath.h", "proj4.h", "wave.h", "kernels.h", "layer.hip"),
 }
 MEASURED = {
-    "birkhoff_fwd_131072_cfg2": {"fetch": 8530011, "write": 8388960, "valu": 2077837, "trans": 122619, "sha": "06fe431b82dd2223"},
-    "birkhoff_bwd_131072_cfg2": {"fetch": 16805842, "write": 8388702, "valu": 1122304, "trans": 24576, "sha": "06fe431b82dd2223"},
-    "birkhoff_pipeline_131072_cfg2": {"fetch": 25360205, "write": 16777267, "valu": 2649196, "trans": 128763, "sha": "06fe431b82dd2223"},
-    "birkhoff_fwd_1048576_cfg3": {"fetch": 67250930, "write": 67118441, "valu": 16073142, "trans": 945927, "sha": "06fe431b82dd2223"},
-    "birkhoff_bwd_1048576_cfg3": {"fetch": 134231236, "write": 67109184, "valu": 8978432, "trans": 196608, "sha": "06fe431b82dd2223"},
-    "birkhoff_pipeline_1048576_cfg3": {"fetch": 201504454, "write": 134222219, "valu": 20644003, "trans": 995079, "sha": "06fe431b82dd2223"},
-    "birkhoff_fwd_bwd_131072_cfg2": {"fetch": 16973961, "write": 16777430, "valu": 2583660, "trans": 128763, "sha": "06fe431b82dd2223"},
-    "birkhoff_fwd_n8_131072_cfg2": {"fetch": 35345359, "write": 36700564, "valu": 22115047, "trans": 745229, "sha": "a86b73ac501fd1c4"},
-    "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67432093, "write": 33555993, "valu": 6424576, "trans": 14336, "sha": "a86b73ac501fd1c4"},
-    "stream_mix_fwd_16384x4x4096": {"fetch": 538001008, "write": 537928107, "valu": 25572352, "trans": 64512, "sha": "cc30e49415216764"},
-    "stream_mix_bwd_16384x4x4096": {"fetch": 1074726509, "write": 537955179, "valu": 49479680, "trans": 0, "sha": "cc30e49415216764"},
-    "layer_step_65536x4x7168": {"fetch": 30723477759, "write": 9469241453, "mfma": {"layer_maps_kernel<0>": 7340032, "layer_dx_kernel": 14680064, "layer_dw_kernel": 14680064}, "us": {"layer_maps_kernel<0>": 664.41, "layer_dx_kernel": 2583.83, "layer_dw_kernel": 749.94}, "sha": "0f8ff8e8be12b95f"},
+    "birkhoff_fwd_131072_cfg2": {"fetch": 8530011, "write": 8388960, "valu": 2077837, "trans": 122619, "sha": "02f6a806bc3f5d91"},
+    "birkhoff_bwd_131072_cfg2": {"fetch": 16805842, "write": 8388702, "valu": 1122304, "trans": 24576, "sha": "02f6a806bc3f5d91"},
+    "birkhoff_pipeline_131072_cfg2": {"fetch": 25360205, "write": 16777267, "valu": 2649196, "trans": 128763, "sha": "02f6a806bc3f5d91"},
+    "birkhoff_fwd_1048576_cfg3": {"fetch": 67250930, "write": 67118441, "valu": 16073142, "trans": 945927, "sha": "02f6a806bc3f5d91"},
+    "birkhoff_bwd_1048576_cfg3": {"fetch": 134231236, "write": 67109184, "valu": 8978432, "trans": 196608, "sha": "02f6a806bc3f5d91"},
+    "birkhoff_pipeline_1048576_cfg3": {"fetch": 201504454, "write": 134222219, "valu": 20644003, "trans": 995079, "sha": "02f6a806bc3f5d91"},
+    "birkhoff_fwd_bwd_131072_cfg2": {"fetch": 16973961, "write": 16777430, "valu": 2583660, "trans": 128763, "sha": "02f6a806bc3f5d91"},
+    "birkhoff_fwd_n8_131072_cfg2": {"fetch": 35345359, "write": 36700564, "valu": 22115047, "trans": 745229, "sha": "a6578b87f2f34140"},
+    "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67432093, "write": 33555993, "valu": 6424576, "trans": 14336, "sha": "a6578b87f2f34140"},
+    "stream_mix_fwd_16384x4x4096": {"fetch": 538001008, "write": 537928107, "valu": 25572352, "trans": 64512, "sha": "bc7166c9c0e6702f"},
+    "stream_mix_bwd_16384x4x4096": {"fetch": 1074726509, "write": 537955179, "valu": 49479680, "trans": 0, "sha": "bc7166c9c0e6702f"},
+    "layer_step_65536x4x7168": {"fetch": 30723477759, "write": 9469241453, "mfma": {"layer_maps_kernel<0>": 7340032, "layer_dx_kernel": 14680064, "layer_dw_kernel": 14680064}, "us": {"layer_maps_kernel<0>": 664.41, "layer_dx_kernel": 2583.83, "layer_dw_kernel": 749.94}, "sha": "a840795921a07568"},
 }
 
 
@@ -111,13 +112,24 @@ def source_group(key):
     return "mix" if key.startswith("stream_mix") else "layer"
 
 
+def code_text(src):
+    """Source text with comments and layout removed: what the compiler sees.
+    (The kernel sources hold no string literal with a comment marker.)"""
+    import re
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    lines = (" ".join(l.split()) for l in src.splitlines())
+    return "\n".join(l for l in lines if l)
+
+
 def sources_sha(group):
+    """Hash of the code (not the comments) of the kernel sources of `group`."""
     import hashlib
     h = hashlib.sha256()
     d = os.path.join(ROOT, "birkhoff_projection_amd", "csrc")
     for f in KERNEL_SOURCES[group]:
-        with open(os.path.join(d, f), "rb") as fh:
-            h.update(f.encode() + b"\0" + fh.read())
+        with open(os.path.join(d, f), encoding="utf-8") as fh:
+            h.update(f.encode() + b"\0" + code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

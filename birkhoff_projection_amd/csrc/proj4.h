@@ -29,7 +29,8 @@
 //
 // Everything is computed in base 2 (a = A log2 e, g in log2 units):
 // 2^(a + g) = e^(A + g ln 2).  The Newton direction of the base-2 objective is
-// the natural-units direction times log2 e; the gradient is still c - 1.
+// the natural-units direction times log2 e, which the solve yields directly
+// from the column defects scaled by log2 e (Eval::b).
 #pragma once
 
 #include "devmath.h"
@@ -298,7 +299,7 @@ MHC_DEV void sink_store(float* sink, const float* P)
 //            psi'(t) <= kCurvature |slope| (it has not overshot the line
 //            minimum by much), which needs only the column sums the
 //            evaluation already has -- no logarithms.  Near the fp32 noise
-//            floor (residual <= kNoiseFloor) a trial is accepted only if it
+//            floor (column residual <= kNoiseFloor) a trial is accepted only if it
 //            lowers the residual, and a rejected trial no longer than the
 //            Newton step ends the solve.  A rejected trial halves t.  Every
 //            trial reaching the tolerance is accepted.
@@ -312,7 +313,7 @@ struct NewtonLane {
     bool slow;           // the lane has left the factored evaluation for good
     float g0, g1, g2;    // accepted potentials (g3 = 0)
     float d0, d1, d2;    // direction (base 2)
-    float t, res, slope; // step length, residual, psi'(0) along d
+    float t, res, slope; // step length, residual and psi'(0) along d (Eval::res units)
     float grow;          // first-trial multiple of the Newton step (>= 1)
     int newton, trials;  // Newton directions taken, halvings this step
     bool failed;         // stopped without converging (iteration code 255)

@@ -38,6 +38,18 @@ def test_stored_counters_are_well_formed():
             assert os.path.exists(os.path.join(ROOT, "birkhoff_projection_amd", "csrc", f)), f
 
 
+
+def test_counter_hash_ignores_comments_only():
+    """The stored counters are keyed by the code of the kernel sources: a
+    comment or layout change keeps the key, a code change does not."""
+    import bench
+    a = "int f(int x) {  // doubles\n  return 2 * x; /* why */\n}\n"
+    b = "// a header note\nint f(int x) {\n\n    return 2 * x;\n}\n"
+    c = "int f(int x) { return 3 * x; }\n"
+    assert bench.code_text(a) == bench.code_text(b)
+    assert bench.code_text(a) != bench.code_text(c)
+    assert "doubles" not in bench.code_text(a) and "why" not in bench.code_text(a)
+
 def test_cpu_baselines_and_roofline_helpers():
     """The per-token oracle baselines of configs 4 and 5 and the projection
     baseline run on small host samples and report what they used; the
