@@ -96,8 +96,8 @@ MEASURED = {
     "birkhoff_bwd_1048576_cfg3": {"fetch": 134231236, "write": 67109184, "valu": 8978432, "trans": 196608, "sha": "02f6a806bc3f5d91"},
     "birkhoff_pipeline_1048576_cfg3": {"fetch": 201504454, "write": 134222219, "valu": 20644003, "trans": 995079, "sha": "02f6a806bc3f5d91"},
     "birkhoff_fwd_bwd_131072_cfg2": {"fetch": 16973961, "write": 16777430, "valu": 2583660, "trans": 128763, "sha": "02f6a806bc3f5d91"},
-    "birkhoff_fwd_n8_131072_cfg2": {"fetch": 35345359, "write": 36700564, "valu": 22115047, "trans": 745229, "sha": "a6578b87f2f34140"},
-    "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67432093, "write": 33555993, "valu": 6424576, "trans": 14336, "sha": "a6578b87f2f34140"},
+    "birkhoff_fwd_n8_131072_cfg2": {"fetch": 33951814, "write": 35652001, "valu": 20632142, "trans": 696051, "sha": "90455b546a1d0f2d"},
+    "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67447617, "write": 33555119, "valu": 6424576, "trans": 14336, "sha": "90455b546a1d0f2d"},
     "stream_mix_fwd_16384x4x4096": {"fetch": 538001008, "write": 537928107, "valu": 25572352, "trans": 64512, "sha": "bc7166c9c0e6702f"},
     "stream_mix_bwd_16384x4x4096": {"fetch": 1074726509, "write": 537955179, "valu": 49479680, "trans": 0, "sha": "bc7166c9c0e6702f"},
     "layer_step_65536x4x7168": {"fetch": 30723477759, "write": 9469241453, "mfma": {"layer_maps_kernel<0>": 7340032, "layer_dx_kernel": 14680064, "layer_dw_kernel": 14680064}, "us": {"layer_maps_kernel<0>": 664.41, "layer_dx_kernel": 2583.83, "layer_dw_kernel": 749.94}, "sha": "a840795921a07568"},

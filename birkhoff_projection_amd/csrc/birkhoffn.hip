@@ -15,12 +15,39 @@ namespace {
 
 constexpr int kBlockN = 256;
 
+// store_records for records that are already in the tile (lane l's record
+// at tile + l * record_pitch<R>(), each written by its own lane): only the
+// coalesced global stores.
+template <int R>
+MHC_DEV void store_tile(float* __restrict__ g, int64_t first, int64_t B, const float* tile,
+                        int lane)
+{
+    constexpr int kP = record_pitch<R>();
+    const int64_t have = B - first;
+    mhc_wave_lds_fence();  // the reads below see the other lanes' writes
+    if (have >= 64) {  // a full wave: no per-element checks
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const int e = lane + 64 * i;
+            __builtin_nontemporal_store(tile[(e / R) * kP + e % R], g + R * first + e);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const int e = lane + 64 * i;
+            const int rec = e / R;
+            if (rec < have) __builtin_nontemporal_store(tile[rec * kP + e % R], g + R * first + e);
+        }
+    }
+}
+
 // At least two waves per SIMD: left to itself the compiler gives the 7x7 and
 // 8x8 Newton solves 276 and 306 registers (all 256 VGPRs plus AGPRs), one
 // wave per SIMD, so 131072 matrices run in two generations of lone waves.
-// Held to 256 the 7x7 solve needs no spill and the 8x8 one spills 204 bytes
-// to scratch, and still: 7x7 51.7 -> 41.1 us, 8x8 74.6 -> 62.7 us at 131072
-// matrices (same-process A/B, bit-identical output).  Smaller n already fit.
+// Held to 256 the 7x7 solve needed no spill and the 8x8 one spilled 204
+// bytes to scratch (20 in the current solver), and still: 7x7 51.7 -> 41.1
+// us, 8x8 74.6 -> 62.7 us at 131072 matrices (same-process A/B, bit-identical
+// output).  Smaller n already fit.
 template <int N, int SOLVER>
 __global__ __launch_bounds__(kBlockN) __attribute__((amdgpu_waves_per_eu(2))) void birkhoff_fwd_n_kernel(const float* logits, float* P,
                                                                  uint8_t* __restrict__ iters,
@@ -31,10 +58,19 @@ __global__ __launch_bounds__(kBlockN) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int64_t first = (int64_t)blockIdx.x * kBlockN + 64 * w;
     if (first >= B) return;  // the whole wave is past the batch
-    float a[R], p[R];
+    float a[R];
     load_records<R>(logits, first, B, tiles[w], a, lane);
-    const uint32_t it = SOLVER == 0 ? project_newton_n<N>(a, p, o) : project_sinkhorn_n<N>(a, p, o);
-    store_records<R>(P, first, B, tiles[w], p, lane);
+    uint32_t it;
+    if (SOLVER == 0) {
+        // the lane's slot of the tile is free once its logits are in
+        // registers; the solve leaves P there and the store reads the tile
+        it = project_newton_lds_n<N>(a, tiles[w] + lane * record_pitch<R>(), o);
+        store_tile<R>(P, first, B, tiles[w], lane);
+    } else {
+        float p[R];
+        it = project_sinkhorn_n<N>(a, p, o);
+        store_records<R>(P, first, B, tiles[w], p, lane);
+    }
     if (iters != nullptr && first + lane < B) iters[first + lane] = (uint8_t)it;
 }
 

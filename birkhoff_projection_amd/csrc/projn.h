@@ -178,7 +178,17 @@ struct NewtonLaneN {
     int newton, trials;
     uint32_t code;
     bool done, slow, kfast;
+    bool stored;  // P is in the lane's sink (SINK solvers)
 };
+
+// Lane-private slot of N*N floats (LDS) that receives P where the lane's
+// solve ends, as sink_store for the 4x4 solver.
+template <int N>
+MHC_DEV void sink_store_n(float* sink, const float* P)
+{
+#pragma unroll
+    for (int e = 0; e < N * N; ++e) sink[e] = P[e];
+}
 
 // Newton direction at E in base-2 units, slope psi'(0) along it, and the
 // longest first step kMaxStep / max|d|.
@@ -321,8 +331,8 @@ MHC_DEV void assignment_start_n(const float* a, float* g)
     for (int j = 0; j < N - 1; ++j) g[j] = finite ? h[j] : 0.f;
 }
 
-template <int N>
-MHC_DEV void newton_init_n(NewtonLaneN<N>& s, const float* a_nat, const SolverOpts& o)
+template <int N, bool SINK>
+MHC_DEV void newton_init_n(NewtonLaneN<N>& s, const float* a_nat, const SolverOpts& o, float* sink)
 {
     float amin = 0.f;
 #pragma unroll
@@ -374,19 +384,30 @@ MHC_DEV void newton_init_n(NewtonLaneN<N>& s, const float* a_nat, const SolverOp
             s.done = s.res <= o.tol;
         }
     }
-    float tcap;
-    newton_direction_n<N>(E, s.d, s.slope, tcap);
+    float tcap = 0.f;
+#pragma unroll
+    for (int j = 0; j < N - 1; ++j) s.d[j] = 0.f;
+    s.slope = 0.f;
+    if (!SINK || wave_any(!s.done)) newton_direction_n<N>(E, s.d, s.slope, tcap);
     s.t = mhc_min(1.f, tcap);
     if (!s.done && o.max_iters < 1) {
         s.done = true;
         s.code = kNotConverged;
     }
     s.newton = 1;
+    s.stored = false;
+    if (SINK && s.done && s.code != kNotConverged) {
+        sink_store_n<N>(sink, E.P);
+        s.stored = true;
+    }
 }
 
-// One trial (see newton_step in proj4.h: same tests, branch-free update).
-template <int N, bool FACTORED>
-MHC_DEV void newton_step_n(NewtonLaneN<N>& s, const SolverOpts& o)
+// One trial (see newton_step in proj4.h: same tests, branch-free update
+// except that the next direction is computed only if some lane of the wave
+// goes on from an accepted point; with SINK a lane that converges writes
+// this trial's P to `sink`).
+template <int N, bool FACTORED, bool SINK>
+MHC_DEV void newton_step_n(NewtonLaneN<N>& s, const SolverOpts& o, float* sink)
 {
     float tg[N - 1];
 #pragma unroll
@@ -397,8 +418,6 @@ MHC_DEV void newton_step_n(NewtonLaneN<N>& s, const SolverOpts& o)
         ok = evaluate_factored_n<N>(s.k, tg, E);
     else
         evaluate_shifted_n<N>(s.a, tg, E);
-    float nd[N - 1], nslope, ncap;
-    newton_direction_n<N>(E, nd, nslope, ncap);
     float dphi = 0.f;
 #pragma unroll
     for (int j = 0; j < N - 1; ++j) dphi = __builtin_fmaf(E.c[j] - 1.f, s.d[j], dphi);
@@ -422,20 +441,32 @@ MHC_DEV void newton_step_n(NewtonLaneN<N>& s, const SolverOpts& o)
     const bool maxed = accept & !conv & (s.newton >= o.max_iters);
     const int trials = s.trials + 1;
     const bool stuck = reject & ((near_floor & (s.t <= 1.f)) | (trials > 30));
+    const bool done = s.done | conv | maxed | stuck;
 
-#pragma unroll
-    for (int j = 0; j < N - 1; ++j) {
-        s.g[j] = accept ? tg[j] : s.g[j];
-        s.d[j] = accept ? nd[j] : s.d[j];
+    // (P goes to the sink before the direction, which is the last use of E)
+    if (SINK && conv) {
+        sink_store_n<N>(sink, E.P);
+        s.stored = true;
     }
+    // The direction, its slope and the next trial length change only here:
+    // a lane that accepts while no lane of its wave goes on is done.
+    if (wave_any(accept & !done)) {
+        float nd[N - 1], nslope, ncap;
+        newton_direction_n<N>(E, nd, nslope, ncap);
+#pragma unroll
+        for (int j = 0; j < N - 1; ++j) s.d[j] = accept ? nd[j] : s.d[j];
+        s.slope = accept ? nslope : s.slope;
+        s.t = accept ? mhc_min(grow, ncap) : s.t;
+    }
+#pragma unroll
+    for (int j = 0; j < N - 1; ++j) s.g[j] = accept ? tg[j] : s.g[j];
     s.res = accept ? E.res : s.res;
-    s.slope = accept ? nslope : s.slope;
     s.grow = accept ? grow : s.grow;
-    s.t = accept ? mhc_min(grow, ncap) : (reject ? 0.5f * s.t : s.t);
+    s.t = reject ? 0.5f * s.t : s.t;
     s.trials = accept ? 0 : (reject ? trials : s.trials);
     s.newton += (accept & !conv & !maxed) ? 1 : 0;
     s.code = conv ? iters_code(s.newton) : ((maxed | stuck) ? kNotConverged : s.code);
-    s.done = s.done | conv | maxed | stuck;
+    s.done = done;
     s.slow = s.slow | !ok;
 }
 
@@ -443,13 +474,32 @@ template <int N>
 MHC_DEV uint32_t project_newton_n(const float* a_nat, float* P_out, const SolverOpts& o)
 {
     NewtonLaneN<N> s;
-    newton_init_n<N>(s, a_nat, o);
-    while (!s.done && !s.slow) newton_step_n<N, true>(s, o);
-    while (!s.done) newton_step_n<N, false>(s, o);
+    newton_init_n<N, false>(s, a_nat, o, nullptr);
+    while (!s.done && !s.slow) newton_step_n<N, true, false>(s, o, nullptr);
+    while (!s.done) newton_step_n<N, false, false>(s, o, nullptr);
     EvalN<N> E;
     evaluate_n<N>(s.a, s.k, s.kfast, s.g, E);
 #pragma unroll
     for (int e = 0; e < N * N; ++e) P_out[e] = E.P[e];
+    return s.code;
+}
+
+// The same projection leaving P in the lane's N*N-float LDS slot `rec`
+// (free once the logits are in registers): a lane writes P there from the
+// evaluation that converged, so only lanes that stop without converging
+// (flag 255) evaluate again at their last accepted point.
+template <int N>
+MHC_DEV uint32_t project_newton_lds_n(const float* a_nat, float* rec, const SolverOpts& o)
+{
+    NewtonLaneN<N> s;
+    newton_init_n<N, true>(s, a_nat, o, rec);
+    while (!s.done && !s.slow) newton_step_n<N, true, true>(s, o, rec);
+    while (!s.done) newton_step_n<N, false, true>(s, o, rec);
+    if (!s.stored) {
+        EvalN<N> E;
+        evaluate_n<N>(s.a, s.k, s.kfast, s.g, E);
+        sink_store_n<N>(rec, E.P);
+    }
     return s.code;
 }
 
