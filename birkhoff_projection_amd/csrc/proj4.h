@@ -2,8 +2,10 @@
 // or Sinkhorn-Knopp) and backward (implicit differentiation).
 //
 // One lane owns one matrix.  All 16 entries, the potentials and the solver
-// state stay in VGPRs; no cross-lane traffic, no LDS.  Every loop below is
-// fully unrolled so that array indices are compile-time constants.
+// state stay in VGPRs, with no cross-lane traffic; the staged kernels also
+// give each lane a private LDS slot, from which the start reads rows of its
+// logits and into which the solve leaves P.  Every loop below is fully
+// unrolled so that array indices are compile-time constants.
 //
 // Method ("Accelerating Birkhoff projection for mHC", gist.science summary):
 //  * section 2 -- the projection of A is the entropy-regularised transport
