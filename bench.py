@@ -98,9 +98,9 @@ MEASURED = {
     "birkhoff_fwd_bwd_131072_cfg2": {"fetch": 16973961, "write": 16777430, "valu": 2583660, "trans": 128763, "sha": "02f6a806bc3f5d91"},
     "birkhoff_fwd_n8_131072_cfg2": {"fetch": 33951814, "write": 35652001, "valu": 20632142, "trans": 696051, "sha": "90455b546a1d0f2d"},
     "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67447617, "write": 33555119, "valu": 6424576, "trans": 14336, "sha": "90455b546a1d0f2d"},
-    "stream_mix_fwd_16384x4x4096": {"fetch": 538001008, "write": 537928107, "valu": 25572352, "trans": 64512, "sha": "bc7166c9c0e6702f"},
-    "stream_mix_bwd_16384x4x4096": {"fetch": 1074726509, "write": 537955179, "valu": 49479680, "trans": 0, "sha": "bc7166c9c0e6702f"},
-    "layer_step_65536x4x7168": {"fetch": 30723477759, "write": 9469241453, "mfma": {"layer_maps_kernel<0>": 7340032, "layer_dx_kernel": 14680064, "layer_dw_kernel": 14680064}, "us": {"layer_maps_kernel<0>": 664.41, "layer_dx_kernel": 2583.83, "layer_dw_kernel": 749.94}, "sha": "a840795921a07568"},
+    "stream_mix_fwd_16384x4x4096": {"fetch": 539059096, "write": 537927787, "valu": 25592832, "trans": 68608, "sha": "f5dd6de6be0f8ebe"},
+    "stream_mix_bwd_16384x4x4096": {"fetch": 1074714477, "write": 537950805, "valu": 49479680, "trans": 0, "sha": "f5dd6de6be0f8ebe"},
+    "layer_step_65536x4x7168": {"fetch": 30741360653, "write": 9469181389, "mfma": {"layer_maps_kernel<0>": 7340032, "layer_dx_kernel": 14680064, "layer_dw_kernel": 14680064}, "us": {"layer_maps_kernel<0>": 670.64, "layer_dx_kernel": 2583.42, "layer_dw_kernel": 754.73}, "sha": "d5726b3030ab4abf"},
 }
 
 

@@ -274,7 +274,8 @@ __global__ __launch_bounds__(kBlock) void layer_maps_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// mix: read-mix u and write-back x_out, 16 tokens per workgroup.
+// mix: read-mix u and write-back x_out, 16 tokens per workgroup (spaced by
+// the grid size).
 // ---------------------------------------------------------------------------
 constexpr int kMixTokens = 16;
 
@@ -284,12 +285,15 @@ __global__ __launch_bounds__(kBlock) void layer_mix_kernel(
     uint4* __restrict__ xo, int64_t T, int64_t C8)
 {
     __shared__ float sM[kMixTokens][kMaps];
-    const int64_t t0 = (int64_t)blockIdx.x * kMixTokens;
+    // tokens b + G l for l < nt, as in the stream mix forward: the
+    // workgroups stream neighbouring tokens at any moment
+    const int64_t b = blockIdx.x, G = gridDim.x;
     const int tid = threadIdx.x;
-    const int nt = (int)((T - t0) < kMixTokens ? (T - t0) : kMixTokens);
+    const int64_t per = (T - b + G - 1) / G;
+    const int nt = (int)(per < kMixTokens ? per : kMixTokens);
     for (int p = tid; p < nt * kMaps; p += kBlock) {
         const int tl = p / kMaps, m = p % kMaps;
-        const int64_t t = t0 + tl;
+        const int64_t t = b + G * tl;
         sM[tl][m] = m < 4 ? Hpre[4 * t + m] : (m < 8 ? Hpost[4 * t + m - 4] : Hres[16 * t + m - 8]);
     }
     __syncthreads();
@@ -297,7 +301,7 @@ __global__ __launch_bounds__(kBlock) void layer_mix_kernel(
         float M[kMaps];
 #pragma unroll
         for (int m = 0; m < kMaps; ++m) M[m] = sM[tl][m];
-        const int64_t t = t0 + tl;
+        const int64_t t = b + G * tl;
         for (int64_t c = tid; c < C8; c += kBlock) {
             float xs[4][8], ff[8];
 #pragma unroll
@@ -331,7 +335,9 @@ __global__ __launch_bounds__(kBlock) void layer_mix_kernel(
 
 // ---------------------------------------------------------------------------
 // dots: wave w of workgroup b handles tokens 64 b + 16 w + [0, 16), one token
-// at a time across the wave; lanes stride over the 8-column chunks.  The pass
+// at a time across the wave; lanes stride over the 8-column chunks.  (Tokens
+// spaced by the grid's wave count, the order that speeds up the mix passes,
+// made the backward 1 % slower here.)  The pass
 // only reads (grad_f, which needs grad_x_out alone, is written by the dx pass:
 // a small write stream mixed into this read stream costs far more than its
 // bytes).  The
