@@ -36,7 +36,10 @@ def _rand_bf16(shape, seed):
     return torch.randn(shape, generator=g, device="cuda").to(torch.bfloat16)
 
 
-@pytest.mark.parametrize("T,C", [(1, 8), (15, 64), (16, 200), (17, 4096), (100, 520)])
+# T = 17, 241 and 4099 leave the grid's workgroups (16 tokens each, spaced by
+# the grid size) with unequal token counts
+@pytest.mark.parametrize("T,C", [(1, 8), (15, 64), (16, 200), (17, 4096), (100, 520), (241, 64),
+                                 (4099, 136)])
 def test_mix_given_H(gpu_lib, T, C):
     print(f"mix given H T={T} C={C}", flush=True)
     x = _rand_bf16((T, 4, C), 1000 + T)
@@ -59,7 +62,7 @@ def test_mix_identity_and_permutation_exact(gpu_lib):
     assert torch.equal(gpu_lib.stream_mix(x, Pm), x[:, perm])
 
 
-@pytest.mark.parametrize("T,C", [(33, 256), (16, 4096)])
+@pytest.mark.parametrize("T,C", [(33, 256), (16, 4096), (241, 128)])
 def test_mix_fused_projection(gpu_lib, T, C):
     x = _rand_bf16((T, 4, C), 2000 + T)
     logits = torch.from_numpy(W.logits_batch("normal2", T, 300 + T)).cuda()
