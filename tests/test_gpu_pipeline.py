@@ -121,3 +121,38 @@ def test_pipeline_sinkhorn_solver(gpu_lib):
         torch.cuda.synchronize()
         assert torch.equal(P, P_ref) and torch.equal(it, it_ref), opts
         assert torch.equal(dA, dA_ref), opts
+
+
+def test_full_size_fused_recompute_pipeline(gpu_lib):
+    """The 131072 N(0,10^2) workload (seed 2) in the launch configurations
+    bench.py times for `--fused`, `--recompute` and the `overlapped` figure:
+    the fused launch's P and the pipeline's P bit for bit mhc_birkhoff_fwd's;
+    the fused and pipeline gradients bit for bit the recompute backward's;
+    the recompute gradient within fp32 rounding of mhc_birkhoff_bwd's for
+    every matrix, and against the oracle on 4096 sampled matrices."""
+    bp = gpu_lib
+    A_np, G_np = W.config2()
+    A = torch.from_numpy(A_np).cuda()
+    G = torch.from_numpy(G_np).cuda()
+    P = bp.birkhoff_fwd(A)
+    dA_rows = bp.birkhoff_bwd(P, G)
+    dA_rec = bp.birkhoff_bwd_recompute(A, G)
+    P_f, dA_f = bp.birkhoff_fwd_bwd(A, G)
+    # pipeline: this batch's backward beside another batch's forward (the
+    # same logits rolled by one matrix, a different batch of the same size)
+    A2 = torch.roll(A, 1, dims=0).contiguous()
+    P2_ref = bp.birkhoff_fwd(A2)
+    P2, dA_p = bp.birkhoff_pipeline_step(A2, P, G)
+    torch.cuda.synchronize()
+    assert torch.equal(P_f, P)
+    assert torch.equal(dA_f, dA_rec)
+    assert torch.equal(P2, P2_ref)
+    assert torch.equal(dA_p, dA_rec)
+    _assert_rounding_close(dA_rec, dA_rows, G)
+    idx = np.sort(np.random.Generator(np.random.PCG64(11)).choice(A_np.shape[0], 4096, replace=False))
+    ref_P = birkhoff_project(A_np[idx].astype(np.float64))
+    G64 = G_np[idx].astype(np.float64)
+    ref = birkhoff_project_bwd(ref_P, G64)
+    err = np.abs(dA_rec.cpu().numpy()[idx] - ref).max(axis=(-2, -1))
+    bar = 1e-4 * np.abs(ref).max(axis=(-2, -1)) + 1e-5 * np.abs(G64).max(axis=(-2, -1))
+    assert (err <= bar).all(), f"worst {np.max(err / bar):.2f} of the bar"
