@@ -123,15 +123,18 @@ def test_pipeline_sinkhorn_solver(gpu_lib):
         assert torch.equal(dA, dA_ref), opts
 
 
-def test_full_size_fused_recompute_pipeline(gpu_lib):
-    """The 131072 N(0,10^2) workload (seed 2) in the launch configurations
-    bench.py times for `--fused`, `--recompute` and the `overlapped` figure:
+@pytest.mark.parametrize("config", [2, 3])
+def test_full_size_fused_recompute_pipeline(gpu_lib, config):
+    """The 131072 N(0,10^2) workload (seed 2) and the 1 M mixed one (seed 3)
+    in the launch configurations bench.py times for `--fused`, `--recompute`
+    and the `overlapped` figures:
     the fused launch's P and the pipeline's P bit for bit mhc_birkhoff_fwd's;
     the fused and pipeline gradients bit for bit the recompute backward's;
     the recompute gradient within fp32 rounding of mhc_birkhoff_bwd's for
     every matrix, and against the oracle on 4096 sampled matrices."""
     bp = gpu_lib
-    A_np, G_np = W.config2()
+    print(f"full-size fused/recompute/pipeline, config {config}", flush=True)
+    A_np, G_np = W.config2() if config == 2 else W.config3()[:2]
     A = torch.from_numpy(A_np).cuda()
     G = torch.from_numpy(G_np).cuda()
     P = bp.birkhoff_fwd(A)
