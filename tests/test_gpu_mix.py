@@ -119,3 +119,28 @@ def test_mix_bwd(gpu_lib, T, C):
     assert_mix(bf16_to_f64(gx), dx_ref, mag, "grad_x")
     magH = np.einsum("tic,tjc->tij", np.abs(g64), np.abs(x64))
     assert (np.abs(gH.cpu().numpy() - dH_ref) <= 1e-4 * magH + 1e-6).all()
+
+
+def test_mix_bwd_full_size(gpu_lib):
+    """The stream-mix backward as `bench.py --config 4 --mix-bwd` times it:
+    T = 16384, C = 4096, inputs seed 44, H projected from their logits by
+    mhc_birkhoff_fwd.  grad_H of every token and grad_x of 64 sampled tokens
+    against the oracle (the oracle's mix backward of the same H)."""
+    T, C = W.CONFIG4_SHAPE["T"], W.CONFIG4_SHAPE["C"]
+    x, g, logits = W.mix_bwd_inputs(T, C, seed=44)
+    H = gpu_lib.birkhoff_fwd(logits)
+    gx, gH = gpu_lib.stream_mix_bwd(x, H, g)
+    torch.cuda.synchronize()
+    H64 = H.cpu().numpy().astype(np.float64)
+    idx = np.sort(np.random.Generator(np.random.PCG64(44)).choice(T, 64, replace=False))
+    ti = torch.from_numpy(idx).cuda()
+    x64, g64 = bf16_to_f64(x[ti]), bf16_to_f64(g[ti])
+    dx_ref, dH_ref = stream_mix_bwd(H64[idx], x64, g64)
+    mag = np.einsum("tij,tic->tjc", np.abs(H64[idx]), np.abs(g64))
+    assert_mix(bf16_to_f64(gx[ti]), dx_ref, mag, "grad_x sample")
+    magH = np.einsum("tic,tjc->tij", np.abs(g64), np.abs(x64))
+    assert (np.abs(gH.cpu().numpy()[idx] - dH_ref) <= 1e-4 * magH + 1e-6).all()
+    # grad_H of every token, in float64 on the GPU from the same bf16 inputs
+    gHall = torch.einsum("tic,tjc->tij", g.double(), x.double())
+    magall = torch.einsum("tic,tjc->tij", g.double().abs(), x.double().abs())
+    assert bool(((gH.double() - gHall).abs() <= 1e-4 * magall + 1e-6).all())
