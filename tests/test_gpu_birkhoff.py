@@ -233,6 +233,26 @@ def test_warm_sweeps_option(gpu_lib):
             assert_fwd(P, ref, label=f"{kind} warm {warm}")
 
 
+
+def test_tolerance_option(gpu_lib):
+    """opts.tol is the column-sum tolerance.  Loose (1e-3): every matrix
+    stops converged with its column sums within tol (rows are stochastic by
+    construction) and in fewer Newton iterations than the default.  Below
+    the fp32 floor (1e-9): the solve ends at the noise floor, flagged 255
+    unless a trial happened to reach tol, and P still meets the oracle bars."""
+    A = W.logits_batch("normal10", 2000, 45)
+    ref = birkhoff_project(A.astype(np.float64))
+    P0, it0 = _fwd(gpu_lib, A)
+    P, it = _fwd(gpu_lib, A, tol=1e-3)
+    assert (it != 255).all()
+    P64 = P.astype(np.float64)
+    assert np.abs(P64.sum(-2) - 1).max() <= 1e-3 * 1.0001 + 1e-6
+    assert np.abs(P64.sum(-1) - 1).max() <= SUM_TOL
+    assert it.astype(np.int64).sum() < it0.astype(np.int64).sum()
+    P9, it9 = _fwd(gpu_lib, A, tol=1e-9)
+    assert (it9 == 255).mean() > 0.5
+    assert_fwd(P9, ref, label="tol 1e-9")
+
 def test_sinkhorn_mode(gpu_lib):
     """Sinkhorn solver: to tolerance on N(0,1), and the fixed 20-sweep mode
     against the oracle's own fixed-count Sinkhorn (float64)."""

@@ -164,3 +164,22 @@ def test_fwd_bwd_n_full_size(gpu_lib, n):
     assert np.isfinite(dA).all()
     idx = np.union1d(np.random.default_rng(1000 + n).choice(B, 1024, replace=False), flagged)
     _check(P[idx], dA[idx], A[idx], G[idx], f"n={n} full size, {idx.size} sampled")
+
+
+
+@pytest.mark.parametrize("n", [3, 8])
+def test_tolerance_option_n(gpu_lib, n):
+    """opts.tol for the n x n solver, as for the 4x4 one: loose tol converges
+    with column sums within it; tol below the fp32 floor ends flagged at the
+    noise floor with P within the oracle bars."""
+    A = W.logits_batch("normal10", 1000, 46 + n, n=n)
+    P, it = _fwd(gpu_lib, A, tol=1e-3)
+    assert (it != 255).all()
+    P64 = P.astype(np.float64)
+    assert np.abs(P64.sum(-2) - 1).max() <= 1e-3 * 1.0001 + 1e-6
+    assert np.abs(P64.sum(-1) - 1).max() <= SUM_TOL
+    P9, it9 = _fwd(gpu_lib, A, tol=1e-9)
+    assert (it9 == 255).mean() > 0.5
+    ref = birkhoff_project(A.astype(np.float64))
+    assert np.abs(P9.astype(np.float64) - ref).max() <= P_TOL
+    assert np.abs(P9.astype(np.float64).sum(-2) - 1).max() <= SUM_TOL
