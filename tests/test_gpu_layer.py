@@ -233,3 +233,25 @@ def test_layer_full_size(gpu_lib):
             + S_dxn + np.abs(xs) * np.abs(s_coef)[:, None, None] / (r ** 2)[:, None, None])
     close("grad_x", gx, ob["dx"], 2.0 ** -8 * np.abs(ob["dx"]) + 2e-4 * S_dx + 1e-6)
     assert not failures, "\n".join(failures)
+
+
+def test_layer_sinkhorn_solver(gpu_lib):
+    """The layer forward with the Sinkhorn-Knopp solver for H_res (opts
+    solver = Sinkhorn, run to tol): H_res within the projection bar of the
+    oracle's projection of the kernel's own logits; the maps, rms and u
+    (which does not involve H_res) bit for bit the Newton run's; x_out
+    within its two bf16 roundings plus what H_res moves it (each entry of
+    both H_res within 1e-5 of the projection, so at most 4 x 2e-5 max|x|)."""
+    x, Wt, f, _, _ = _small_case(64, 128, 77)
+    dev = torch.device("cuda")
+    xg, Wg, fg = (t.to(dev) for t in (x, Wt, f))
+    fn = gpu_lib.layer_fwd(xg, Wg, fg)
+    fs = gpu_lib.layer_fwd(xg, Wg, fg, solver="sinkhorn", tol=1e-6)
+    torch.cuda.synchronize()
+    for k in ("rms", "logits", "H_pre", "H_post", "u"):
+        assert torch.equal(fs[k], fn[k]), k
+    logits = fs["logits"].cpu().numpy().astype(np.float64)[:, 8:].reshape(-1, 4, 4)
+    assert np.abs(fs["H_res"].cpu().numpy() - birkhoff_project(logits)).max() <= 1e-5
+    a, b = fs["x_out"].float(), fn["x_out"].float()
+    bound = 2.0 ** -7 * b.abs() + 4 * 2e-5 * xg.float().abs().amax() + 1e-6
+    assert bool(((a - b).abs() <= bound).all())
