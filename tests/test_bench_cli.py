@@ -39,6 +39,15 @@ def test_stored_counters_are_well_formed():
 
 
 
+
+def test_stored_counters_match_the_sources():
+    """Every stored counter entry was taken on the kernel code as it stands
+    (a code change without retaking the counters would make the bench report
+    traffic and instruction counts as unknown)."""
+    import bench
+    stale = [k for k in bench.MEASURED if bench.measured(k) is None]
+    assert not stale, f"counters taken on other kernel code: {stale}"
+
 def test_counter_hash_ignores_comments_only():
     """The stored counters are keyed by the code of the kernel sources: a
     comment or layout change keeps the key, a code change does not."""
