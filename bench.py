@@ -100,7 +100,7 @@ MEASURED = {
     "birkhoff_bwd_n8_131072_cfg2": {"fetch": 67447617, "write": 33555119, "valu": 6424576, "trans": 14336, "sha": "90455b546a1d0f2d"},
     "stream_mix_fwd_16384x4x4096": {"fetch": 539059096, "write": 537927787, "valu": 25592832, "trans": 68608, "sha": "f5dd6de6be0f8ebe"},
     "stream_mix_bwd_16384x4x4096": {"fetch": 1074714477, "write": 537950805, "valu": 49479680, "trans": 0, "sha": "f5dd6de6be0f8ebe"},
-    "layer_step_65536x4x7168": {"fetch": 30741360653, "write": 9469181389, "mfma": {"layer_maps_kernel<0>": 7340032, "layer_dx_kernel": 14680064, "layer_dw_kernel": 14680064}, "us": {"layer_maps_kernel<0>": 670.64, "layer_dx_kernel": 2583.42, "layer_dw_kernel": 754.73}, "sha": "d5726b3030ab4abf"},
+    "layer_step_65536x4x7168": {"fetch": 30741360653, "write": 9469181389, "mfma": {"layer_maps_kernel<0>": 7340032, "layer_dx_kernel": 14680064, "layer_dw_kernel": 14680064}, "us": {"layer_maps_kernel<0>": 670.64, "layer_dx_kernel": 2583.42, "layer_dw_kernel": 754.73}, "sha": "a54d06b4171c20b2"},
 }
 
 

@@ -739,7 +739,7 @@ struct DwLoads {
 
 MHC_DEV void dw_issue(DwLoads& d, const uint16_t* __restrict__ x, const __bf16* __restrict__ dlT_hi,
                       const __bf16* __restrict__ dlT_lo, int64_t tc, int64_t T, int64_t Tp,
-                      int64_t tg1, int64_t D, int64_t k0, int lane)
+                      int64_t D, int64_t k0, int lane)
 {
     const int row = lane & 15, kq = lane >> 4;
     // chunks past the group read a clamped chunk; their A is zeroed on use
@@ -816,13 +816,13 @@ __global__ __launch_bounds__(kBlock) void layer_dw_kernel(
     // compiler's waits stay one chunk behind the issue
     DwLoads d0, d1;
     const int64_t first = tg0 + 32 * w;
-    dw_issue(d0, x, dlT_hi, dlT_lo, first, T, Tp, tg1, D, k0, lane);
+    dw_issue(d0, x, dlT_hi, dlT_lo, first, T, Tp, D, k0, lane);
     for (int64_t tc = first; tc < tg1; tc += 256) {
-        dw_issue(d1, x, dlT_hi, dlT_lo, tc + 128, T, Tp, tg1, D, k0, lane);
+        dw_issue(d1, x, dlT_hi, dlT_lo, tc + 128, T, Tp, D, k0, lane);
         __builtin_amdgcn_sched_barrier(0);
         dw_consume(d0, sX[w], acc, true, lane);
         __builtin_amdgcn_sched_barrier(0);
-        dw_issue(d0, x, dlT_hi, dlT_lo, tc + 256, T, Tp, tg1, D, k0, lane);
+        dw_issue(d0, x, dlT_hi, dlT_lo, tc + 256, T, Tp, D, k0, lane);
         __builtin_amdgcn_sched_barrier(0);
         dw_consume(d1, sX[w], acc, tc + 128 < tg1, lane);
         __builtin_amdgcn_sched_barrier(0);
